@@ -1,0 +1,239 @@
+"""Pins of the CPU oracle: checks against facts the oracle's code does not
+produce itself (closed forms, invariants, brute force at high precision,
+library format conversions). Each check takes the oracle module so the
+mutation tests can run the same checks against deliberately broken copies.
+
+Every check raises AssertionError on failure.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+
+mpmath.mp.dps = 50
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def tiny_case(seed, n, H=2, d_c=8, d_n=4, d_r=2, d_v=3):
+    """Random tiny MLA decode problem in float64 (non-square shapes everywhere
+    so that a transposed operand cannot go unnoticed)."""
+    r = _rng(seed)
+    return dict(
+        q_nope=r.standard_normal((1, H, d_n)), q_pe=r.standard_normal((1, H, d_r)),
+        w_uk=r.standard_normal((H, d_n, d_c)) / math.sqrt(d_c),
+        w_uv=r.standard_normal((H, d_c, d_v)) / math.sqrt(d_c),
+        C=r.standard_normal((n, d_c)), R=r.standard_normal((n, d_r)),
+        scale=1.0 / math.sqrt(d_n + d_r))
+
+
+def bruteforce_head(case, h):
+    """Decode of one head straight from the definition, in 50-digit mpmath:
+    key k_t = [W_UK[h] c_t ; k^R_t], value v_t = c_t W_UV[h], query
+    [q_nope ; q_pe], weights exp(scale * q.k_t) normalised over t."""
+    mp = mpmath.mp
+    C, R = case["C"], case["R"]
+    n, d_c = C.shape
+    wuk, wuv = case["w_uk"][h], case["w_uv"][h]
+    qn, qp = case["q_nope"][0, h], case["q_pe"][0, h]
+    d_n, d_v, d_r = wuk.shape[0], wuv.shape[1], R.shape[1]
+    sc = mp.mpf(case["scale"])
+    scores = []
+    values = []
+    for t in range(n):
+        key = [mp.fsum(mp.mpf(wuk[j, c]) * mp.mpf(C[t, c]) for c in range(d_c)) for j in range(d_n)]
+        key += [mp.mpf(R[t, r]) for r in range(d_r)]
+        q = [mp.mpf(x) for x in qn] + [mp.mpf(x) for x in qp]
+        scores.append(sc * mp.fsum(a * b for a, b in zip(q, key)))
+        values.append([mp.fsum(mp.mpf(C[t, c]) * mp.mpf(wuv[c, v]) for c in range(d_c)) for v in range(d_v)])
+    w = [mp.exp(s) for s in scores]
+    z = mp.fsum(w)
+    out = [mp.fsum(w[t] * values[t][v] for t in range(n)) / z for v in range(d_v)]
+    return np.array([float(x) for x in out]), float(mp.log(z))
+
+
+def _decode1(orc, case, absorbed=False):
+    return orc.decode(case["q_nope"], case["q_pe"], case["w_uk"], case["w_uv"],
+                      [case["C"]], [case["R"]], case["scale"], absorbed=absorbed)
+
+
+def pin_bruteforce(orc, seeds=(0, 1, 2), ns=(1, 2, 5, 8), tol=1e-13):
+    for seed in seeds:
+        for n in ns:
+            case = tiny_case(seed * 100 + n, n)
+            out, lse = _decode1(orc, case)
+            for h in range(case["w_uk"].shape[0]):
+                ref, ref_lse = bruteforce_head(case, h)
+                err = np.max(np.abs(out[0, h] - ref)) / max(np.max(np.abs(ref)), 1e-300)
+                assert err <= tol, f"brute force mismatch seed={seed} n={n} h={h}: {err}"
+                assert abs(lse[0, h] - ref_lse) <= tol * max(1.0, abs(ref_lse)), "lse mismatch"
+
+
+def pin_single_row(orc):
+    """N = 1: softmax of one score is 1, so o = c_0 W_UV[h] whatever the
+    query, and lse equals that single score."""
+    case = tiny_case(7, 1)
+    out, lse = _decode1(orc, case)
+    for h in range(2):
+        expect = case["C"][0] @ case["w_uv"][h]
+        assert np.allclose(out[0, h], expect, rtol=1e-14, atol=1e-14)
+        s0 = case["scale"] * (case["q_nope"][0, h] @ (case["w_uk"][h] @ case["C"][0])
+                              + case["q_pe"][0, h] @ case["R"][0])
+        assert abs(lse[0, h] - s0) <= 1e-14 * max(1, abs(s0))
+
+
+def pin_zero_query(orc):
+    """q = 0: all scores are 0, attention is uniform: o = mean(C) W_UV[h],
+    lse = ln N."""
+    case = tiny_case(11, 6)
+    case["q_nope"][:] = 0
+    case["q_pe"][:] = 0
+    out, lse = _decode1(orc, case)
+    for h in range(2):
+        expect = case["C"].mean(axis=0) @ case["w_uv"][h]
+        assert np.allclose(out[0, h], expect, rtol=1e-13, atol=1e-15)
+        assert abs(lse[0, h] - math.log(6)) < 1e-14
+
+
+def pin_rope_shift(orc):
+    """All RoPE-key rows equal: the RoPE term adds the same constant to every
+    score, so o does not depend on q_pe and lse moves by exactly that constant."""
+    case = tiny_case(13, 5)
+    case["R"][:] = case["R"][0]
+    out1, lse1 = _decode1(orc, case)
+    delta = np.array([0.7, -1.3])
+    case2 = dict(case)
+    case2["q_pe"] = case["q_pe"] + delta
+    out2, lse2 = _decode1(orc, case2)
+    assert np.allclose(out1, out2, rtol=1e-13, atol=1e-15)
+    shift = case["scale"] * (delta @ case["R"][0])
+    assert np.allclose(lse2 - lse1, shift, atol=1e-13)
+
+
+def pin_permutation(orc):
+    """Attention is a sum over rows: permuting the cache rows changes nothing."""
+    case = tiny_case(17, 8)
+    out1, lse1 = _decode1(orc, case)
+    p = _rng(3).permutation(8)
+    case2 = dict(case, C=case["C"][p], R=case["R"][p])
+    out2, lse2 = _decode1(orc, case2)
+    assert np.allclose(out1, out2, rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse1, lse2, rtol=1e-14)
+
+
+def pin_absorption(orc):
+    """Q K^T = (Q W_UK^T) c^T: the absorbed and non-absorbed forms agree to
+    float64 rounding."""
+    for seed in range(3):
+        case = tiny_case(seed + 50, 7, H=3, d_c=16, d_n=5, d_r=4, d_v=6)
+        o1, l1 = _decode1(orc, case)
+        o2, l2 = _decode1(orc, case, absorbed=True)
+        assert np.max(np.abs(o1 - o2)) <= 1e-12 * np.max(np.abs(o1))
+        assert np.max(np.abs(l1 - l2)) <= 1e-12 * np.max(np.abs(l1))
+
+
+def pin_hand_example(orc):
+    """Hand-worked case: one head, d_c=2, d_nope=1, d_rope=1, d_v=1,
+    W_UK=[[1,0]] (key = first latent coordinate), W_UV=[[0],[1]] (value =
+    second coordinate), q_nope=1, q_pe=0, two rows c_0=(0,v0), c_1=(x,v1)
+    with x = sqrt(2) ln 3 and scale 1/sqrt(2). Scores are 0 and ln 3, so the
+    weights are 1/4 and 3/4: o = (v0 + 3 v1)/4 and lse = ln 4."""
+    v0, v1 = 2.0, -6.0
+    x = math.sqrt(2.0) * math.log(3.0)
+    out, lse = orc.decode(np.array([[[1.0]]]), np.array([[[0.0]]]),
+                          np.array([[[1.0, 0.0]]]), np.array([[[0.0], [1.0]]]),
+                          [np.array([[0.0, v0], [x, v1]])], [np.array([[5.0], [-2.0]])],
+                          1.0 / math.sqrt(2.0))
+    assert abs(out[0, 0, 0] - (v0 + 3 * v1) / 4) < 1e-14
+    assert abs(lse[0, 0] - math.log(4.0)) < 1e-14
+
+
+def pin_causal_prefill(orc):
+    """[KV cache experiment] the decode of the token at step t over a cache of
+    t+1 rows equals row t of full causal attention over the whole sequence."""
+    T, H, d_c, d_n, d_r, d_v = 6, 2, 8, 4, 2, 3
+    r = _rng(5)
+    Qn = r.standard_normal((T, H, d_n))
+    Qp = r.standard_normal((T, H, d_r))
+    Wuk = r.standard_normal((H, d_n, d_c))
+    Wuv = r.standard_normal((H, d_c, d_v))
+    C = r.standard_normal((T, d_c))
+    R = r.standard_normal((T, d_r))
+    sc = 1 / math.sqrt(d_n + d_r)
+    for h in range(H):
+        full = orc.causal_prefill(Qn[:, h], Qp[:, h], Wuk[h], Wuv[h], C, R, sc)
+        for t in range(T):
+            o, _ = orc.decode(Qn[t:t + 1], Qp[t:t + 1], Wuk, Wuv, [C[:t + 1]], [R[:t + 1]],
+                              sc, heads=[h])
+            assert np.allclose(o[0, h], full[t], rtol=1e-12, atol=1e-14)
+    # and the first row of causal attention is the first value exactly
+    full = orc.causal_prefill(Qn[:, 0], Qp[:, 0], Wuk[0], Wuv[0], C, R, sc)
+    assert np.allclose(full[0], C[0] @ Wuv[0], rtol=1e-14)
+
+
+def pin_lse_combine(orc):
+    """Split the rows in two, decode each part, merge with the log-sum-exp
+    weights e^{lse_i - lse}: the merge equals the decode over all rows. This
+    pins lse (a wrong lse gives wrong weights)."""
+    case = tiny_case(23, 8)
+    out, lse = _decode1(orc, case)
+    a = dict(case, C=case["C"][:3], R=case["R"][:3])
+    b = dict(case, C=case["C"][3:], R=case["R"][3:])
+    oa, la = _decode1(orc, a)
+    ob, lb = _decode1(orc, b)
+    L = np.logaddexp(la, lb)
+    merged = np.exp(la - L)[..., None] * oa + np.exp(lb - L)[..., None] * ob
+    assert np.allclose(merged, out, rtol=1e-13, atol=1e-15)
+    assert np.allclose(L, lse, rtol=1e-14)
+
+
+def pin_empty(orc):
+    out, lse = orc.decode(np.ones((1, 1, 2)), np.ones((1, 1, 1)), np.ones((1, 2, 3)),
+                          np.ones((1, 3, 2)), [np.zeros((0, 3))], [np.zeros((0, 1))], 1.0)
+    assert np.all(out == 0) and lse[0, 0] == -math.inf
+
+
+def pin_paged_rows(orc):
+    """Hand-computed block-table addressing: block size 4, table [[2, 0], [1, 3]]:
+    sequence 0 token 5 -> block 0 slot 1 -> row 1; sequence 1 token 2 ->
+    block 1 slot 2 -> row 6; sequence 1 token 7 -> block 3 slot 3 -> row 15."""
+    table = np.array([[2, 0], [1, 3]])
+    assert orc.paged_row(table, 0, 5, 4) == 1
+    assert orc.paged_row(table, 0, 0, 4) == 8
+    assert orc.paged_row(table, 1, 2, 4) == 6
+    assert orc.paged_row(table, 1, 7, 4) == 15
+    assert list(orc.gather_rows(1, 3, seq_capacity=10)) == [10, 11, 12]
+    assert list(orc.gather_rows(0, 6, block_table=table, block_size=4)) == [8, 9, 10, 11, 0, 1]
+
+
+def pin_rope(orc):
+    """RoPE facts: position 0 is the identity; every pair keeps its norm;
+    pair 0 has frequency 1 (rotation by p radians); pair 16 of 64 has
+    frequency 10000^-0.5 = 0.01; R(a)R(b) = R(a+b); <R(p)q, R(p')k> depends
+    only on p - p'."""
+    r = _rng(9)
+    x = r.standard_normal(64)
+    y = r.standard_normal(64)
+    assert np.array_equal(orc.rope_rotate(x, 0), x)
+    z = orc.rope_rotate(x, 123)
+    assert np.allclose(np.hypot(z[0::2], z[1::2]), np.hypot(x[0::2], x[1::2]), rtol=1e-14)
+    e0 = np.zeros(64)
+    e0[0] = 1.0
+    e0[32] = 1.0
+    w = orc.rope_rotate(e0, 3)
+    assert np.allclose(w[0:2], [math.cos(3.0), math.sin(3.0)], atol=1e-15)
+    assert np.allclose(w[32:34], [math.cos(0.03), math.sin(0.03)], atol=1e-15)
+    assert np.allclose(orc.rope_rotate(orc.rope_rotate(x, 17), 40), orc.rope_rotate(x, 57), atol=1e-12)
+    d1 = orc.rope_rotate(x, 100) @ orc.rope_rotate(y, 90)
+    d2 = orc.rope_rotate(x, 1010) @ orc.rope_rotate(y, 1000)
+    assert abs(d1 - d2) < 1e-11
+
+
+ALL_DECODE_PINS = [pin_bruteforce, pin_single_row, pin_zero_query, pin_rope_shift,
+                   pin_permutation, pin_absorption, pin_hand_example, pin_causal_prefill,
+                   pin_lse_combine, pin_empty]

@@ -1,0 +1,145 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+its pins catch every one of them: a pin set that passes a broken oracle pins
+nothing."""
+
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "mla_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("mla_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def m_drop_rope_term(o):
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        K = C @ w_uk_h.T
+        return o.softmax_attend(scale * (K @ q_nope), C @ w_uv_h)
+    o.decode_head_nonabsorbed = f
+
+
+def m_wrong_scale(o):
+    orig = o.decode_head_nonabsorbed
+    o.decode_head_nonabsorbed = lambda *a: orig(*a[:-1], a[-1] * math.sqrt(2.0))
+
+
+def m_head_index(o):
+    orig = o.decode
+
+    def f(q_nope, q_pe, w_uk, w_uv, lat, rope, scale, **kw):
+        return orig(q_nope, q_pe, np.repeat(w_uk[:1], w_uk.shape[0], 0), w_uv, lat, rope, scale, **kw)
+    o.decode = f
+
+
+def m_uv_for_uk_layout(o):
+    # use the absorbed latent output without W_UV's proper contraction axis
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        K = C @ w_uk_h.T
+        V = C @ (w_uv_h[::-1])
+        return o.softmax_attend(scale * (K @ q_nope + R @ q_pe), V)
+    o.decode_head_nonabsorbed = f
+
+
+def m_unnormalised(o):
+    def f(scores, values):
+        m = np.max(scores) if len(scores) else 0.0
+        e = np.exp(scores - m)
+        return e @ values, m + math.log(np.sum(e)) if len(scores) else -math.inf
+    o.softmax_attend = f
+
+
+def m_lse_without_max(o):
+    def f(scores, values):
+        if len(scores) == 0:
+            return np.zeros(values.shape[1]), -math.inf
+        m = np.max(scores)
+        e = np.exp(scores - m)
+        return (e / e.sum()) @ values, math.log(e.sum())
+    o.softmax_attend = f
+
+
+def m_rope_sign(o):
+    def f(x, pos, base=10000.0):
+        ang = o.rope_angles(pos, x.shape[-1], base)
+        c, s = np.cos(ang), np.sin(ang)
+        out = np.empty_like(x, dtype=np.float64)
+        out[0::2] = x[0::2] * c + x[1::2] * s
+        out[1::2] = -x[0::2] * s + x[1::2] * c
+        return out
+    o.rope_rotate = f
+
+
+def m_rope_half_split(o):
+    def f(x, pos, base=10000.0):
+        d = x.shape[-1]
+        ang = o.rope_angles(pos, d, base)
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[: d // 2], x[d // 2:]
+        return np.concatenate([a * c - b * s, a * s + b * c])
+    o.rope_rotate = f
+
+
+def m_rope_freq(o):
+    o.rope_angles = lambda pos, d, base=10000.0: float(pos) * base ** (-np.arange(d // 2) / d)
+
+
+def m_paged_slot(o):
+    o.paged_row = lambda table, b, t, bs: int(table[b][t // bs]) * bs + (t % bs) + (1 if t % bs else 0)
+
+
+def m_paged_block(o):
+    o.paged_row = lambda table, b, t, bs: int(table[b][t // bs]) + (t % bs)
+
+
+def m_causal_mask(o):
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        K = C @ w_uk_h.T
+        V = C @ w_uv_h
+        S = scale * (q_nope @ K.T + q_pe @ R.T)
+        T = S.shape[0]
+        S = np.where(np.triu(np.ones((T, T), bool), k=2), -np.inf, S)
+        E = np.exp(S - S.max(1, keepdims=True))
+        return (E / E.sum(1, keepdims=True)) @ V
+    o.causal_prefill = f
+
+
+def m_absorbed_missing_uv(o):
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        q_lat = q_nope @ w_uk_h
+        o_lat, lse = o.softmax_attend(scale * (C @ q_lat + R @ q_pe), C)
+        return o_lat[: w_uv_h.shape[1]], lse
+    o.decode_head_absorbed = f
+
+
+MUTATIONS = [m_drop_rope_term, m_wrong_scale, m_head_index, m_uv_for_uk_layout,
+             m_unnormalised, m_lse_without_max, m_rope_sign, m_rope_half_split, m_rope_freq,
+             m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv]
+
+PINS = P.ALL_DECODE_PINS + [P.pin_paged_rows, P.pin_rope]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
+def test_pins_catch_mutation(mutation):
+    o = fresh_oracle()
+    for pin in PINS:          # the healthy copy passes every pin
+        if pin is not P.pin_bruteforce:
+            pin(o)
+    mutation(o)
+    caught = []
+    for pin in PINS:
+        kw = dict(seeds=(0,), ns=(1, 5)) if pin is P.pin_bruteforce else {}
+        try:
+            pin(o, **kw)
+        except Exception:     # AssertionError, or a shape error from a bad operand
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches {mutation.__name__}"
