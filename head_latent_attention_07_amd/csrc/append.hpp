@@ -1,0 +1,129 @@
+// Cache append: write the new token's latent row and RoPE-rotated key into the
+// cache ("How DeepSeek Rewrote the Transformer [MLA]", section "MLA: compress
+// the pair, not the heads": c_KV and the decoupled key k^R both go to the
+// cache, 576 numbers per token per layer).
+#pragma once
+
+#include "common.hpp"
+
+namespace mla {
+
+struct AppendParams {
+  const void* c_kv;           // [B, 512]
+  const void* k_pe;           // [B, 64], un-rotated
+  int in_bf16;                // input type: 1 bf16, 0 f32
+  const int32_t* positions;   // [B]
+  void* latent;
+  int64_t latent_stride;
+  void* rope;
+  int64_t rope_stride;
+  bf16* scales;               // fp8 cache only
+  int cache_kind;             // CacheKind
+  int64_t rows, seq_capacity;
+  const int32_t* block_table;
+  int max_blocks, block_size;
+  double theta;
+};
+
+// OCP e4m3fn code of v, round to nearest even, saturating to +-448.
+__device__ __forceinline__ uint32_t e4m3fn_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                      // below 2^-6: subnormal step 2^-9
+    return sign | (uint32_t)rintf(a * 512.0f);  // 8 lands on 0x08 = 2^-6
+  }
+  int e;
+  const float m = frexpf(a, &e);            // a = m 2^e, m in [0.5, 1)
+  int E = e - 1;                            // a = (2m) 2^E, 2m in [1, 2)
+  float q = rintf((2.0f * m - 1.0f) * 8.0f);
+  if (q == 8.0f) { q = 0.0f; E += 1; }
+  return sign | (uint32_t)(((E + 7) << 3) | (int)q);
+}
+
+// one wave per sequence: lane l owns latent values 8l..8l+7 and, for l < 32,
+// the RoPE pair (2l, 2l+1)
+__global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
+  const int b = blockIdx.x, l = threadIdx.x;
+  const int pos = p.positions[b];
+  int64_t r;
+  if (p.block_table) {
+    if (pos < 0 || pos / p.block_size >= p.max_blocks) return;
+    r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
+        pos % p.block_size;
+  } else {
+    if (pos < 0 || pos >= p.seq_capacity) return;
+    r = (int64_t)b * p.seq_capacity + pos;
+  }
+  if (r < 0 || r >= p.rows) return;
+
+  float x[8];
+  if (p.in_bf16) {
+    const bf16x8 v = *(const bf16x8*)((const bf16*)p.c_kv + (int64_t)b * D_C + 8 * l);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+  } else {
+    const f32x4* src = (const f32x4*)((const float*)p.c_kv + (int64_t)b * D_C + 8 * l);
+    const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = v0[i]; x[4 + i] = v1[i]; }
+  }
+  float r0 = 0.f, r1 = 0.f;
+  if (l < D_R / 2) {
+    double xe, xo;
+    if (p.in_bf16) {
+      const bf16* k = (const bf16*)p.k_pe + (int64_t)b * D_R;
+      xe = (float)k[2 * l];
+      xo = (float)k[2 * l + 1];
+    } else {
+      const float* k = (const float*)p.k_pe + (int64_t)b * D_R;
+      xe = k[2 * l];
+      xo = k[2 * l + 1];
+    }
+    const double freq = pow(p.theta, -2.0 * (double)l / (double)D_R);
+    double sn, cs;
+    sincos((double)pos * freq, &sn, &cs);
+    r0 = (float)(xe * cs - xo * sn);
+    r1 = (float)(xe * sn + xo * cs);
+  }
+
+  if (p.cache_kind == CACHE_F32) {
+    float* dst = (float*)p.latent + r * p.latent_stride + 8 * l;
+    *(f32x4*)dst = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    if (l < D_R / 2) *(f32x2*)((float*)p.rope + r * p.rope_stride + 2 * l) = f32x2{r0, r1};
+  } else if (p.cache_kind == CACHE_BF16) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+    *(bf16x8*)((bf16*)p.latent + r * p.latent_stride + 8 * l) = v;
+    if (l < D_R / 2) *(bf16x2*)((bf16*)p.rope + r * p.rope_stride + 2 * l) = bf16x2{(bf16)r0, (bf16)r1};
+  } else {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, fmaxf(fabsf(r0), fabsf(r1)));
+    amax = wave_max(amax);
+    float s;
+    if (amax == 0.f) {
+      s = 1.0f;
+    } else {
+      const float s32 = amax / 448.0f;
+      s = (s32 < 1.17549435e-38f) ? 1.17549435e-38f : (float)(bf16)s32;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3fn_encode(x[i] / s) << (8 * i);
+      hi |= e4m3fn_encode(x[4 + i] / s) << (8 * i);
+    }
+    *(u32x2*)((uint8_t*)p.latent + r * p.latent_stride + 8 * l) = u32x2{lo, hi};
+    if (l < D_R / 2) {
+      const uint32_t c0 = e4m3fn_encode(r0 / s), c1 = e4m3fn_encode(r1 / s);
+      *(uint16_t*)((uint8_t*)p.rope + r * p.rope_stride + 2 * l) = (uint16_t)(c0 | (c1 << 8));
+    }
+    if (l == 0) p.scales[r] = (bf16)s;
+  }
+}
+
+}  // namespace mla

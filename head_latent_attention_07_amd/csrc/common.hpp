@@ -1,0 +1,61 @@
+// Shared device types and helpers for the gfx950 MLA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D_C = 512;      // latent width
+constexpr int D_R = 64;       // decoupled RoPE key width
+constexpr int D_QK = D_C + D_R;
+constexpr int D_N = 128;      // no-RoPE query/key width
+constexpr int D_V = 128;      // value width
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+enum CacheKind { CACHE_F32 = 0, CACHE_BF16 = 1, CACHE_FP8 = 2 };
+
+// 64-lane wavefront helpers
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Physical cache row of token t of sequence b (contiguous or paged), clamped
+// into [0, rows) so that malformed device-side tables cannot fault.
+__device__ __forceinline__ int64_t cache_row(int b, int t, int64_t seq_capacity,
+                                             const int32_t* __restrict__ block_table,
+                                             int max_blocks, int block_size, int64_t rows) {
+  int64_t r;
+  if (block_table) {
+    int blk = block_table[(int64_t)b * max_blocks + t / block_size];
+    r = (int64_t)blk * block_size + (t % block_size);
+  } else {
+    r = (int64_t)b * seq_capacity + t;
+  }
+  return (r >= 0 && r < rows) ? r : 0;
+}
+
+}  // namespace mla

@@ -1,0 +1,599 @@
+// Split-KV flash-decode for MLA on gfx950 (bf16 MFMA, bf16 or fp8 cache).
+//
+// Absorbed MLA decode ("How DeepSeek Rewrote the Transformer [MLA]", section
+// "MLA: compress the pair, not the heads"): every head scores its absorbed
+// query q = [q_nope W_UK[h] | q_pe] against the same cached rows
+// [c_t | k^R_t] and mixes the same latent rows c_t, so the head dimension is
+// the M dimension of two dense contractions that share one operand stream:
+//
+//   S^T[t, h]  = sum_d  K[t, d] Q^T[d, h]        (d over 576)
+//   O^T[d, h] += sum_t  C^T[d, t] P^T[t, h]      (d over 512)
+//
+// Work decomposition
+//   * workgroup = (sequence b, token split s, head group g), NW waves;
+//     wave w owns 32 heads; its absorbed queries live in registers as the
+//     MFMA B operand (36 k-steps x 8 bf16 per lane) and its output
+//     accumulator O^T (32 heads x 512 dims, fp32) in 16 32x32 tiles.
+//   * the workgroup streams its token range in tiles of 32 rows through LDS,
+//     double buffered: global loads of tile i+1 are in flight while tile i is
+//     computed. A tile is 32 rows x 1152 bytes, stored row-major with a
+//     16-byte-chunk XOR swizzle (see lds_off) so that both read patterns
+//     below are free of bank conflicts.
+//   * QK^T reads the tile with ds_read_b128 (token-major A operand); PV reads
+//     the same bytes with ds_read_b64_tr_b16, the gfx950 transposing LDS
+//     read, which hands each lane 4 consecutive tokens of one latent column.
+//     The token order inside a 16-token k-step is permuted to match the
+//     32x32 accumulator layout of S^T, so P^T goes from the QK accumulator to
+//     the PV B operand without any cross-lane traffic.
+//   * online softmax in base 2 (the absorbed query is pre-scaled by
+//     softmax_scale * log2 e) with lazy rescaling: the running max used for
+//     exp2 moves only when a tile's max exceeds it by more than 8, which keeps
+//     every p <= 2^8 and skips most of the 256-register rescale.
+//   * fp8 cache: rows are converted to bf16 (exact) as they are written to
+//     LDS; the per-row scale multiplies the row's scores and, after the
+//     softmax sum, its probabilities, so both MFMAs see exact e4m3 values.
+//   * each split writes its normalised partial O (fp32) and its log2
+//     sum-exp; a separate kernel merges the splits and applies W_UV.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace mla {
+
+struct DecodeParams {
+  const bf16* q;               // [B, H, 576] absorbed query, pre-scaled
+  const void* latent;          // cache latent array
+  int64_t latent_stride;       // elements
+  const void* rope;            // cache RoPE-key array
+  int64_t rope_stride;         // elements
+  const bf16* scales;          // fp8 cache: bf16 scale per row
+  int64_t rows;                // rows in the cache arrays
+  int64_t seq_capacity;        // contiguous cache: rows per sequence
+  const int32_t* block_table;  // paged cache: [B, max_blocks] (nullptr: contiguous)
+  int max_blocks;
+  int block_size;
+  const int32_t* lengths;      // [B]
+  int max_len;
+  int B, H, S, tokens_per_split, G;
+  float* part_o;               // [B, S, H, 512] normalised partial outputs
+  float* part_lse;             // [B, S, H] log2 sum-exp of each split
+};
+
+
+constexpr int TILE = 32;                    // tokens per LDS tile
+constexpr int LAT_ROW = D_C * 2;            // 1024 B: bf16 latent row in LDS
+constexpr int ROPE_ROW = D_R * 2;           // 128 B: bf16 RoPE-key row in LDS
+constexpr int ROPE_OFF = TILE * LAT_ROW;    // RoPE rows follow the 32 latent rows
+constexpr int TILE_BYTES = ROPE_OFF + TILE * ROPE_ROW;  // 36864
+
+// The absorbed query of a lane's head is the QK^T B operand: its 32 latent
+// k-steps stay in registers (128 VGPRs), its 4 RoPE k-steps are read from
+// LDS (4 KB per wave), which leaves the register file room for the rest.
+constexpr int QREG = D_C / 16;
+
+// Swizzle of the 16-byte chunk index inside an LDS row (XOR on its low three
+// bits). Rows r..r+7 map a given chunk to 8 distinct 16-byte bank groups
+// (ds_read_b128 of 8 tokens at one column), and rows 4k..4k+3 map an aligned
+// pair of chunks to 4 distinct 32-byte bank groups (ds_read_b64_tr_b16 of 4
+// tokens), since the pair index is XORed with r mod 4.
+__device__ __forceinline__ int row_swizzle(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
+// this wave's LDS traffic is done and at most N of its global loads remain.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Per-lane LDS byte offsets of the MFMA operand reads (relative to a tile).
+// QK^T A operand, k-step j: latent j < 32 at qb[j & 3] + 128 (j >> 2), RoPE
+// key j >= 32 at rb[j - 32]. PV A operand (transposing read) for 32-dim tile
+// dt: tb[dt & 1] + 128 (dt >> 1), +8 rows for the upper 4 tokens, +16 rows
+// for the second 16-token k-step.
+struct LaneAddr {
+  int qb[4];
+  int rb[4];
+  int tb[2];
+};
+
+__device__ __forceinline__ LaneAddr lane_addr(int l) {
+  LaneAddr a;
+  const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
+  const int sw = row_swizzle(l32);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a.qb[k] = l32 * LAT_ROW + 16 * ((2 * k + h) ^ sw);
+    a.rb[k] = ROPE_OFF + l32 * ROPE_ROW + 16 * ((2 * k + h) ^ sw);
+  }
+  const int row1 = 4 * h + (jj >> 2);
+  const int x = (2 * (g16 & 1) + ((jj & 3) >> 1)) ^ row_swizzle(row1);
+  const int phi = (x >> 2) & 1, low = x & 3;
+  a.tb[0] = row1 * LAT_ROW + 64 * phi + 16 * low + 8 * (jj & 1);
+  a.tb[1] = row1 * LAT_ROW + 64 * (1 - phi) + 16 * low + 8 * (jj & 1);
+  return a;
+}
+
+__device__ __forceinline__ bf16x8 lds_tr8(const char* lo, const char* hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lo);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)hi);
+  return __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Softmax state and output accumulator of one wave (32 heads).
+//
+// The exponent reference m_ref of each head is fixed at the max of its first
+// tile and never moves, so the accumulator is never rescaled (a rescale
+// would need vector ALU passes over all 256 accumulator registers). A later
+// score may exceed m_ref by up to OVERFLOW_SLACK (p <= 2^64, far from fp32 or
+// bf16 overflow); a larger excess is reported and the workgroup recomputes
+// the split with m_ref set to the split's true maximum.
+constexpr float OVERFLOW_SLACK = 64.0f;  // log2 units
+
+struct WaveState {
+  f32x16 o[D_C / 32];   // O^T tiles: lane holds head l%32, dims 32dt + 8(r/4) + 4h + r%4
+  float m_ref;          // exponent reference (log2 units), -inf before the first tile
+  float lsum;           // this lane's share of the softmax denominator
+};
+
+// S^T = K Q^T for one tile; returns this lane's 16 scores (masked, scaled for
+// fp8) and the tile max of this lane's head.
+template <int CK>
+__device__ __forceinline__ float tile_scores(const char* tile, const float* scale, int tile_t0,
+                                             int t1, const bf16x8 (&qreg)[QREG],
+                                             const char* qpe, const LaneAddr& la, int h,
+                                             float (&sv)[16]) {
+  f32x16 sacc = f32x16{};
+#pragma unroll
+  for (int j = 0; j < D_QK / 16; ++j) {
+    const int off = (j < 32) ? la.qb[j & 3] + 128 * (j >> 2) : la.rb[j - 32];
+    const bf16x8 a = *(const bf16x8*)(tile + off);
+    const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : *(const bf16x8*)(qpe + (j - QREG) * 1024);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, sacc, 0, 0, 0);
+  }
+  // accumulator row r of this lane is token 8(r/4) + 4h + r%4 of the tile
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+    float v = sacc[r];
+    if (CK == CACHE_FP8) v *= scale[row];
+    sv[r] = (tile_t0 + row < t1) ? v : -INFINITY;
+    tmax = fmaxf(tmax, sv[r]);
+  }
+  return fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+}
+
+// One 32-token tile: scores, softmax weights against m_ref, O^T += C^T P^T.
+// Returns true if some score of this wave exceeded m_ref + OVERFLOW_SLACK.
+template <int CK>
+__device__ __forceinline__ bool tile_compute(const char* tile, const float* scale, int tile_t0,
+                                             int t1, const bf16x8 (&qreg)[QREG], const char* qpe,
+                                             const LaneAddr& la, int h, WaveState& st) {
+  float sv[16];
+  const float tmax = tile_scores<CK>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv);
+  st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
+  const bool ovf = __any(tmax > st.m_ref + OVERFLOW_SLACK);
+  bf16x8 pb[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = fast_exp2(sv[r] - st.m_ref);
+    st.lsum += e;
+    if (CK == CACHE_FP8) e *= scale[8 * (r >> 2) + 4 * h + (r & 3)];
+    pb[r >> 3][r & 7] = (bf16)e;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int dt = 0; dt < D_C / 32; ++dt) {
+      const char* p = tile + la.tb[dt & 1] + 128 * (dt >> 1) + ks * 16 * LAT_ROW;
+      const bf16x8 a = lds_tr8(p, p + 8 * LAT_ROW);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], st.o[dt], 0, 0, 0);
+    }
+  }
+  return ovf;
+}
+
+// Map a flat workgroup id to (sequence*split index q, head group g) so that
+// the G workgroups reading the same rows land on the same XCD (workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2).
+__device__ __forceinline__ void xcd_map(int x, int G, int& q, int& g) {
+  const int q_lo = x & 7;
+  const int rest = x >> 3;
+  g = rest % G;
+  q = (rest / G) * 8 + q_lo;
+}
+
+// Scalar (SMEM) load of a wave-uniform int. A plain load placed after the
+// direct-to-LDS loads becomes a vector load (the compiler cannot prove the
+// table unmodified across them), and waiting on it would also wait for every
+// DMA in flight; the scalar path is counted separately (lgkmcnt).
+__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// Physical row of the first token of a tile (tiles never cross a block:
+// block_size is a multiple of 32).
+__device__ __forceinline__ int64_t tile_base_row(const DecodeParams& p, int b, int tile_t0) {
+  if (p.block_table) {
+    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + tile_t0 / p.block_size);
+    const int blk = scalar_load_i32(p.block_table + idx);
+    return (int64_t)blk * p.block_size + (tile_t0 % p.block_size);
+  }
+  return (int64_t)b * p.seq_capacity + tile_t0;
+}
+
+// Buffer resource over [base, base + bytes) for raw buffer loads: accesses at
+// or past `bytes` return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = (int32_t)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+}
+
+// Buffer resources of one tile's rows: latent and RoPE-key arrays rebased at
+// the tile's first physical row (row offsets inside a tile fit in 32 bits).
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t lat, rope;
+};
+
+__device__ __forceinline__ TileRsrc tile_rsrc(const DecodeParams& p, int64_t base_row, int esize,
+                                              bool valid = true) {
+  TileRsrc t;
+  base_row = (base_row >= 0 && base_row < p.rows) ? base_row : 0;
+  const int64_t left = valid ? p.rows - base_row : 0;  // 0: every load returns zeros
+  t.lat = make_rsrc((const char*)p.latent + base_row * p.latent_stride * esize,
+                    left * p.latent_stride * esize);
+  t.rope = make_rsrc((const char*)p.rope + base_row * p.rope_stride * esize,
+                     left * p.rope_stride * esize);
+  return t;
+}
+
+// bf16 cache: direct global->LDS loads (16 bytes per lane), 36 wave-wide
+// loads per tile (32 latent rows of 1 KB, 4 groups of 8 RoPE-key rows).
+// Lane i writes LDS slot i of its 1 KB, so it fetches the chunk that the
+// swizzle places there. Rows past the split's last token re-read the last
+// token (their scores are masked).
+// With valid == false the loads are still issued (so every wave's count of
+// loads in flight stays the same on every path) but read nothing from memory.
+template <int NW>
+__device__ __forceinline__ void tile_dma(const DecodeParams& p, char* tile, int64_t base_row,
+                                         int last_row, int w, int l, bool valid) {
+  constexpr int RPW = TILE / NW;   // latent rows per wave (a multiple of 8)
+  constexpr int GPW = 4 / NW;      // RoPE-key row groups per wave
+  const TileRsrc rs = tile_rsrc(p, base_row, 2, valid);
+  const int lsb = (int)(p.latent_stride * 2), rsb = (int)(p.rope_stride * 2);
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int u = w * RPW + k;     // u % 8 == k % 8: the swizzle is a constant
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs.lat, (__attribute__((address_space(3))) void*)(tile + u * LAT_ROW), 16,
+        16 * (l ^ row_swizzle(k)), min(u, last_row) * lsb, 0, 0);
+  }
+  const int lrow = l >> 3;
+  const int lchunk = 16 * ((l & 7) ^ row_swizzle(lrow));
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const int v = w * GPW + k;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs.rope, (__attribute__((address_space(3))) void*)(tile + ROPE_OFF + v * 8 * ROPE_ROW), 16,
+        min(8 * v + lrow, last_row) * rsb + lchunk, 0, 0, 0);
+  }
+}
+
+// fp8 cache: the raw codes of a tile (32 rows x 576 bytes) and its 32 bf16
+// row scales are brought into an LDS staging area with direct global->LDS
+// loads, then widened to bf16 (exactly: e4m3 values are a subset of bf16)
+// into the same swizzled tile layout as a bf16 cache, so the MFMA path is
+// shared. Staging layout: latent [32][512], RoPE key [32][64], scales [32].
+constexpr int STG_ROPE = TILE * D_C;                 // 16384
+constexpr int STG_SCALE = STG_ROPE + TILE * D_R;     // 18432
+constexpr int STG_BYTES = STG_SCALE + 256;           // scale DMA writes 64 lanes x 4 B
+
+// Per wave: 16/NW latent loads (two 512-byte rows each) and M loads of the
+// three small pieces (RoPE rows 0-15, RoPE rows 16-31, scales), padded with
+// repeats so that every wave issues the same count.
+template <int NW>
+struct Fp8Dma {
+  static constexpr int LAT = 16 / NW;
+  static constexpr int MISC = (3 + NW - 1) / NW;
+  static constexpr int PER_TILE = LAT + MISC;
+};
+
+template <int NW>
+__device__ __forceinline__ void fp8_tile_dma(const DecodeParams& p, char* stage,
+                                             int64_t base_row, int last_row, int w, int l,
+                                             bool valid) {
+  const TileRsrc rs = tile_rsrc(p, base_row, 1, valid);
+  base_row = (base_row >= 0 && base_row < p.rows) ? base_row : 0;
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.scales + base_row, valid ? (p.rows - base_row) * 2 : 0);
+  const int lsb = (int)p.latent_stride, rsb = (int)p.rope_stride;
+#pragma unroll
+  for (int k = 0; k < Fp8Dma<NW>::LAT; ++k) {
+    const int pair = w * Fp8Dma<NW>::LAT + k;          // rows 2*pair, 2*pair+1
+    const int row = 2 * pair + (l >> 5);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs.lat, (__attribute__((address_space(3))) void*)(stage + pair * 2 * D_C), 16,
+        min(row, last_row) * lsb + 16 * (l & 31), 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < Fp8Dma<NW>::MISC; ++k) {
+    const int piece = min(w * Fp8Dma<NW>::MISC + k, 2);  // 0, 1: RoPE halves; 2: scales
+    if (piece < 2) {
+      const int row = 16 * piece + (l >> 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs.rope, (__attribute__((address_space(3))) void*)(stage + STG_ROPE + piece * 16 * D_R), 16,
+          min(row, last_row) * rsb + 16 * (l & 3), 0, 0, 0);
+    } else {
+      // 16 lanes x 4 bytes = 32 bf16 scales (rows past the split re-read
+      // neighbouring scales; those rows are masked)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsc, (__attribute__((address_space(3))) void*)(stage + STG_SCALE), 4,
+          4 * (l & 15), 0, 0, 0);
+    }
+  }
+}
+
+// Widen one staged tile into a bf16 tile; `scale` receives the row scales.
+template <int NT>
+__device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, float* scale,
+                                               int tid) {
+  constexpr int CHUNKS = TILE * (D_QK / 16);  // 1152 chunks of 16 codes
+#pragma unroll
+  for (int i = 0; i < (CHUNKS + NT - 1) / NT; ++i) {
+    const int q = i * NT + tid;
+    if (CHUNKS % NT == 0 || q < CHUNKS) {
+      int row, c;
+      const char* src;
+      char* dst;
+      if (q < TILE * (D_C / 16)) {
+        row = q >> 5;
+        c = q & 31;
+        src = stage + q * 16;
+        dst = tile + row * LAT_ROW;
+      } else {
+        const int qq = q - TILE * (D_C / 16);
+        row = qq >> 2;
+        c = qq & 3;
+        src = stage + STG_ROPE + qq * 16;
+        dst = tile + ROPE_OFF + row * ROPE_ROW;
+      }
+      const u32x4 v = *(const u32x4*)src;
+      u32x4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, false));
+        lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, true));
+        hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, false));
+        hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, true));
+      }
+      const int sw = row_swizzle(row);
+      *(u32x4*)(dst + 16 * ((2 * c) ^ sw)) = lo;
+      *(u32x4*)(dst + 16 * ((2 * c + 1) ^ sw)) = hi;
+    }
+  }
+  if (tid < TILE) scale[tid] = (float)((const bf16*)(stage + STG_SCALE))[tid];
+}
+
+// Common prologue: work item of this workgroup, the empty-split case, the
+// absorbed queries of this lane's head.
+struct WorkItem {
+  int b, s, t0, t1, head;
+  float* po;
+  float* pl;
+};
+
+template <int NW>
+__device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, WorkItem& wi) {
+  int q, g;
+  xcd_map(blockIdx.x, p.G, q, g);
+  if (q >= p.B * p.S) return false;
+  wi.b = __builtin_amdgcn_readfirstlane(q / p.S);
+  wi.s = __builtin_amdgcn_readfirstlane(q - wi.b * p.S);
+  const int len = min(max(__builtin_amdgcn_readfirstlane(p.lengths[wi.b]), 0), p.max_len);
+  wi.t0 = wi.s * p.tokens_per_split;
+  wi.t1 = min(wi.t0 + p.tokens_per_split, len);
+  wi.head = (g * NW + w) * 32 + (l & 31);
+  wi.po = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + wi.head) * D_C + 4 * (l >> 5);
+  wi.pl = p.part_lse + ((int64_t)wi.b * p.S + wi.s) * p.H + wi.head;
+  return true;
+}
+
+__device__ __forceinline__ void write_empty(const WorkItem& wi, int h) {
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) *(f32x4*)(wi.po + 32 * dt + 8 * rq) = f32x4{0, 0, 0, 0};
+  if (h == 0) *wi.pl = -INFINITY;
+}
+
+__device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveState& st, int h) {
+  const float ltot = st.lsum + __shfl_xor(st.lsum, 32, 64);
+  const float inv = 1.0f / ltot;
+#pragma unroll
+  for (int dt = 0; dt < D_C / 32; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
+      *(f32x4*)(wi.po + 32 * dt + 8 * rq) = v * inv;
+    }
+  if (h == 0) *wi.pl = st.m_ref + __builtin_log2f(ltot);
+}
+
+// qpe: this wave's 4 KB of LDS, [k-step][lane][16 bytes]
+__device__ __forceinline__ void load_q(const DecodeParams& p, const WorkItem& wi, int h, int l,
+                                       bf16x8 (&qreg)[QREG], char* qpe) {
+  const bf16* qp = p.q + ((int64_t)wi.b * p.H + wi.head) * D_QK + 8 * h;
+#pragma unroll
+  for (int j = 0; j < QREG; ++j) qreg[j] = *(const bf16x8*)(qp + 16 * j);
+#pragma unroll
+  for (int j = QREG; j < D_QK / 16; ++j)
+    *(bf16x8*)(qpe + (j - QREG) * 1024 + 16 * l) = *(const bf16x8*)(qp + 16 * j);
+}
+
+__device__ __forceinline__ void reset_state(WaveState& st, float m_ref) {
+#pragma unroll
+  for (int dt = 0; dt < D_C / 32; ++dt) st.o[dt] = f32x16{};
+  st.m_ref = m_ref;
+  st.lsum = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 cache: three LDS tile buffers, two tiles of DMA in flight
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_bf16_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char buf0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char buf1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char buf2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * 4096];
+  __shared__ int overflow;
+  constexpr int DMA_PER_TILE = 36 / NW;  // wave-wide loads per tile per wave
+
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  WorkItem wi;
+  if (!work_item<NW>(p, w, l, wi)) return;
+  if (wi.t0 >= wi.t1) {
+    write_empty(wi, h);
+    return;
+  }
+  bf16x8 qreg[QREG];
+  char* qpe = qpe_all + w * 4096;
+  load_q(p, wi, h, l, qreg, qpe);
+  const LaneAddr la = lane_addr(l);
+  WaveState st;
+  reset_state(st, -INFINITY);
+  if (tid == 0) overflow = 0;
+
+  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  // tile k into `tile`; tiles past the split are issued as empty loads
+  auto dma = [&](char* tile, int k) {
+    const bool valid = k < ntiles;
+    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
+    tile_dma<NW>(p, tile, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
+  };
+
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    dma(buf0, 0);
+    dma(buf1, 1);
+    wait_vm_lgkm0<DMA_PER_TILE>();   // tile 0 landed (tile 1 may be in flight)
+    __builtin_amdgcn_s_barrier();
+
+    // phase on buffer X (tile k): refill buffer Z with tile k+2, compute X,
+    // wait for tile k+1, barrier. Phases are predicated rather than exited
+    // early so the accumulators keep one register assignment.
+    auto phase = [&](char* __restrict__ X, char* __restrict__ Z, int k) {
+      dma(Z, k + 2);
+      if (tile_compute<CACHE_BF16>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la, h, st) && l == 0)
+        overflow = 1;
+      wait_vm_lgkm0<DMA_PER_TILE>();  // tile k+1 landed, tile k+2 may be in flight
+      __builtin_amdgcn_s_barrier();
+    };
+    for (int k = 0; k < ntiles; k += 3) {
+      phase(buf0, buf2, k);
+      if (k + 1 < ntiles) phase(buf1, buf0, k + 1);
+      if (k + 2 < ntiles) phase(buf2, buf1, k + 2);
+    }
+    if (overflow == 0) break;
+
+    // Rare path: some score exceeded its head's reference by more than
+    // 2^64. Drain the loads in flight, find each head's true maximum over the
+    // split (scores only), then recompute the split against it.
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    float mtrue = -INFINITY;
+    for (int k = 0; k < ntiles; ++k) {
+      dma(buf0, k);
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      float sv[16];
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16>(buf0, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la, h, sv));
+      __builtin_amdgcn_s_barrier();
+    }
+    reset_state(st, mtrue);
+    if (tid == 0) overflow = 0;
+  }
+  write_partial(wi, st, h);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 cache: the codes of tile k+1 are staged in LDS by DMA while tile k is
+// computed, then widened to bf16 into the other tile buffer
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_fp8_kernel(DecodeParams p) {
+  constexpr int NT = 64 * NW;
+  __shared__ __attribute__((aligned(1024))) char tiles[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage[STG_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * 4096];
+  __shared__ float scl[2][TILE];
+  __shared__ int overflow;
+
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  WorkItem wi;
+  if (!work_item<NW>(p, w, l, wi)) return;
+  if (wi.t0 >= wi.t1) {
+    write_empty(wi, h);
+    return;
+  }
+  bf16x8 qreg[QREG];
+  char* qpe = qpe_all + w * 4096;
+  load_q(p, wi, h, l, qreg, qpe);
+  const LaneAddr la = lane_addr(l);
+  WaveState st;
+  reset_state(st, -INFINITY);
+  if (tid == 0) overflow = 0;
+
+  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  auto dma = [&](int k) {
+    const bool valid = k < ntiles;
+    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
+    fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
+  };
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    dma(0);
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    for (int k = 0; k < ntiles; ++k) {
+      // the stage holds tile k: widen it, then refill the stage with tile k+1
+      // while tile k is computed
+      fp8_tile_widen<NT>(stage, tiles[k & 1], scl[k & 1], tid);
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      dma(k + 1);
+      if (tile_compute<CACHE_FP8>(tiles[k & 1], scl[k & 1], wi.t0 + k * TILE, wi.t1, qreg,
+                                  qpe + 16 * l, la, h, st) && l == 0)
+        overflow = 1;
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+    }
+    if (overflow == 0) break;
+    // rare path (see the bf16 kernel): true maximum, then recompute
+    float mtrue = -INFINITY;
+    for (int k = 0; k < ntiles; ++k) {
+      dma(k);
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      fp8_tile_widen<NT>(stage, tiles[0], scl[0], tid);
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      float sv[16];
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8>(tiles[0], scl[0], wi.t0 + k * TILE, wi.t1,
+                                                   qreg, qpe + 16 * l, la, h, sv));
+      __builtin_amdgcn_s_barrier();
+    }
+    reset_state(st, mtrue);
+    if (tid == 0) overflow = 0;
+  }
+  write_partial(wi, st, h);
+}
+
+}  // namespace mla

@@ -1,0 +1,211 @@
+/*
+ * mla.h: C ABI of an MI355X (gfx950) library for Multi-Head Latent Attention
+ * (MLA) decode over a compressed KV cache.
+ *
+ * The method (sources cited by page title and section):
+ *   - "How DeepSeek Rewrote the Transformer [MLA]" (linuxpro, English
+ *     edition), section "MLA: compress the pair, not the heads": each cached
+ *     token is a 512-wide latent c_KV plus a 64-wide decoupled RoPE key k^R
+ *     (576 numbers per token per layer, independent of the head count); the
+ *     heads rebuild K and V from the latent; by associativity
+ *     Q K^T = (Q W_UK^T) c^T, so W_UK is absorbed into the query and W_UV is
+ *     applied after attention, and attention runs on the latent cache.
+ *   - same page, section "Classic attention and the cost of the KV cache":
+ *     softmax(Q K^T / sqrt(d_k) + M) V with a causal mask M; the new token
+ *     appends its own K/V row and reads the whole history.
+ *   - "DeepSeek AI efficiency, architecture, benchmarks" (technova-ai),
+ *     section "Architectural Innovations: MLA": c_KV = W_DKV h_t,
+ *     K = W_UK c_KV, V = W_UV c_KV.
+ *
+ * Shapes used throughout (the only ones supported): d_c = 512 (latent),
+ * d_rope = 64 (RoPE key), d_nope = 128 (no-RoPE query/key), d_v = 128.
+ *
+ * Conventions
+ *   - All pointers are DEVICE pointers unless stated; the caller owns every
+ *     buffer. The library never allocates or frees device memory.
+ *   - Calls are asynchronous on the given HIP stream; none synchronizes.
+ *   - Host-visible arguments are validated before anything is launched: an
+ *     invalid call returns an error status, launches nothing and leaves all
+ *     outputs untouched. Launch failures return MLA_ERR_HIP.
+ *   - Device-resident integers (lengths, positions, block tables) cannot be
+ *     checked without a sync. Preconditions: 0 <= lengths[b] <= max_len,
+ *     every block id read is in [0, cache_rows / block_size), positions are
+ *     within the cache. Kernels clamp out-of-range values to stay inside the
+ *     buffers (no fault), but the result of such a call is unspecified.
+ *   - Strides are in ELEMENTS. Rows of the latent and RoPE arrays must start
+ *     16-byte aligned (stride * element size a multiple of 16, pointers
+ *     16-byte aligned). A packed 576-wide row (latent | RoPE key) is passed as
+ *     latent = base, rope = base + 512, both with stride 576.
+ *   - The library is stateless apart from a per-device cache of the compute
+ *     unit count; all entry points are thread-safe. Calls that share a
+ *     workspace must be ordered by the caller (same stream).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment */
+  MLA_ERR_UNSUPPORTED = 2,  /* valid request outside what is implemented */
+  MLA_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  MLA_ERR_HIP = 4           /* a HIP call or kernel launch failed */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,       /* IEEE binary32 */
+  MLA_BF16 = 1,      /* bfloat16 */
+  MLA_FP8_E4M3 = 2   /* OCP fp8 e4m3fn codes (cache only), one bf16 scale per row */
+} mla_dtype;
+
+/* Head count and per-head widths. Supported: d_c = 512, d_rope = 64,
+ * d_nope = 128, d_v = 128; heads >= 1 for the f32 path, heads a multiple of
+ * 32 for the bf16 / fp8-cache path. */
+typedef struct {
+  int32_t heads, d_c, d_rope, d_nope, d_v;
+} mla_dims;
+
+/* Optional tuning and instrumentation for the decode calls (pass NULL for the
+ * defaults). Zero fields mean "choose automatically".
+ *   num_splits     number of token ranges each sequence is cut into (split-KV).
+ *   attn_begin/end if non-NULL, HIP events recorded on `stream` immediately
+ *                  before and after the split attention kernel, for timing it. */
+typedef struct {
+  int32_t num_splits;
+  int32_t reserved0;
+  hipEvent_t attn_begin;
+  hipEvent_t attn_end;
+} mla_decode_options;
+
+/* Text for a status code (static storage; never NULL). */
+const char* mla_status_string(mla_status status);
+
+/* Bytes of cache per token per layer: 576 * element size, plus 2 bytes of
+ * scale for the fp8 cache (1152 for bf16, 2304 for f32, 578 for fp8). This is
+ * the MLA row of "How DeepSeek Rewrote the Transformer [MLA]", section
+ * "MLA: compress the pair, not the heads" (576 numbers per token per layer).
+ * Returns 0 for an unknown dtype or non-positive widths. */
+size_t mla_cache_bytes_per_token(mla_dtype cache_dtype, int32_t d_c, int32_t d_rope);
+
+/*
+ * mla_cache_append: write the new token of every sequence into the cache.
+ *
+ * For each b in [0, batch): the latent c_kv[b, 0:512] is stored as is
+ * (converted to the cache type with round-to-nearest-even), and the RoPE key
+ * k_pe[b, 0:64] is rotated by its position p = positions[b] and stored:
+ * interleaved pairs (x[2i], x[2i+1]) turn by angle p * rope_theta^(-2i/64),
+ * p 0-based; the angle and its sine/cosine are computed in double precision,
+ * the rotation is rounded to fp32, then to the cache type. (Source: the
+ * decoupled RoPE key of "How DeepSeek Rewrote the Transformer [MLA]",
+ * section "MLA: compress the pair, not the heads", cached beside the latent;
+ * the pages name RoPE but give no formula, so this standard form is a
+ * documented reading.)
+ *
+ * fp8 cache: the 576 values of the row (latent and rotated key, in fp32) get
+ * one scale s = bf16_rne(amax / 448) (s = 1 if amax == 0; s = 2^-126 if
+ * amax / 448 is below 2^-126), written to scales[row], and each value x is
+ * stored as the e4m3fn code of x / s (fp32 division), rounded to nearest
+ * even and saturated to +-448.
+ *
+ * Arguments
+ *   c_kv       [batch, 512] in in_dtype (MLA_F32 or MLA_BF16), row stride 512
+ *   k_pe       [batch, 64]  in in_dtype, un-rotated, row stride 64
+ *   positions  [batch] int32 (device): 0-based position of the new token
+ *   latent/rope/scales, strides: the cache arrays (scales: fp8 only, else NULL)
+ *   cache_rows total rows of the cache arrays (bounds for the kernel)
+ *   contiguous cache (block_table == NULL): row = b * seq_capacity + p
+ *   paged cache: row = block_table[b * max_blocks_per_seq + p / block_size]
+ *                * block_size + p % block_size
+ *   rope_theta the RoPE base (10000 for the workloads here)
+ * Errors: INVALID_ARG for null/misaligned pointers or bad sizes,
+ * UNSUPPORTED for other dims/dtypes, HIP on launch failure. batch == 0 is a
+ * valid no-op.
+ */
+mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* k_pe,
+                            mla_dtype in_dtype, const int32_t* positions, int32_t batch,
+                            void* latent, int64_t latent_stride, void* rope,
+                            int64_t rope_stride, void* scales, mla_dtype cache_dtype,
+                            int64_t cache_rows, int64_t seq_capacity,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, float rope_theta, hipStream_t stream);
+
+/* Workspace bytes needed by mla_decode / mla_decode_paged for these sizes
+ * (absorbed queries, split partials). 0 on invalid arguments. The split plan
+ * depends on the current device's compute-unit count, so query it on the
+ * device that will run the decode, with the same options. */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_len,
+                                 mla_dtype act_dtype, mla_dtype cache_dtype,
+                                 const mla_decode_options* opts);
+
+/*
+ * mla_decode: one decode step of MLA attention for `batch` sequences over a
+ * contiguous cache (sequence b owns rows [b*seq_capacity, b*seq_capacity +
+ * lengths[b])).
+ *
+ * For every sequence b and head h, with N = lengths[b] (the causal length,
+ * counting the current token once it has been appended):
+ *   q_lat        = q_nope[b,h,:] . W_UK[h]                  (absorbed query)
+ *   s_t          = softmax_scale * (q_lat . c_t + q_pe[b,h,:] . k^R_t), t < N
+ *   out[b,h,:]   = (sum_t softmax(s)_t c_t) . W_UV[h]
+ *   lse[b,h]     = ln sum_t exp(s_t)
+ * which equals softmax attention with keys W_UK[h] c_t | k^R_t and values
+ * c_t W_UV[h] (the non-absorbed form) up to rounding. N == 0 gives out = 0
+ * and lse = -inf.
+ *
+ * Arguments
+ *   q_nope [batch, H, 128], q_pe [batch, H, 64] (already rotated): act_dtype
+ *   w_uk   [H, 128, 512], w_uv [H, 512, 128]: act_dtype, row-major
+ *   act_dtype   MLA_F32 (requires an MLA_F32 cache) or MLA_BF16 (bf16 or fp8
+ *               cache); bf16 math uses bf16 MFMA operands, fp32 accumulation
+ *   latent, rope, strides, scales (fp8 only), cache_dtype: the cache
+ *   cache_rows  total rows of the cache arrays
+ *   lengths     [batch] int32 (device)
+ *   max_len     host upper bound of lengths (sizes the split plan)
+ *   softmax_scale  usually 1/sqrt(d_nope + d_rope)
+ *   out    [batch, H, 128] act_dtype;  lse [batch, H] fp32 or NULL
+ *   workspace   device buffer of at least mla_decode_workspace_size(...)
+ *               bytes (256-byte aligned)
+ *   opts   NULL or tuning/timing options
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP (see above). batch == 0 is
+ * a valid no-op.
+ */
+mla_status mla_decode(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                      const void* w_uk, const void* w_uv, mla_dtype act_dtype,
+                      const void* latent, int64_t latent_stride, const void* rope,
+                      int64_t rope_stride, const void* scales, mla_dtype cache_dtype,
+                      int64_t cache_rows, int64_t seq_capacity, const int32_t* lengths,
+                      int32_t batch, int32_t max_len, float softmax_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes,
+                      const mla_decode_options* opts, hipStream_t stream);
+
+/*
+ * mla_decode_paged: as mla_decode, over a paged cache. Token t of sequence b
+ * lives in row block_table[b * max_blocks_per_seq + t / block_size] *
+ * block_size + t % block_size. block_size must be a positive multiple of 32
+ * (the kernel's token tile). Block-table indexing is exact: the result equals
+ * mla_decode on the same rows laid out contiguously.
+ */
+mla_status mla_decode_paged(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                            const void* w_uk, const void* w_uv, mla_dtype act_dtype,
+                            const void* latent, int64_t latent_stride, const void* rope,
+                            int64_t rope_stride, const void* scales, mla_dtype cache_dtype,
+                            int64_t cache_rows, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t block_size,
+                            const int32_t* lengths, int32_t batch, int32_t max_len,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, const mla_decode_options* opts,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,121 @@
+"""GPU parity of the HIP decode path against the CPU oracle (element-wise on
+the same seeded inputs), through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import LSE_TOL, TOL, gpu_f64, oracle_decode, rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(mla, inp, tol_key, batch_ids=None, heads=None, **kw):
+    dev = inp.to("cuda")
+    print(f"[case] cfg={inp.cfg} B={inp.B} H={inp.H} max_len={inp.max_len} "
+          f"cache={inp.cache_dtype} paged={inp.paged} kw={kw}", flush=True)
+    out, lse = mla.decode_inputs(dev, **kw)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(inp, batch_ids=batch_ids, heads=heads)
+    g = gpu_f64(out)
+    gl = lse.cpu().double().numpy()
+    if batch_ids is not None:
+        g, gl = g[batch_ids], gl[batch_ids]
+    if heads is not None:
+        g, gl = g[:, heads], gl[:, heads]
+        ref, ref_lse = ref[:, heads], ref_lse[:, heads]
+    err = rel_err_rows(g, ref)
+    lerr = float(np.nanmax(np.abs(gl - ref_lse))) if np.isfinite(ref_lse).any() else 0.0
+    print(f"[result] max normwise rel err {err:.3e} (tol {TOL[tol_key]}), lse abs err {lerr:.3e}",
+          flush=True)
+    assert err <= TOL[tol_key], err
+    assert lerr <= LSE_TOL[tol_key], lerr
+    return out, lse
+
+
+def test_config1_fp32_full(gpu):
+    """fp32, B=1, H=16, N=512: every output against the oracle at 1e-4."""
+    run_and_compare(gpu, synth.make_inputs(1), "f32")
+
+
+def test_fp32_ragged_splits(gpu):
+    """fp32 path: ragged lengths, several splits, a tail not a multiple of 32."""
+    lengths = torch.tensor([1, 33, 700, 1500], dtype=torch.int32)
+    inp = synth.make_inputs(1, B=4, N=1500, H=16, lengths=lengths)
+    run_and_compare(gpu, inp, "f32")
+    run_and_compare(gpu, inp, "f32", num_splits=5)
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_bf16_ragged_contiguous(gpu, H):
+    """bf16 MFMA path for each wave count (H/32 = 1, 2, 4 waves per workgroup):
+    lengths 1 (single row), 31 (partial first tile), 33 (tile + 1 row),
+    320 and 1001 (several tiles and a ragged tail)."""
+    lengths = torch.tensor([1, 31, 33, 320, 1001], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=5, N=1001, H=H, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16")
+
+
+def test_bf16_paged_small(gpu):
+    lengths = torch.tensor([64, 65, 130, 1000], dtype=torch.int32)
+    inp = synth.make_inputs(3, B=4, N=1000, lengths=lengths, paged=True)
+    run_and_compare(gpu, inp, "bf16")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 32])
+def test_split_invariance(gpu, splits):
+    """The split-KV merge is an exact re-association of the softmax: every
+    forced split count agrees with the oracle."""
+    lengths = torch.tensor([1024, 700], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=2, N=1024, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16", num_splits=splits)
+
+
+def test_paged_equals_contiguous_bitwise(gpu):
+    """Block-table indexing is exact: the same rows, placed in a permuted
+    pool of 64-token blocks, give bit-identical outputs under the same split
+    plan."""
+    lengths = torch.tensor([1000, 257, 64], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=3, N=1024, lengths=lengths, seq_capacity=1024)
+    bs = 64
+    nb = 1024 // bs
+    perm = torch.randperm(3 * nb, generator=torch.Generator().manual_seed(5))
+    table = perm.view(3, nb).to(torch.int32)
+    pool = torch.empty_like(inp.cache)
+    for b in range(3):
+        for j in range(nb):
+            pool[int(table[b, j]) * bs:(int(table[b, j]) + 1) * bs] = \
+                inp.cache[b * 1024 + j * bs:b * 1024 + (j + 1) * bs]
+    paged = synth.DecodeInputs(**{**inp.__dict__, "cache": pool, "block_table": table,
+                                  "seq_capacity": 0, "block_size": bs})
+    o1, l1 = gpu.decode_inputs(inp.to("cuda"), num_splits=3)
+    o2, l2 = gpu.decode_inputs(paged.to("cuda"), num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_empty_sequence(gpu):
+    """len 0: output 0 and lse = -inf; the other sequence is unaffected."""
+    lengths = torch.tensor([0, 40], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=2, N=64, lengths=lengths)
+    out, lse = gpu.decode_inputs(inp.to("cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(out[0].float() == 0)
+    assert torch.all(torch.isneginf(lse[0]))
+    run_and_compare(gpu, inp, "bf16", batch_ids=[1])
+
+
+def test_fp8_cache_small(gpu):
+    """fp8 e4m3 cache with a bf16 scale per row, compared on the dequantised
+    cache at 3e-2."""
+    lengths = torch.tensor([1, 100, 777], dtype=torch.int32)
+    inp = synth.make_inputs(5, B=3, N=777, lengths=lengths)
+    run_and_compare(gpu, inp, "fp8")
+    run_and_compare(gpu, inp, "fp8", num_splits=4)
+
+
+def test_config2_full(gpu):
+    """bf16, B=1, H=128, N=4096 (DeepSeek-V3 shape): every output."""
+    run_and_compare(gpu, synth.make_inputs(2), "bf16")
