@@ -292,25 +292,23 @@ __device__ __forceinline__ void tile_dma(const DecodeParams& p, char* tile, int6
 // shared. Staging layout: latent [32][512], RoPE key [32][64], scales [32].
 constexpr int STG_ROPE = TILE * D_C;                 // 16384
 constexpr int STG_SCALE = STG_ROPE + TILE * D_R;     // 18432
-constexpr int STG_BYTES = STG_SCALE + 256;           // scale DMA writes 64 lanes x 4 B
+constexpr int STG_BYTES = STG_SCALE + TILE * 4;      // scales as fp32
 
-// Per wave: 16/NW latent loads (two 512-byte rows each) and M loads of the
-// three small pieces (RoPE rows 0-15, RoPE rows 16-31, scales), padded with
-// repeats so that every wave issues the same count.
+// Per wave: 16/NW latent loads (two 512-byte rows each) and the RoPE-key
+// halves (rows 0-15, rows 16-31) spread over the waves. The bf16 row scales
+// are not DMA'd (a dword load could cross the end of an odd-length scale
+// array); lanes 0..31 load them as 2-byte values into a register instead.
 template <int NW>
 struct Fp8Dma {
   static constexpr int LAT = 16 / NW;
-  static constexpr int MISC = (3 + NW - 1) / NW;
-  static constexpr int PER_TILE = LAT + MISC;
+  static constexpr int MISC = (2 + NW - 1) / NW;
 };
 
 template <int NW>
-__device__ __forceinline__ void fp8_tile_dma(const DecodeParams& p, char* stage,
-                                             int64_t base_row, int last_row, int w, int l,
-                                             bool valid) {
+__device__ __forceinline__ float fp8_tile_dma(const DecodeParams& p, char* stage,
+                                              int64_t base_row, int last_row, int w, int l,
+                                              bool valid) {
   const TileRsrc rs = tile_rsrc(p, base_row, 1, valid);
-  base_row = (base_row >= 0 && base_row < p.rows) ? base_row : 0;
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.scales + base_row, valid ? (p.rows - base_row) * 2 : 0);
   const int lsb = (int)p.latent_stride, rsb = (int)p.rope_stride;
 #pragma unroll
   for (int k = 0; k < Fp8Dma<NW>::LAT; ++k) {
@@ -322,20 +320,22 @@ __device__ __forceinline__ void fp8_tile_dma(const DecodeParams& p, char* stage,
   }
 #pragma unroll
   for (int k = 0; k < Fp8Dma<NW>::MISC; ++k) {
-    const int piece = min(w * Fp8Dma<NW>::MISC + k, 2);  // 0, 1: RoPE halves; 2: scales
+    const int piece = w * Fp8Dma<NW>::MISC + k;          // RoPE rows 16*piece ..
     if (piece < 2) {
       const int row = 16 * piece + (l >> 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs.rope, (__attribute__((address_space(3))) void*)(stage + STG_ROPE + piece * 16 * D_R), 16,
           min(row, last_row) * rsb + 16 * (l & 3), 0, 0, 0);
-    } else {
-      // 16 lanes x 4 bytes = 32 bf16 scales (rows past the split re-read
-      // neighbouring scales; those rows are masked)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsc, (__attribute__((address_space(3))) void*)(stage + STG_SCALE), 4,
-          4 * (l & 15), 0, 0, 0);
     }
   }
+  // scale of row (lane) of the tile, wave 0 lanes 0..31
+  float sc = 1.0f;
+  if (w == 0 && l < TILE) {
+    int64_t r = base_row + min(l, last_row);
+    r = (r >= 0 && r < p.rows) ? r : 0;
+    sc = (float)p.scales[r];
+  }
+  return sc;
 }
 
 // Widen one staged tile into a bf16 tile; `scale` receives the row scales.
@@ -376,7 +376,7 @@ __device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, fl
       *(u32x4*)(dst + 16 * ((2 * c + 1) ^ sw)) = hi;
     }
   }
-  if (tid < TILE) scale[tid] = (float)((const bf16*)(stage + STG_SCALE))[tid];
+  if (tid < TILE) scale[tid] = ((const float*)(stage + STG_SCALE))[tid];
 }
 
 // Common prologue: work item of this workgroup, the empty-split case, the
@@ -553,15 +553,22 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   if (tid == 0) overflow = 0;
 
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  float sc_next = 1.0f;
   auto dma = [&](int k) {
     const bool valid = k < ntiles;
     const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
+    sc_next = fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
+  };
+  // the staged tile is complete once the loads landed and the scales are in LDS
+  auto finish_stage = [&]() {
+    wait_vm_lgkm0<0>();
+    if (tid < TILE) ((float*)(stage + STG_SCALE))[tid] = sc_next;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
   };
   for (int attempt = 0; attempt < 2; ++attempt) {
     dma(0);
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
+    finish_stage();
     for (int k = 0; k < ntiles; ++k) {
       // the stage holds tile k: widen it, then refill the stage with tile k+1
       // while tile k is computed
@@ -572,16 +579,14 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       if (tile_compute<CACHE_FP8>(tiles[k & 1], scl[k & 1], wi.t0 + k * TILE, wi.t1, qreg,
                                   qpe + 16 * l, la, h, st) && l == 0)
         overflow = 1;
-      wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
+      finish_stage();
     }
     if (overflow == 0) break;
     // rare path (see the bf16 kernel): true maximum, then recompute
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
       dma(k);
-      wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
+      finish_stage();
       fp8_tile_widen<NT>(stage, tiles[0], scl[0], tid);
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
