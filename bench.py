@@ -1,0 +1,254 @@
+"""Benchmark: one MLA decode step on one MI355X (gfx950).
+
+A step is one pass of the whole hot path over one batch: mla_cache_append
+(the new token of every sequence, RoPE on its key) then mla_decode_paged
+(absorb GEMM, split-KV flash decode over the latent+RoPE cache, merge of the
+splits and the W_UV projection). Workload: 64 sequences, 128 heads, 4096
+cached tokens each (the new one included), DeepSeek-V3 widths, bf16, paged
+cache of 64-token blocks placed by a seeded random permutation.
+
+Inputs are resident in HBM before the timed region. Steps cycle over three
+independent layers (own weights, queries and cache, ~1 GB in total) so that
+a step never finds its cache in the 256 MB last-level cache left by the
+previous step, as in a real model where the other layers run in between.
+
+Prints ONE JSON line (see the fields below). Options:
+  --steps K --warmup W     timed and untimed steps (defaults 50 / 10)
+  --gpus N                 only N = 1 is supported (one process, one GPU)
+  --no-cpu                 skip the CPU-oracle baseline leg
+  --config NAME            3u (default), 3, 4 or 5 (other workloads, for study)
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), B=64 H=128 N=4096"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+N_LAYERS_CYCLED = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--config", default="3u")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs from libamdhip64 (the decode call records them around
+    the split attention kernel on its own stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "head_latent_attention_07_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, per_launch_bytes: float):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"mla_decode_bf16_kernel_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds: float):
+    """The oracle as it stands (float64, non-absorbed), on a bounded sample of
+    the same workload: whole sequences (all heads) until `seconds` elapse."""
+    import numpy as np
+    import synth
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = synth.make_inputs(cfg)
+
+    def f64(t, kind):
+        return orc.decode_storage(synth.raw_bits(t), kind)
+
+    wuk, wuv = f64(inp.w_uk, "bf16"), f64(inp.w_uv, "bf16")
+    table = None if inp.block_table is None else inp.block_table.numpy()
+    done = 0
+    tokens = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % inp.B
+        n = int(inp.lengths[b])
+        rows = orc.gather_rows(b, n, seq_capacity=inp.seq_capacity, block_table=table,
+                               block_size=inp.block_size)
+        import torch
+        vals = f64(inp.cache[torch.from_numpy(rows)], inp.cache_dtype)
+        orc.decode(f64(inp.q_nope[b:b + 1], "bf16"), f64(inp.q_pe[b:b + 1], "bf16"), wuk, wuv,
+                   [vals[:, :512]], [vals[:, 512:]], inp.scale)
+        done += 1
+        tokens += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} sequence(s) x 128 heads of the same workload (N={inp.max_len}), "
+                      f"float64 non-absorbed oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (one process, no collectives); "
+              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_07_amd as mla
+    import synth
+
+    mla.load()
+    cfg = args.config if args.config in ("3u", "3", "4", "5") else "3u"
+    cfg = cfg if cfg == "3u" else int(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (resident in HBM), one set per cycled layer ----
+    layers = []
+    for layer in range(N_LAYERS_CYCLED):
+        gen = "cuda" if cfg == 5 else "cpu"
+        inp = synth.make_inputs(cfg, layer=layer, gen_device=gen).to(dev)
+        lat, rope = mla.split_cache(inp.cache)
+        B, H = inp.B, inp.H
+        # the new token of each sequence sits at position N_b - 1
+        c_new, k_new = synth.append_inputs(7000 + layer, B, "bf16", device=dev)
+        pos = (inp.lengths - 1).to(dev)
+        cdt = mla.dtype_code(inp.cache.dtype)
+        ws = torch.empty(mla.workspace_size(H, B, inp.max_len, mla.MLA_BF16, cdt),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        layers.append(dict(inp=inp, lat=lat, rope=rope, c=c_new, k=k_new, pos=pos, ws=ws,
+                           out=out, lse=lse))
+    torch.cuda.synchronize()
+    inp0 = layers[0]["inp"]
+    B, H = inp0.B, inp0.H
+    tok_rows = int(inp0.lengths.sum())
+    row_bytes = mla.cache_bytes_per_token(mla.dtype_code(inp0.cache.dtype))
+    cache_bytes = tok_rows * row_bytes                  # algorithmic bytes per launch
+    flop_attn = tok_rows * (2 * H * 576 + 2 * H * 512)  # QK^T + PV per launch
+
+    ev = HipEvents()
+
+    def step(L, events=None):
+        inp = L["inp"]
+        mla.cache_append(L["c"], L["k"], L["pos"], L["lat"], L["rope"], heads=H,
+                         scales=inp.scales, seq_capacity=inp.seq_capacity,
+                         block_table=inp.block_table, block_size=inp.block_size)
+        mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events)
+
+    for i in range(args.warmup):
+        step(layers[i % N_LAYERS_CYCLED])
+    torch.cuda.synchronize()
+
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(layers[i % N_LAYERS_CYCLED], events=pairs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = B * args.steps / (t1 - t0)
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    achieved_gbs = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
+    workload = {"3u": "mla_decode_b64_h128_n4096_paged_bf16",
+                3: "mla_decode_b64_h128_ragged1024to4096_paged_bf16",
+                4: "mla_decode_b4_h128_n131072_bf16",
+                5: "mla_decode_b32_h128_n32768_fp8cache_per_layer"}[cfg]
+    traffic = measured_traffic(str(cfg), cache_bytes)
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp0.cache_dtype == "bf16" else "bf16+fp8cache",
+        "data": "synthetic (seeded normals; random-init weights of the DeepSeek-V3 MLA widths)",
+        "config": {"workload": workload, "B": B, "H": H, "N_max": inp0.max_len,
+                   "cache_token_rows": tok_rows, "paged": inp0.paged,
+                   "block_size": inp0.block_size if inp0.paged else None,
+                   "d_c": 512, "d_rope": 64, "d_nope": 128, "d_v": 128,
+                   "layers_cycled": N_LAYERS_CYCLED},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "mla_decode_bf16_kernel" if inp0.cache_dtype == "bf16"
+                     else "mla_decode_fp8_kernel",
+                     "bytes_per_launch": cache_bytes, "avg_launch_us": attn_avg_ms * 1e3},
+        "latent_cache_gbs": achieved_gbs,
+        "latent_cache_pct_of_hbm_peak": 100.0 * achieved_gbs / HBM_PEAK_GBS,
+        "attention_mfma_tflops": flop_attn / (attn_avg_ms * 1e-3) / 1e12,
+        "attention_mfma_frac_of_bf16_peak": flop_attn / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "step_cache_gbs": cache_bytes / (ms_per_step * 1e-3) / 1e9,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg if cfg != 5 else 5, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
