@@ -71,14 +71,20 @@ constexpr int TILE_BYTES = ROPE_OFF + TILE * ROPE_ROW;  // 36864
 // The absorbed query of a lane's head is the QK^T B operand: its 32 latent
 // k-steps stay in registers (128 VGPRs), its 4 RoPE k-steps are read from
 // LDS (4 KB per wave), which leaves the register file room for the rest.
-constexpr int QREG = D_C / 16;
+constexpr int QREG = D_C / 16;           // k-steps of Q held in registers
+constexpr int QLDS = D_QK / 16 - QREG;   // k-steps of Q read from LDS (the RoPE part)
 
-// Swizzle of the 16-byte chunk index inside an LDS row (XOR on its low three
-// bits). Rows r..r+7 map a given chunk to 8 distinct 16-byte bank groups
-// (ds_read_b128 of 8 tokens at one column), and rows 4k..4k+3 map an aligned
-// pair of chunks to 4 distinct 32-byte bank groups (ds_read_b64_tr_b16 of 4
-// tokens), since the pair index is XORed with r mod 4.
-__device__ __forceinline__ int row_swizzle(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// LDS swizzles (gfx950 LDS: 64 banks of 4 bytes, 256 bytes per cycle).
+// Latent rows are 1 KB (64 chunks of 16 bytes); chunk c of row r is stored at
+// c ^ lat_swz(r), an XOR on the low four bits, so that
+//   * a ds_read_b128 of one chunk from 16 consecutive rows (QK^T A operand,
+//     16 lanes per cycle) touches 16 distinct 16-byte bank groups, and
+//   * a ds_read_b64_tr_b16 of 64 bytes from each of 4 consecutive rows (PV A
+//     operand, 32 lanes per cycle) touches 4 distinct 64-byte bank groups.
+// RoPE-key rows are 128 bytes (8 chunks), chunk c of row r at c ^ rope_swz(r):
+// 16 consecutive rows then cover the 256 bytes of banks exactly once.
+__device__ __forceinline__ int lat_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+__device__ __forceinline__ int rope_swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
 // this wave's LDS traffic is done and at most N of its global loads remain.
@@ -89,30 +95,34 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // Per-lane LDS byte offsets of the MFMA operand reads (relative to a tile).
-// QK^T A operand, k-step j: latent j < 32 at qb[j & 3] + 128 (j >> 2), RoPE
-// key j >= 32 at rb[j - 32]. PV A operand (transposing read) for 32-dim tile
-// dt: tb[dt & 1] + 128 (dt >> 1), +8 rows for the upper 4 tokens, +16 rows
-// for the second 16-token k-step.
+// QK^T A operand, k-step j: latent (j < 32) at qb[j & 7] + 256 (j >> 3),
+// RoPE key (j >= 32) at rb[j - 32]. PV A operand (transposing read) for
+// 32-dim tile dt and 16-token k-step ks: lower 4 tokens at
+// tb[0][dt & 3] + 256 (dt >> 2) + 16 KB ks, upper 4 tokens (8 rows further)
+// at tb[1][...] (the swizzle of row+8 differs from that of row).
 struct LaneAddr {
-  int qb[4];
+  int qb[8];
   int rb[4];
-  int tb[2];
+  int tb[2][4];
 };
 
 __device__ __forceinline__ LaneAddr lane_addr(int l) {
   LaneAddr a;
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
-  const int sw = row_swizzle(l32);
+  const int sw = lat_swz(l32), rsw = rope_swz(l32);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    a.qb[k] = l32 * LAT_ROW + 16 * ((2 * k + h) ^ sw);
-    a.rb[k] = ROPE_OFF + l32 * ROPE_ROW + 16 * ((2 * k + h) ^ sw);
-  }
+  for (int k = 0; k < 8; ++k) a.qb[k] = l32 * LAT_ROW + 16 * ((2 * k + h) ^ sw);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a.rb[k] = ROPE_OFF + l32 * ROPE_ROW + 16 * ((2 * k + h) ^ rsw);
   const int row1 = 4 * h + (jj >> 2);
-  const int x = (2 * (g16 & 1) + ((jj & 3) >> 1)) ^ row_swizzle(row1);
-  const int phi = (x >> 2) & 1, low = x & 3;
-  a.tb[0] = row1 * LAT_ROW + 64 * phi + 16 * low + 8 * (jj & 1);
-  a.tb[1] = row1 * LAT_ROW + 64 * (1 - phi) + 16 * low + 8 * (jj & 1);
+  const int cbase = 2 * (g16 & 1) + ((jj & 3) >> 1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = row1 + 8 * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a.tb[u][e] = row * LAT_ROW + 16 * ((4 * e + cbase) ^ lat_swz(row)) + 8 * (jj & 1);
+  }
   return a;
 }
 
@@ -139,20 +149,31 @@ struct WaveState {
   float lsum;           // this lane's share of the softmax denominator
 };
 
-// S^T = K Q^T for one tile; returns this lane's 16 scores (masked, scaled for
-// fp8) and the tile max of this lane's head.
+// S^T = K Q^T for one tile; returns this lane's 16 scores (masked, scaled
+// for fp8) and the tile max of this lane's head. The A operands are read from
+// LDS three k-steps ahead of the MFMA that consumes them (a software pipeline
+// pinned with scheduling barriers), so LDS latency overlaps the MFMA chain.
 template <int CK>
 __device__ __forceinline__ float tile_scores(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG],
                                              const char* qpe, const LaneAddr& la, int h,
                                              float (&sv)[16]) {
+  constexpr int NJ = D_QK / 16;   // 36 k-steps
+  constexpr int AHEAD = 3;
+  auto a_off = [&](int j) { return (j < 32) ? la.qb[j & 7] + 256 * (j >> 3) : la.rb[j - 32]; };
+  bf16x8 ring[AHEAD + 1];
+  bf16x8 qring[QLDS];
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j) ring[j] = *(const bf16x8*)(tile + a_off(j));
   f32x16 sacc = f32x16{};
 #pragma unroll
-  for (int j = 0; j < D_QK / 16; ++j) {
-    const int off = (j < 32) ? la.qb[j & 3] + 128 * (j >> 2) : la.rb[j - 32];
-    const bf16x8 a = *(const bf16x8*)(tile + off);
-    const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : *(const bf16x8*)(qpe + (j - QREG) * 1024);
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, sacc, 0, 0, 0);
+  for (int j = 0; j < NJ; ++j) {
+    if (j + AHEAD < NJ) ring[(j + AHEAD) % (AHEAD + 1)] = *(const bf16x8*)(tile + a_off(j + AHEAD));
+    if (j + AHEAD >= QREG && j + AHEAD < NJ)
+      qring[j + AHEAD - QREG] = *(const bf16x8*)(qpe + (j + AHEAD - QREG) * 1024);
+    const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : qring[j < QREG ? 0 : j - QREG];
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j % (AHEAD + 1)], bq, sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // accumulator row r of this lane is token 8(r/4) + 4h + r%4 of the tile
   float tmax = -INFINITY;
@@ -175,6 +196,16 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
                                              const LaneAddr& la, int h, WaveState& st) {
   float sv[16];
   const float tmax = tile_scores<CK>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv);
+  // PV operands: 32 steps (2 k-steps x 16 dim tiles), two ahead
+  constexpr int NS = 32, AHEAD = 2;
+  auto v_op = [&](int s) {
+    const int ks = s >> 4, dt = s & 15;
+    const int off = 256 * (dt >> 2) + ks * 16 * LAT_ROW;
+    return lds_tr8(tile + la.tb[0][dt & 3] + off, tile + la.tb[1][dt & 3] + off);
+  };
+  bf16x8 ring[AHEAD + 1];
+#pragma unroll
+  for (int s = 0; s < AHEAD; ++s) ring[s] = v_op(s);
   st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
   const bool ovf = __any(tmax > st.m_ref + OVERFLOW_SLACK);
   bf16x8 pb[2];
@@ -185,14 +216,13 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
     if (CK == CACHE_FP8) e *= scale[8 * (r >> 2) + 4 * h + (r & 3)];
     pb[r >> 3][r & 7] = (bf16)e;
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-    for (int dt = 0; dt < D_C / 32; ++dt) {
-      const char* p = tile + la.tb[dt & 1] + 128 * (dt >> 1) + ks * 16 * LAT_ROW;
-      const bf16x8 a = lds_tr8(p, p + 8 * LAT_ROW);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], st.o[dt], 0, 0, 0);
-    }
+  for (int s = 0; s < NS; ++s) {
+    if (s + AHEAD < NS) ring[(s + AHEAD) % (AHEAD + 1)] = v_op(s + AHEAD);
+    const int dt = s & 15;
+    st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % (AHEAD + 1)], pb[s >> 4], st.o[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   return ovf;
 }
@@ -263,25 +293,25 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const DecodeParams& p, int64_t bas
 template <int NW>
 __device__ __forceinline__ void tile_dma(const DecodeParams& p, char* tile, int64_t base_row,
                                          int last_row, int w, int l, bool valid) {
-  constexpr int RPW = TILE / NW;   // latent rows per wave (a multiple of 8)
+  constexpr int RPW = TILE / NW;   // latent rows per wave
   constexpr int GPW = 4 / NW;      // RoPE-key row groups per wave
   const TileRsrc rs = tile_rsrc(p, base_row, 2, valid);
   const int lsb = (int)(p.latent_stride * 2), rsb = (int)(p.rope_stride * 2);
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
-    const int u = w * RPW + k;     // u % 8 == k % 8: the swizzle is a constant
+    const int u = w * RPW + k;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs.lat, (__attribute__((address_space(3))) void*)(tile + u * LAT_ROW), 16,
-        16 * (l ^ row_swizzle(k)), min(u, last_row) * lsb, 0, 0);
+        16 * (l ^ lat_swz(u)), min(u, last_row) * lsb, 0, 0);
   }
   const int lrow = l >> 3;
-  const int lchunk = 16 * ((l & 7) ^ row_swizzle(lrow));
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
     const int v = w * GPW + k;
+    const int row = 8 * v + lrow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs.rope, (__attribute__((address_space(3))) void*)(tile + ROPE_OFF + v * 8 * ROPE_ROW), 16,
-        min(8 * v + lrow, last_row) * rsb + lchunk, 0, 0, 0);
+        min(row, last_row) * rsb + 16 * ((l & 7) ^ rope_swz(row)), 0, 0, 0);
   }
 }
 
@@ -371,7 +401,7 @@ __device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, fl
         hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, false));
         hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, true));
       }
-      const int sw = row_swizzle(row);
+      const int sw = (q < TILE * (D_C / 16)) ? lat_swz(row) : rope_swz(row);
       *(u32x4*)(dst + 16 * ((2 * c) ^ sw)) = lo;
       *(u32x4*)(dst + 16 * ((2 * c + 1) ^ sw)) = hi;
     }
@@ -451,7 +481,7 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char buf0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf2[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * 4096];
+  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   __shared__ int overflow;
   constexpr int DMA_PER_TILE = 36 / NW;  // wave-wide loads per tile per wave
 
@@ -532,7 +562,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(1024))) char tiles[2][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage[STG_BYTES];
-  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * 4096];
+  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   __shared__ float scl[2][TILE];
   __shared__ int overflow;
 

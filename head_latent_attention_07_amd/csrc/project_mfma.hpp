@@ -27,91 +27,113 @@ __device__ __forceinline__ bf16x8 tr_read_8(const char* p_lo, const char* p_hi) 
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// Buffer resource for raw buffer loads (bounds-checked: reads past `bytes`
+// return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t proj_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = (int32_t)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+}
+
+// XOR swizzle of 16-byte chunks within a 1 KB weight row in LDS (same scheme
+// as the attention tiles): ds_read_b64_tr_b16 over 4 consecutive rows hits 4
+// distinct 32-byte bank groups.
+__device__ __forceinline__ int wrow_swizzle(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
 // ----------------------------------------------------------------------------
-// absorb: one workgroup (4 waves) per (head, chunk of 32 sequences)
+// absorb: one workgroup (4 waves) per head; W_UK[h] (128 rows x 1 KB) is
+// brought into LDS whole by direct-to-LDS loads, then every chunk of 32
+// sequences is multiplied against it.
 // ----------------------------------------------------------------------------
 struct AbsorbParams {
   const bf16* q_nope;  // [B, H, 128]
   const bf16* q_pe;    // [B, H, 64]
   const bf16* w_uk;    // [H, 128, 512]
   bf16* q;             // [B, H, 576]
-  int B, H, nbc;       // nbc = number of 32-sequence chunks
+  int B, H, nbc;       // nbc: unused (kept for the launch code)
   float c;             // softmax_scale * log2(e)
 };
 
-constexpr int AB_KC = 32;                  // W_UK rows per LDS stage
-constexpr int AB_WPITCH = D_C * 2 + 32;    // 1056 B: 4 rows' 32-byte spans hit distinct banks
 constexpr int AB_APITCH = D_N * 2 + 16;    // 272 B: 8 rows' 16-byte chunks hit distinct banks
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_N * D_C * 2];   // 128 KB
   __shared__ __attribute__((aligned(16))) char a_lds[32 * AB_APITCH];
-  __shared__ __attribute__((aligned(16))) char w_lds[AB_KC * AB_WPITCH];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
-  // the nbc chunks of one head share its W_UK rows: keep them on one XCD
-  int head, bc;
+  const int head = blockIdx.x;
+  if (head >= p.H) return;
+
+  // W_UK[h]: 128 rows of 1 KB, one wave-wide 16-byte-per-lane load per row
   {
-    const int x = blockIdx.x;
-    const int q_lo = x & 7, rest = x >> 3;
-    bc = rest % p.nbc;
-    head = (rest / p.nbc) * 8 + q_lo;
-    if (head >= p.H) return;
-  }
-  const int b0 = bc * 32;
-
-  // q_nope rows of the chunk -> LDS (zero rows past B); q_pe scaled copy
-  for (int i = tid; i < 32 * (D_N / 8); i += 256) {
-    const int r = i / (D_N / 8), c = i % (D_N / 8);
-    u32x4 v = {0, 0, 0, 0};
-    if (b0 + r < p.B) v = *(const u32x4*)(p.q_nope + ((int64_t)(b0 + r) * p.H + head) * D_N + 8 * c);
-    *(u32x4*)(a_lds + r * AB_APITCH + 16 * c) = v;
-  }
-  for (int i = tid; i < 32 * D_R; i += 256) {
-    const int r = i / D_R, c = i % D_R;
-    if (b0 + r < p.B) {
-      const int64_t bh = (int64_t)(b0 + r) * p.H + head;
-      p.q[bh * D_QK + D_C + c] = (bf16)((float)p.q_pe[bh * D_R + c] * p.c);
+    const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uk + (int64_t)head * D_N * D_C, D_N * D_C * 2);
+#pragma unroll
+    for (int k = 0; k < D_N / 4; ++k) {
+      const int row = w * (D_N / 4) + k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(w_lds + row * 1024), 16,
+          16 * (l ^ wrow_swizzle(row)), row * 1024, 0, 0);
     }
   }
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
-  const bf16* wsrc = p.w_uk + (int64_t)head * D_N * D_C;
-  for (int k0 = 0; k0 < D_N; k0 += AB_KC) {
-    __syncthreads();
-    for (int i = tid; i < AB_KC * (D_C / 8); i += 256) {
-      const int r = i / (D_C / 8), c = i % (D_C / 8);
-      *(u32x4*)(w_lds + r * AB_WPITCH + 16 * c) = *(const u32x4*)(wsrc + (int64_t)(k0 + r) * D_C + 8 * c);
+  // tr-read bases for this lane's B operand
+  const int r1 = 8 * h + (jj >> 2);                    // + 16 ks, and + 4 for the upper half
+  const int cx = (2 * (g16 & 1) + ((jj & 3) >> 1));    // chunk low bits before the swizzle
+  for (int b0 = 0; b0 < p.B; b0 += 32) {
+    // q_nope rows of the chunk -> LDS (zero rows past B); q_pe scaled copy
+    for (int i = tid; i < 32 * (D_N / 8); i += 256) {
+      const int r = i / (D_N / 8), c = i % (D_N / 8);
+      u32x4 v = {0, 0, 0, 0};
+      if (b0 + r < p.B) v = *(const u32x4*)(p.q_nope + ((int64_t)(b0 + r) * p.H + head) * D_N + 8 * c);
+      *(u32x4*)(a_lds + r * AB_APITCH + 16 * c) = v;
     }
-    __syncthreads();
+    {
+      // q_pe: 8 consecutive values per thread (32 rows x 64)
+      const int r = tid >> 3, c = 8 * (tid & 7);
+      if (b0 + r < p.B) {
+        const int64_t bh = (int64_t)(b0 + r) * p.H + head;
+        const bf16x8 v = *(const bf16x8*)(p.q_pe + bh * D_R + c);
+        bf16x8 o;
 #pragma unroll
-    for (int ks = 0; ks < AB_KC / 16; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(a_lds + l32 * AB_APITCH + 2 * (k0 + 16 * ks + 8 * h));
-      const int r1 = 16 * ks + 8 * h + (jj >> 2);
+        for (int k = 0; k < 8; ++k) o[k] = (bf16)((float)v[k] * p.c);
+        *(bf16x8*)(p.q + bh * D_QK + D_C + c) = o;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK landed (first chunk)
+    __syncthreads();
+    f32x16 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D_N / 16; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(a_lds + l32 * AB_APITCH + 2 * (16 * ks + 8 * h));
+      const int ra = 16 * ks + r1, rb = ra + 4;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int col = 32 * (4 * w + nt) + 16 * (g16 & 1) + 4 * (jj & 3);
-        const bf16x8 bop = tr_read_8(w_lds + r1 * AB_WPITCH + 2 * col,
-                                     w_lds + (r1 + 4) * AB_WPITCH + 2 * col);
+        const int chunk = 4 * (4 * w + nt) + cx;
+        const int off = 8 * (jj & 1);
+        const bf16x8 bop = tr_read_8(w_lds + ra * 1024 + 16 * (chunk ^ wrow_swizzle(ra)) + off,
+                                     w_lds + rb * 1024 + 16 * (chunk ^ wrow_swizzle(rb)) + off);
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[nt], 0, 0, 0);
       }
     }
-  }
-  // lane holds column n, rows b = 8(r/4) + 4h + r%4
+    // lane holds column n, rows b = 8(r/4) + 4h + r%4
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = 32 * (4 * w + nt) + l32;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = 32 * (4 * w + nt) + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (bb < p.B) p.q[((int64_t)bb * p.H + head) * D_QK + n] = (bf16)(acc[nt][r] * p.c);
+      for (int r = 0; r < 16; ++r) {
+        const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (bb < p.B) p.q[((int64_t)bb * p.H + head) * D_QK + n] = (bf16)(acc[nt][r] * p.c);
+      }
     }
+    __syncthreads();   // a_lds is rewritten by the next chunk
   }
 }
 
 // ----------------------------------------------------------------------------
-// combine + W_UV: one workgroup (4 waves) per (head, chunk of 32 sequences)
+// merge + W_UV: one workgroup (4 waves) per head; W_UV[h] (512 rows x 256 B)
+// is brought into LDS whole by direct-to-LDS loads while the splits of the
+// first chunk of 32 sequences are merged.
 // ----------------------------------------------------------------------------
 struct CombineParams {
   const float* part_o;    // [B, S, H, 512]
@@ -122,15 +144,16 @@ struct CombineParams {
   int B, H, S, nbc;
 };
 
-constexpr int CB_KC = 64;                   // W_UV rows per LDS stage
-constexpr int CB_WPITCH = D_V * 2 + 32;     // 288 B
-constexpr int CB_APITCH = D_C * 2 + 16;     // 1040 B
+constexpr int CB_APITCH = D_C + 16;         // 528 B: half a merged row (256 dims) + pad
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
-  __shared__ __attribute__((aligned(16))) char a_lds[32 * CB_APITCH];
-  __shared__ __attribute__((aligned(16))) char w_lds[CB_KC * CB_WPITCH];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_C * D_V * 2];   // 128 KB
+  __shared__ __attribute__((aligned(16))) char a_lds[32 * CB_APITCH];    // 32 seq x 256 dims
+  __shared__ float lmax[32], winv[32];   // per sequence of the chunk: max lse, 1/sum of weights
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
+  // (head, chunk of 32 sequences); the chunks of one head share an XCD (L2)
   int head, bc;
   {
     const int x = blockIdx.x;
@@ -139,61 +162,77 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
     head = (rest / p.nbc) * 8 + q_lo;
     if (head >= p.H) return;
   }
-  const int b0 = bc * 32;
-
-  // merge the splits of the 32 sequences into a bf16 A tile: o_lat[b][0:512]
-  for (int r = 0; r < 32; ++r) {
-    const int b = b0 + r;
-    float2 acc = {0.f, 0.f};
-    if (b < p.B) {
-      const float* lse_s = p.part_lse + (int64_t)b * p.S * p.H + head;
-      float L = -INFINITY;
-      for (int s = 0; s < p.S; ++s) L = fmaxf(L, lse_s[(int64_t)s * p.H]);
-      if (L > -INFINITY) {
-        float wsum = 0.f;
-        for (int s = 0; s < p.S; ++s) {
-          const float ls = lse_s[(int64_t)s * p.H];
-          const float wgt = fast_exp2(ls - L);
-          wsum += wgt;
-          const float2 v = *(const float2*)(p.part_o + (((int64_t)b * p.S + s) * p.H + head) * D_C + 2 * tid);
-          acc.x += wgt * v.x;
-          acc.y += wgt * v.y;
-        }
-        const float inv = 1.0f / wsum;
-        acc.x *= inv;
-        acc.y *= inv;
-        if (tid == 0 && p.lse) p.lse[(int64_t)b * p.H + head] = (L + __builtin_log2f(wsum)) * LN2;
-      } else if (tid == 0 && p.lse) {
-        p.lse[(int64_t)b * p.H + head] = -INFINITY;
+  {
+    const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {   // 128 lines of 1 KB (4 rows each), 32 per wave
+      const int line = w * 32 + k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(w_lds + line * 1024), 16, 16 * l,
+          line * 1024, 0, 0);
+    }
+  }
+  const int colb = 32 * w + 16 * (g16 & 1) + 4 * (jj & 3);   // B-operand column base
+  {
+    const int b0 = bc * 32;
+    // merge weights: per sequence, 2^(lse_s - L) / sum over splits
+    if (tid < 32) {
+      const int b = b0 + tid;
+      float L = -INFINITY, wsum = 0.f;
+      if (b < p.B) {
+        const float* ls = p.part_lse + (int64_t)b * p.S * p.H + head;
+        for (int s = 0; s < p.S; ++s) L = fmaxf(L, ls[(int64_t)s * p.H]);
+        if (L > -INFINITY)
+          for (int s = 0; s < p.S; ++s) wsum += fast_exp2(ls[(int64_t)s * p.H] - L);
+        if (p.lse)
+          p.lse[(int64_t)b * p.H + head] =
+              (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
       }
-    }
-    bf16x2 pk = {(bf16)acc.x, (bf16)acc.y};
-    *(bf16x2*)(a_lds + r * CB_APITCH + 4 * tid) = pk;
-  }
-
-  f32x16 acc = f32x16{};
-  const bf16* wsrc = p.w_uv + (int64_t)head * D_C * D_V;
-  for (int k0 = 0; k0 < D_C; k0 += CB_KC) {
-    __syncthreads();
-    for (int i = tid; i < CB_KC * (D_V / 8); i += 256) {
-      const int r = i / (D_V / 8), c = i % (D_V / 8);
-      *(u32x4*)(w_lds + r * CB_WPITCH + 16 * c) = *(const u32x4*)(wsrc + (int64_t)(k0 + r) * D_V + 8 * c);
+      winv[tid] = (L > -INFINITY) ? 1.0f / wsum : 0.0f;
+      lmax[tid] = L;
     }
     __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < CB_KC / 16; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(a_lds + l32 * CB_APITCH + 2 * (k0 + 16 * ks + 8 * h));
-      const int r1 = 16 * ks + 8 * h + (jj >> 2);
-      const int col = 32 * w + 16 * (g16 & 1) + 4 * (jj & 3);
-      const bf16x8 bop = tr_read_8(w_lds + r1 * CB_WPITCH + 2 * col, w_lds + (r1 + 4) * CB_WPITCH + 2 * col);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+    f32x16 acc = f32x16{};
+    for (int half = 0; half < 2; ++half) {
+      // thread: dims half*256 + 4*(tid%64) .. +3 of sequences b0 + tid/64 + 4i
+      const int d4 = tid & 63;
+#pragma unroll 2
+      for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 6) + 4 * i;
+        const int b = b0 + r;
+        f32x4 m = {0.f, 0.f, 0.f, 0.f};
+        if (b < p.B && winv[r] > 0.f) {
+          const float L = lmax[r];
+          const float* ls = p.part_lse + (int64_t)b * p.S * p.H + head;
+          const float* po = p.part_o + ((int64_t)b * p.S * p.H + head) * D_C + half * 256 + 4 * d4;
+#pragma unroll 4
+          for (int s = 0; s < p.S; ++s) {
+            const float wgt = fast_exp2(ls[(int64_t)s * p.H] - L);
+            const f32x4 v = *(const f32x4*)(po + (int64_t)s * p.H * D_C);
+            m += wgt * v;
+          }
+          m *= winv[r];
+        }
+        bf16x4 pk = {(bf16)m[0], (bf16)m[1], (bf16)m[2], (bf16)m[3]};
+        *(bf16x4*)(a_lds + r * CB_APITCH + 8 * d4) = pk;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UV landed (first pass)
+      __syncthreads();
+#pragma unroll 4
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(a_lds + l32 * CB_APITCH + 2 * (16 * ks + 8 * h));
+        const int ra = half * 256 + 16 * ks + 8 * h + (jj >> 2);
+        const bf16x8 bop = tr_read_8(w_lds + ra * 256 + 2 * colb, w_lds + (ra + 4) * 256 + 2 * colb);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+      }
+      __syncthreads();   // a_lds is rewritten next
     }
-  }
-  const int n = 32 * w + l32;
+    const int n = 32 * w + l32;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)acc[r];
+    for (int r = 0; r < 16; ++r) {
+      const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)acc[r];
+    }
   }
 }
 
