@@ -17,6 +17,9 @@ Prints ONE JSON line (see the fields below). Options:
   --gpus N                 only N = 1 is supported (one process, one GPU)
   --no-cpu                 skip the CPU-oracle baseline leg
   --config NAME            3u (default), 3, 4 or 5 (other workloads, for study)
+  --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
+                           five times (the reference kernel that scales the
+                           HBM byte counters of a profiler run) and exit
 """
 
 from __future__ import annotations
@@ -47,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", default="3u")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0)
     return ap.parse_args()
 
 
@@ -139,8 +143,26 @@ def cpu_baseline(cfg, seconds: float):
                       f"float64 non-absorbed oracle, {dt:.1f} s"}
 
 
+def copy_calibration(mib: int):
+    """A plain copy of known size: each launch reads and writes exactly
+    mib MiB, so a profiler's HBM read/write counters for it give the factor
+    between counted and true bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only (one process, no collectives); "

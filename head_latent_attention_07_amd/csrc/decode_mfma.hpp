@@ -227,14 +227,15 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
   return ovf;
 }
 
-// Map a flat workgroup id to (sequence*split index q, head group g) so that
-// the G workgroups reading the same rows land on the same XCD (workgroups are
-// dispatched round-robin over the 8 XCDs, each with its own L2).
-__device__ __forceinline__ void xcd_map(int x, int G, int& q, int& g) {
-  const int q_lo = x & 7;
+// Map a flat workgroup id to (sequence*split index q, head group g).
+// Workgroups are dispatched round-robin over the 8 XCDs (x mod 8), each with
+// its own L2; every XCD gets a contiguous range of q, so the head groups and
+// the splits of one sequence (which share its queries and rows) run on the
+// same XCD. `per` = ceil(B*S / 8); the grid is 8 * per * G workgroups.
+__device__ __forceinline__ void xcd_map(int x, int G, int per, int& q, int& g) {
   const int rest = x >> 3;
   g = rest % G;
-  q = (rest / G) * 8 + q_lo;
+  q = (x & 7) * per + rest / G;
 }
 
 // Scalar (SMEM) load of a wave-uniform int. A plain load placed after the
@@ -413,14 +414,15 @@ __device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, fl
 // absorbed queries of this lane's head.
 struct WorkItem {
   int b, s, t0, t1, head;
-  float* po;
+  float* po;        // this lane's head row (+4 floats for the upper half-wave)
+  float* po_wave;   // the row of the wave's first head
   float* pl;
 };
 
 template <int NW>
 __device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, WorkItem& wi) {
   int q, g;
-  xcd_map(blockIdx.x, p.G, q, g);
+  xcd_map(blockIdx.x, p.G, (p.B * p.S + 7) / 8, q, g);
   if (q >= p.B * p.S) return false;
   wi.b = __builtin_amdgcn_readfirstlane(q / p.S);
   wi.s = __builtin_amdgcn_readfirstlane(q - wi.b * p.S);
@@ -429,6 +431,7 @@ __device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, W
   wi.t1 = min(wi.t0 + p.tokens_per_split, len);
   wi.head = (g * NW + w) * 32 + (l & 31);
   wi.po = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + wi.head) * D_C + 4 * (l >> 5);
+  wi.po_wave = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + (g * NW + w) * 32) * D_C;
   wi.pl = p.part_lse + ((int64_t)wi.b * p.S + wi.s) * p.H + wi.head;
   return true;
 }
@@ -441,16 +444,38 @@ __device__ __forceinline__ void write_empty(const WorkItem& wi, int h) {
   if (h == 0) *wi.pl = -INFINITY;
 }
 
-__device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveState& st, int h) {
+// The wave's normalised partial output (32 heads x 512 latent dims, fp32)
+// goes out through LDS, 128 dims at a time: the accumulator layout puts the
+// 32 heads across lanes (each store instruction would touch 32 rows 2 KB
+// apart), so the values are first written to a [32 heads][128 dims] LDS
+// block (rows padded by 16 bytes: conflict-free 16-byte writes), then read
+// back row-wise, and every store instruction writes two contiguous 512-byte
+// row segments. `scr` is PART_SCR_BYTES of LDS owned by this wave.
+constexpr int PART_ROW = 4 * 128 + 16;
+constexpr int PART_SCR_BYTES = 32 * PART_ROW;   // 16896
+
+__device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveState& st, int h,
+                                              int l, char* scr) {
   const float ltot = st.lsum + __shfl_xor(st.lsum, 32, 64);
   const float inv = 1.0f / ltot;
+  const int head = l & 31;
 #pragma unroll
-  for (int dt = 0; dt < D_C / 32; ++dt)
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
-      *(f32x4*)(wi.po + 32 * dt + 8 * rq) = v * inv;
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x16& o = st.o[4 * c + d];
+        const f32x4 v = {o[4 * rq], o[4 * rq + 1], o[4 * rq + 2], o[4 * rq + 3]};
+        *(f32x4*)(scr + head * PART_ROW + 4 * (32 * d + 8 * rq + 4 * h)) = v * inv;
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + h;
+      const f32x4 v = *(const f32x4*)(scr + row * PART_ROW + 16 * head);
+      *(f32x4*)(wi.po_wave + row * D_C + 128 * c + 4 * head) = v;
     }
+  }
   if (h == 0) *wi.pl = st.m_ref + __builtin_log2f(ltot);
 }
 
@@ -549,7 +574,11 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     reset_state(st, mtrue);
     if (tid == 0) overflow = 0;
   }
-  write_partial(wi, st, h);
+  // loads of tiles past the end may still be landing in any buffer, and other
+  // waves may still read the last tile: drain both before reusing the LDS
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  write_partial(wi, st, h, l, (w < 2 ? buf0 : buf1) + (w & 1) * PART_SCR_BYTES);
 }
 
 // ---------------------------------------------------------------------------
@@ -628,7 +657,8 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     reset_state(st, mtrue);
     if (tid == 0) overflow = 0;
   }
-  write_partial(wi, st, h);
+  // finish_stage ended with a barrier: no load in flight, no wave reading
+  write_partial(wi, st, h, l, tiles[w >> 1] + (w & 1) * PART_SCR_BYTES);
 }
 
 }  // namespace mla
