@@ -20,6 +20,10 @@ Prints ONE JSON line (see the fields below). Options:
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
+  --write-traffic F W CF CW  only turn four rocprofv3 counter CSVs (decode
+                           kernel FETCH_SIZE, WRITE_SIZE; copy FETCH_SIZE,
+                           WRITE_SIZE, taken with --copy-calibration 1024)
+                           into profiles/<kernel>_<config>_traffic.json
 """
 
 from __future__ import annotations
@@ -51,6 +55,7 @@ def parse():
     ap.add_argument("--config", default="3u")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--write-traffic", nargs=4, default=None)
     return ap.parse_args()
 
 
@@ -158,8 +163,39 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def _counter_mean(csv_path: str, kernel_substr: str, counter: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic(paths, config: str, kernel: str, copy_mib: int = 1024):
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the factor between the true bytes of a
+    plain copy of copy_mib MiB and what the same counter reads for it."""
+    f, w, cf, cw = paths
+    true_kib = copy_mib * 1024.0
+    rf = true_kib / _counter_mean(cf, "copyBuffer", "FETCH_SIZE")
+    wf = true_kib / _counter_mean(cw, "copyBuffer", "WRITE_SIZE")
+    fetch = _counter_mean(f, kernel, "FETCH_SIZE") * 1024.0 * rf
+    write = _counter_mean(w, kernel, "WRITE_SIZE") * 1024.0 * wf
+    rec = {"kernel": kernel, "workload": config, "kernel_source_hash": kernel_source_hash(),
+           "read_factor": rf, "write_factor": wf, "hbm_read_bytes_per_launch": fetch,
+           "hbm_write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write}
+    out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.config, "mla_decode_bf16_kernel")
+        return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
         return
