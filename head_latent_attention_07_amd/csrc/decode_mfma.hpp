@@ -149,15 +149,27 @@ struct WaveState {
   float lsum;           // this lane's share of the softmax denominator
 };
 
+// max(x[l], x[l ^ 32]): the two half-waves hold the two token halves of the
+// same heads. v_permlane32_swap exchanges lanes 32-63 of its first operand
+// with lanes 0-31 of its second, so with both operands x the two results
+// hold, in every lane, x of that lane and x of its partner.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
+}
+
 // S^T = K Q^T for one tile; returns this lane's 16 scores (masked, scaled
 // for fp8) and the tile max of this lane's head. The A operands are read from
 // LDS three k-steps ahead of the MFMA that consumes them (a software pipeline
 // pinned with scheduling barriers), so LDS latency overlaps the MFMA chain.
-template <int CK>
+// `issue(j)` runs after k-step j's MFMA (the main loop issues the next
+// tile's loads there).
+template <int CK, typename Issue>
 __device__ __forceinline__ float tile_scores(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG],
                                              const char* qpe, const LaneAddr& la, int h,
-                                             float (&sv)[16]) {
+                                             float (&sv)[16], const Issue& issue) {
   constexpr int NJ = D_QK / 16;   // 36 k-steps
   constexpr int AHEAD = 3;
   auto a_off = [&](int j) { return (j < 32) ? la.qb[j & 7] + 256 * (j >> 3) : la.rb[j - 32]; };
@@ -173,29 +185,37 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
       qring[j + AHEAD - QREG] = *(const bf16x8*)(qpe + (j + AHEAD - QREG) * 1024);
     const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : qring[j < QREG ? 0 : j - QREG];
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j % (AHEAD + 1)], bq, sacc, 0, 0, 0);
+    issue(j);
     __builtin_amdgcn_sched_barrier(0);
   }
   // accumulator row r of this lane is token 8(r/4) + 4h + r%4 of the tile
-  float tmax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = 8 * (r >> 2) + 4 * h + (r & 3);
     float v = sacc[r];
     if (CK == CACHE_FP8) v *= scale[row];
     sv[r] = (tile_t0 + row < t1) ? v : -INFINITY;
-    tmax = fmaxf(tmax, sv[r]);
   }
-  return fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  float m4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m4[i] = fmaxf(fmaxf(sv[4 * i], sv[4 * i + 1]), fmaxf(sv[4 * i + 2], sv[4 * i + 3]));
+  return pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
 }
 
 // One 32-token tile: scores, softmax weights against m_ref, O^T += C^T P^T.
 // Returns true if some score of this wave exceeded m_ref + OVERFLOW_SLACK.
-template <int CK>
+// The weights of the first 16 tokens (B operand of the first 16 PV MFMAs)
+// are computed before the PV chain, those of the last 16 between its first
+// MFMAs, where the vector ALU work overlaps the matrix pipe. `issue(t)` runs
+// after MFMA t of the tile's 68 (36 for S, 32 for PV).
+template <int CK, typename Issue>
 __device__ __forceinline__ bool tile_compute(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG], const char* qpe,
-                                             const LaneAddr& la, int h, WaveState& st) {
+                                             const LaneAddr& la, int h, WaveState& st,
+                                             const Issue& issue) {
   float sv[16];
-  const float tmax = tile_scores<CK>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv);
+  const float tmax = tile_scores<CK>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv, issue);
   // PV operands: 32 steps (2 k-steps x 16 dim tiles), two ahead
   constexpr int NS = 32, AHEAD = 2;
   auto v_op = [&](int s) {
@@ -207,24 +227,27 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
 #pragma unroll
   for (int s = 0; s < AHEAD; ++s) ring[s] = v_op(s);
   st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
-  const bool ovf = __any(tmax > st.m_ref + OVERFLOW_SLACK);
-  bf16x8 pb[2];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float e = fast_exp2(sv[r] - st.m_ref);
+  const float mref = st.m_ref;
+  auto weight = [&](int r) {
+    float e = fast_exp2(sv[r] - mref);
     st.lsum += e;
     if (CK == CACHE_FP8) e *= scale[8 * (r >> 2) + 4 * h + (r & 3)];
-    pb[r >> 3][r & 7] = (bf16)e;
-  }
+    return (bf16)e;
+  };
+  bf16x8 pb[2];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pb[0][r] = weight(r);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s + AHEAD < NS) ring[(s + AHEAD) % (AHEAD + 1)] = v_op(s + AHEAD);
     const int dt = s & 15;
     st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % (AHEAD + 1)], pb[s >> 4], st.o[dt], 0, 0, 0);
+    if (s < 8) pb[1][s] = weight(8 + s);
+    issue(36 + s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  return ovf;
+  return __any(tmax > mref + OVERFLOW_SLACK);
 }
 
 // Map a flat workgroup id to (sequence*split index q, head group g).
@@ -238,22 +261,29 @@ __device__ __forceinline__ void xcd_map(int x, int G, int per, int& q, int& g) {
   q = (x & 7) * per + rest / G;
 }
 
-// Scalar (SMEM) load of a wave-uniform int. A plain load placed after the
-// direct-to-LDS loads becomes a vector load (the compiler cannot prove the
-// table unmodified across them), and waiting on it would also wait for every
-// DMA in flight; the scalar path is counted separately (lgkmcnt).
-__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
+// Paged caches: the block-table entries a split touches are copied to LDS
+// once (at most MAX_SPLIT_BLOCKS; the split planner keeps every split within
+// that), so finding a tile's physical row is an LDS read instead of a global
+// or scalar load in the loop. Returns the first block index of the split.
+constexpr int MAX_SPLIT_BLOCKS = 2048;
+
+template <int NT>
+__device__ __forceinline__ int load_block_table(const DecodeParams& p, int b, int t0, int t1,
+                                                int* tab, int tid) {
+  if (!p.block_table) return 0;
+  const int first = t0 / p.block_size;
+  const int nblk = min((t1 - 1) / p.block_size - first + 1, MAX_SPLIT_BLOCKS);
+  const int32_t* src = p.block_table + (int64_t)b * p.max_blocks + first;
+  for (int i = tid; i < nblk; i += NT) tab[i] = src[i];
+  return first;
 }
 
 // Physical row of the first token of a tile (tiles never cross a block:
-// block_size is a multiple of 32).
-__device__ __forceinline__ int64_t tile_base_row(const DecodeParams& p, int b, int tile_t0) {
+// block_size is a multiple of 32). `tab` is the split's block table in LDS.
+__device__ __forceinline__ int64_t tile_base_row(const DecodeParams& p, int b, int tile_t0,
+                                                 const int* tab, int first_blk) {
   if (p.block_table) {
-    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + tile_t0 / p.block_size);
-    const int blk = scalar_load_i32(p.block_table + idx);
+    const int blk = __builtin_amdgcn_readfirstlane(tab[tile_t0 / p.block_size - first_blk]);
     return (int64_t)blk * p.block_size + (tile_t0 % p.block_size);
   }
   return (int64_t)b * p.seq_capacity + tile_t0;
@@ -284,36 +314,97 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const DecodeParams& p, int64_t bas
   return t;
 }
 
+// One wave-wide direct-to-LDS load: 16 bytes per lane from
+// rsrc + soffset + voffset (bounds-checked against the resource: zeros past
+// its end) to LDS at lds_addr + 16 * lane (lds_addr wave-uniform, in M0).
+// Written as inline assembly so that the compiler's wait-count tracking does
+// not see it: it cannot tell which LDS buffer each pending load targets once
+// control flow merges, and would then wait for every load in flight before
+// each LDS read. The kernels wait for these loads themselves (vmcnt) before
+// the barrier that publishes a tile, and fence the compiler there.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// M0 is reserved by the compiler, so the block saves and restores it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voffset,
+                                      int soffset) {
+  int saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+
+// Compiler-only fence: no memory access moves across it (emits nothing).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 // bf16 cache: direct global->LDS loads (16 bytes per lane), 36 wave-wide
-// loads per tile (32 latent rows of 1 KB, 4 groups of 8 RoPE-key rows).
-// Lane i writes LDS slot i of its 1 KB, so it fetches the chunk that the
-// swizzle places there. Rows past the split's last token re-read the last
-// token (their scores are masked).
+// loads per tile (32 latent rows of 1 KB, 4 groups of 8 RoPE-key rows), of
+// which each of the NW waves issues PIECES: piece i < RPW is latent row
+// w*RPW + i, the others are RoPE-key groups. Lane i writes LDS slot i of its
+// 1 KB, so it fetches the chunk that the swizzle places there. Rows past the
+// split's last token re-read the last token (their scores are masked).
 // With valid == false the loads are still issued (so every wave's count of
 // loads in flight stays the same on every path) but read nothing from memory.
+//
+// A wave that issues several direct-to-LDS loads back to back stalls at issue
+// until the CU's memory pipeline accepts them (about a thousand cycles for a
+// tile's worth), and issues nothing else meanwhile. The main loop therefore
+// spreads the next tile's pieces through the MFMA chains of the current one
+// (step(t) after MFMA t), where a stall only delays MFMAs already queued.
 template <int NW>
-__device__ __forceinline__ void tile_dma(const DecodeParams& p, char* tile, int64_t base_row,
-                                         int last_row, int w, int l, bool valid) {
-  constexpr int RPW = TILE / NW;   // latent rows per wave
-  constexpr int GPW = 4 / NW;      // RoPE-key row groups per wave
-  const TileRsrc rs = tile_rsrc(p, base_row, 2, valid);
-  const int lsb = (int)(p.latent_stride * 2), rsb = (int)(p.rope_stride * 2);
-#pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int u = w * RPW + k;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs.lat, (__attribute__((address_space(3))) void*)(tile + u * LAT_ROW), 16,
-        16 * (l ^ lat_swz(u)), min(u, last_row) * lsb, 0, 0);
+struct TileLoad {
+  static constexpr int RPW = TILE / NW;          // latent rows per wave
+  static constexpr int GPW = 4 / NW;             // RoPE-key row groups per wave
+  static constexpr int PIECES = RPW + GPW;       // 9, 18, 36
+  TileRsrc rs;
+  char* tile;
+  int lsb, rsb, last_row, w, l;
+
+  __device__ __forceinline__ void piece(int i) const {
+    if (i < RPW) {
+      const int u = __builtin_amdgcn_readfirstlane(w * RPW + i);
+      dma16(rs.lat, lds_u32(tile + u * LAT_ROW), 16 * (l ^ lat_swz(u)),
+            __builtin_amdgcn_readfirstlane(min(u, last_row) * lsb));
+    } else {
+      const int v = w * GPW + (i - RPW);
+      const int row = 8 * v + (l >> 3);
+      dma16(rs.rope, lds_u32(tile + ROPE_OFF + v * 8 * ROPE_ROW),
+            min(row, last_row) * rsb + 16 * ((l & 7) ^ rope_swz(row)), 0);
+    }
   }
-  const int lrow = l >> 3;
+  __device__ __forceinline__ void all() const {
 #pragma unroll
-  for (int k = 0; k < GPW; ++k) {
-    const int v = w * GPW + k;
-    const int row = 8 * v + lrow;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs.rope, (__attribute__((address_space(3))) void*)(tile + ROPE_OFF + v * 8 * ROPE_ROW), 16,
-        min(row, last_row) * rsb + 16 * ((l & 7) ^ rope_swz(row)), 0, 0, 0);
+    for (int i = 0; i < PIECES; ++i) piece(i);
   }
+  // after MFMA t (0..67) of the tile being computed: piece i goes out at
+  // t = 2 + 64 i / PIECES, spread over both MFMA chains
+  __device__ __forceinline__ void step(int t) const {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i)
+      if (t == 2 + (64 * i) / PIECES) piece(i);
+  }
+};
+
+template <int NW>
+__device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* tile,
+                                                  int64_t base_row, int last_row, int w, int l,
+                                                  bool valid) {
+  TileLoad<NW> t;
+  t.rs = tile_rsrc(p, base_row, 2, valid);
+  t.tile = tile;
+  t.lsb = (int)(p.latent_stride * 2);
+  t.rsb = (int)(p.rope_stride * 2);
+  t.last_row = last_row;
+  t.w = w;
+  t.l = l;
+  return t;
 }
 
 // fp8 cache: the raw codes of a tile (32 rows x 576 bytes) and its 32 bf16
@@ -507,8 +598,9 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char buf1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
+  __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
   __shared__ int overflow;
-  constexpr int DMA_PER_TILE = 36 / NW;  // wave-wide loads per tile per wave
+  constexpr int DMA_PER_TILE = TileLoad<NW>::PIECES;  // wave-wide loads per tile per wave
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -518,6 +610,25 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     write_empty(wi, h);
     return;
   }
+  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  const int first_blk = load_block_table<64 * NW>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  // loads of tile k into `tile`; tiles past the split are issued as empty loads
+  auto load = [&](char* tile, int k) {
+    const bool valid = k < ntiles;
+    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
+    return tile_load<NW>(p, tile, tile_base_row(p, wi.b, tt0, blk_tab, first_blk),
+                         wi.t1 - 1 - tt0, w, l, valid);
+  };
+  auto dma = [&](char* tile, int k) { load(tile, k).all(); };
+  const auto no_issue = [](int) {};
+
+  // tiles 0 and 1 first, then the queries, then one wait for all of it: the
+  // compiler does not count the tile loads, so a wait it placed for the
+  // query loads inside the loop would drain every tile load in flight
+  dma(buf0, 0);
+  dma(buf1, 1);
   bf16x8 qreg[QREG];
   char* qpe = qpe_all + w * 4096;
   load_q(p, wi, h, l, qreg, qpe);
@@ -525,35 +636,43 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   WaveState st;
   reset_state(st, -INFINITY);
   if (tid == 0) overflow = 0;
-
-  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
-  // tile k into `tile`; tiles past the split are issued as empty loads
-  auto dma = [&](char* tile, int k) {
-    const bool valid = k < ntiles;
-    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    tile_dma<NW>(p, tile, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
-  };
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 
   for (int attempt = 0; attempt < 2; ++attempt) {
-    dma(buf0, 0);
-    dma(buf1, 1);
-    wait_vm_lgkm0<DMA_PER_TILE>();   // tile 0 landed (tile 1 may be in flight)
-    __builtin_amdgcn_s_barrier();
+    if (attempt > 0) {
+      dma(buf0, 0);
+      dma(buf1, 1);
+      wait_vm_lgkm0<DMA_PER_TILE>();   // tile 0 landed (tile 1 may be in flight)
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+    }
 
-    // phase on buffer X (tile k): refill buffer Z with tile k+2, compute X,
-    // wait for tile k+1, barrier. Phases are predicated rather than exited
-    // early so the accumulators keep one register assignment.
-    auto phase = [&](char* __restrict__ X, char* __restrict__ Z, int k) {
-      dma(Z, k + 2);
-      if (tile_compute<CACHE_BF16>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la, h, st) && l == 0)
-        overflow = 1;
+    // phase on buffer X (tile k): compute X while refilling buffer Z with
+    // tile k+2 (its loads spread through the MFMA chain), wait for tile
+    // k+1, barrier. Phases past the last tile only issue their (empty) loads,
+    // so every phase issues the same number and the vmcnt waits stay exact;
+    // they are predicated rather than exited early so the accumulators keep
+    // one register assignment.
+    auto phase = [&](char* X, char* Z, int k) {
+      const TileLoad<NW> next = load(Z, k + 2);
+      if (k < ntiles) {
+        if (tile_compute<CACHE_BF16>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la,
+                                     h, st, [&](int j) { next.step(j); }) &&
+            l == 0)
+          overflow = 1;
+      } else {
+        next.all();
+      }
       wait_vm_lgkm0<DMA_PER_TILE>();  // tile k+1 landed, tile k+2 may be in flight
       __builtin_amdgcn_s_barrier();
+      compiler_fence();               // no LDS read of tile k+1 moves above this
     };
     for (int k = 0; k < ntiles; k += 3) {
       phase(buf0, buf2, k);
-      if (k + 1 < ntiles) phase(buf1, buf0, k + 1);
-      if (k + 2 < ntiles) phase(buf2, buf1, k + 2);
+      phase(buf1, buf0, k + 1);
+      phase(buf2, buf1, k + 2);
     }
     if (overflow == 0) break;
 
@@ -562,14 +681,18 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     // split (scores only), then recompute the split against it.
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
+    compiler_fence();
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
       dma(buf0, k);
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
+      compiler_fence();
       float sv[16];
-      mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16>(buf0, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la, h, sv));
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16>(buf0, nullptr, wi.t0 + k * TILE, wi.t1, qreg,
+                                                   qpe + 16 * l, la, h, sv, no_issue));
       __builtin_amdgcn_s_barrier();
+      compiler_fence();
     }
     reset_state(st, mtrue);
     if (tid == 0) overflow = 0;
@@ -578,6 +701,7 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   // waves may still read the last tile: drain both before reusing the LDS
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
+  compiler_fence();
   write_partial(wi, st, h, l, (w < 2 ? buf0 : buf1) + (w & 1) * PART_SCR_BYTES);
 }
 
@@ -593,6 +717,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char stage[STG_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   __shared__ float scl[2][TILE];
+  __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
   __shared__ int overflow;
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
@@ -612,11 +737,15 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   if (tid == 0) overflow = 0;
 
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  const int first_blk = load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
   float sc_next = 1.0f;
   auto dma = [&](int k) {
     const bool valid = k < ntiles;
     const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    sc_next = fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0), wi.t1 - 1 - tt0, w, l, valid);
+    sc_next = fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0, blk_tab, first_blk),
+                               wi.t1 - 1 - tt0, w, l, valid);
   };
   // the staged tile is complete once the loads landed and the scales are in LDS
   auto finish_stage = [&]() {
@@ -636,7 +765,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       __builtin_amdgcn_s_barrier();
       dma(k + 1);
       if (tile_compute<CACHE_FP8>(tiles[k & 1], scl[k & 1], wi.t0 + k * TILE, wi.t1, qreg,
-                                  qpe + 16 * l, la, h, st) && l == 0)
+                                  qpe + 16 * l, la, h, st, [](int) {}) && l == 0)
         overflow = 1;
       finish_stage();
     }
@@ -651,7 +780,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       __builtin_amdgcn_s_barrier();
       float sv[16];
       mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8>(tiles[0], scl[0], wi.t0 + k * TILE, wi.t1,
-                                                   qreg, qpe + 16 * l, la, h, sv));
+                                                   qreg, qpe + 16 * l, la, h, sv, [](int) {}));
       __builtin_amdgcn_s_barrier();
     }
     reset_state(st, mtrue);

@@ -84,6 +84,10 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   int forced = (opts && opts->num_splits > 0) ? opts->num_splits : env_int("MLA_SPLITS");
   if (forced > 0) S = forced;
   S = std::max(1, std::min(S, ceil_div(len, TILE)));
+  // a split of a paged cache touches at most MAX_SPLIT_BLOCKS blocks (its
+  // table is staged in LDS): with the smallest block size (32) and tokens
+  // per split rounded up to 32, TS <= 2046*32 + 31 keeps ceil(TS/32)+1 <= 2048
+  if (act != MLA_F32) S = std::max(S, ceil_div(len, (MAX_SPLIT_BLOCKS - 2) * TILE));
   int ts = ceil_div(len, S);
   ts = ceil_div(ts, TILE) * TILE;
   if (act == MLA_F32) ts = std::min(ts, F32_MAX_SPLIT);
