@@ -57,7 +57,8 @@ struct DecodeParams {
   const int32_t* lengths;      // [B]
   int max_len;
   int B, H, S, tokens_per_split, G;
-  float* part_o;               // [B, S, H, 512] normalised partial outputs
+  _Float16* part_o;            // [B, S, H, 512] normalised partial outputs / part_scale
+  float* part_scale;           // [B, S, H] max |normalised output| of each partial row
   float* part_lse;             // [B, S, H] log2 sum-exp of each split
 };
 
@@ -505,9 +506,10 @@ __device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, fl
 // absorbed queries of this lane's head.
 struct WorkItem {
   int b, s, t0, t1, head;
-  float* po;        // this lane's head row (+4 floats for the upper half-wave)
-  float* po_wave;   // the row of the wave's first head
+  _Float16* po;       // this lane's head row (+4 values for the upper half-wave)
+  _Float16* po_wave;  // the row of the wave's first head
   float* pl;
+  float* ps;
 };
 
 template <int NW>
@@ -524,6 +526,7 @@ __device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, W
   wi.po = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + wi.head) * D_C + 4 * (l >> 5);
   wi.po_wave = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + (g * NW + w) * 32) * D_C;
   wi.pl = p.part_lse + ((int64_t)wi.b * p.S + wi.s) * p.H + wi.head;
+  wi.ps = p.part_scale + ((int64_t)wi.b * p.S + wi.s) * p.H + wi.head;
   return true;
 }
 
@@ -531,24 +534,38 @@ __device__ __forceinline__ void write_empty(const WorkItem& wi, int h) {
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) *(f32x4*)(wi.po + 32 * dt + 8 * rq) = f32x4{0, 0, 0, 0};
-  if (h == 0) *wi.pl = -INFINITY;
+    for (int rq = 0; rq < 4; ++rq) *(f16x4*)(wi.po + 32 * dt + 8 * rq) = f16x4{0, 0, 0, 0};
+  if (h == 0) {
+    *wi.pl = -INFINITY;
+    *wi.ps = 0.f;
+  }
 }
 
-// The wave's normalised partial output (32 heads x 512 latent dims, fp32)
-// goes out through LDS, 128 dims at a time: the accumulator layout puts the
-// 32 heads across lanes (each store instruction would touch 32 rows 2 KB
-// apart), so the values are first written to a [32 heads][128 dims] LDS
-// block (rows padded by 16 bytes: conflict-free 16-byte writes), then read
-// back row-wise, and every store instruction writes two contiguous 512-byte
-// row segments. `scr` is PART_SCR_BYTES of LDS owned by this wave.
-constexpr int PART_ROW = 4 * 128 + 16;
-constexpr int PART_SCR_BYTES = 32 * PART_ROW;   // 16896
+// The wave's normalised partial output (32 heads x 512 latent dims) is
+// stored as fp16 relative to its row maximum (values in [-1, 1], the fp32
+// factor in part_scale): half the bytes of fp32, and a rounding error
+// (2^-11 of the row maximum) far below that of the bf16 operand the merge
+// later feeds to the W_UV product. It goes out through LDS, 128 dims at a
+// time: the accumulator layout puts the 32 heads across lanes (each store
+// instruction would touch 32 rows 1 KB apart), so the values are first
+// written to a [32 heads][128 dims] LDS block (rows padded by 16 bytes), then
+// read back row-wise, and every store instruction writes four contiguous
+// 256-byte row segments. `scr` is PART_SCR_BYTES of LDS owned by this wave.
+constexpr int PART_ROW = 2 * 128 + 16;
+constexpr int PART_SCR_BYTES = 32 * PART_ROW;   // 8704
 
 __device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveState& st, int h,
                                               int l, char* scr) {
-  const float ltot = st.lsum + __shfl_xor(st.lsum, 32, 64);
-  const float inv = 1.0f / ltot;
+  const unsigned ul = __builtin_bit_cast(unsigned, st.lsum);
+  const auto sw = __builtin_amdgcn_permlane32_swap(ul, ul, false, false);
+  const float ltot = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
+  float mx = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D_C / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(st.o[dt][r]));
+  mx = pair_max(mx);
+  const float f = (mx > 0.f) ? 1.0f / mx : 0.f;
   const int head = l & 31;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -557,17 +574,21 @@ __device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveStat
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const f32x16& o = st.o[4 * c + d];
-        const f32x4 v = {o[4 * rq], o[4 * rq + 1], o[4 * rq + 2], o[4 * rq + 3]};
-        *(f32x4*)(scr + head * PART_ROW + 4 * (32 * d + 8 * rq + 4 * h)) = v * inv;
+        const f16x4 v = {(_Float16)(o[4 * rq] * f), (_Float16)(o[4 * rq + 1] * f),
+                         (_Float16)(o[4 * rq + 2] * f), (_Float16)(o[4 * rq + 3] * f)};
+        *(f16x4*)(scr + head * PART_ROW + 2 * (32 * d + 8 * rq + 4 * h)) = v;
       }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 2 * i + h;
-      const f32x4 v = *(const f32x4*)(scr + row * PART_ROW + 16 * head);
-      *(f32x4*)(wi.po_wave + row * D_C + 128 * c + 4 * head) = v;
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (l >> 4);
+      const u32x4 v = *(const u32x4*)(scr + row * PART_ROW + 16 * (l & 15));
+      *(u32x4*)(wi.po_wave + row * D_C + 128 * c + 8 * (l & 15)) = v;
     }
   }
-  if (h == 0) *wi.pl = st.m_ref + __builtin_log2f(ltot);
+  if (h == 0) {
+    *wi.pl = st.m_ref + __builtin_log2f(ltot);
+    *wi.ps = mx / ltot;
+  }
 }
 
 // qpe: this wave's 4 KB of LDS, [k-step][lane][16 bytes]

@@ -96,17 +96,23 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   return pl;
 }
 
+// Workspace: absorbed queries [B, H, 576] (activation dtype), split partials
+// [B, S, H, 512] (fp32 on the fp32 path; fp16 relative to a per-row fp32
+// scale [B, S, H] otherwise), split lse [B, S, H] fp32.
 struct WsLayout {
-  size_t q_off, po_off, pl_off, total;
+  size_t q_off, po_off, ps_off, pl_off, total;
 };
 
 WsLayout ws_layout(int B, int H, const Plan& pl, mla_dtype act) {
   WsLayout w;
   const size_t qe = (act == MLA_F32) ? 4 : 2;
+  const size_t pe = (act == MLA_F32) ? 4 : 2;
+  const size_t rows = (size_t)B * pl.S * H;
   w.q_off = 0;
   w.po_off = align_up((size_t)B * H * D_QK * qe, 256);
-  w.pl_off = align_up(w.po_off + (size_t)B * pl.S * H * D_C * 4, 256);
-  w.total = align_up(w.pl_off + (size_t)B * pl.S * H * 4, 256);
+  w.ps_off = align_up(w.po_off + rows * D_C * pe, 256);
+  w.pl_off = align_up(w.ps_off + (act == MLA_F32 ? 0 : rows * 4), 256);
+  w.total = align_up(w.pl_off + rows * 4, 256);
   return w;
 }
 
@@ -167,7 +173,9 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
     return MLA_ERR_WORKSPACE;
   char* ws = (char*)workspace;
-  float* part_o = (float*)(ws + wl.po_off);
+  float* part_o = (float*)(ws + wl.po_off);           // fp32 path
+  _Float16* part_h = (_Float16*)(ws + wl.po_off);     // bf16 path
+  float* part_scale = (float*)(ws + wl.ps_off);
   float* part_lse = (float*)(ws + wl.pl_off);
   const float c = softmax_scale * LOG2E;
   (void)hipGetLastError();  // start from a clean launch-error state
@@ -208,7 +216,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   bf16* q = (bf16*)(ws + wl.q_off);
   const int nbc = ceil_div(B, 32);
   AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c};
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(H), dim3(256), 0, stream, ap);
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(H * 4), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());
 
   DecodeParams dp;
@@ -230,7 +238,8 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   dp.S = pl.S;
   dp.tokens_per_split = pl.TS;
   dp.G = pl.G;
-  dp.part_o = part_o;
+  dp.part_o = part_h;
+  dp.part_scale = part_scale;
   dp.part_lse = part_lse;
   const int nq = B * pl.S;
   const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
@@ -248,7 +257,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   MLA_TRY(launch_status());
   if (opts && opts->attn_end) (void)hipEventRecord(opts->attn_end, stream);
 
-  CombineParams cp{part_o, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
+  CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
   hipLaunchKernelGGL(mla_combine_kernel, dim3(ceil_div(H, 8) * 8 * nbc), dim3(256), 0, stream, cp);
   return launch_status();
 }

@@ -40,9 +40,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t proj_rsrc(const void* base, in
 __device__ __forceinline__ int wrow_swizzle(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
 // ----------------------------------------------------------------------------
-// absorb: one workgroup (4 waves) per head; W_UK[h] (128 rows x 1 KB) is
-// brought into LDS whole by direct-to-LDS loads, then every chunk of 32
-// sequences is multiplied against it.
+// absorb: four workgroups (4 waves each) per head, each owning 128 of the 512
+// output columns; its slice of W_UK[h] (128 rows x 256 B = 32 KB) is brought
+// into LDS by direct-to-LDS loads, then every chunk of 32 sequences is
+// multiplied against it (wave w: columns 32w..32w+31 of the slice).
 // ----------------------------------------------------------------------------
 struct AbsorbParams {
   const bf16* q_nope;  // [B, H, 128]
@@ -54,30 +55,35 @@ struct AbsorbParams {
 };
 
 constexpr int AB_APITCH = D_N * 2 + 16;    // 272 B: 8 rows' 16-byte chunks hit distinct banks
+constexpr int AB_COLS = 128;               // output columns per workgroup
+constexpr int AB_ROW = AB_COLS * 2;        // 256 B per W row slice in LDS
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
-  __shared__ __attribute__((aligned(1024))) char w_lds[D_N * D_C * 2];   // 128 KB
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_N * AB_ROW];   // 32 KB
   __shared__ __attribute__((aligned(16))) char a_lds[32 * AB_APITCH];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
-  const int head = blockIdx.x;
+  const int head = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   if (head >= p.H) return;
 
-  // W_UK[h]: 128 rows of 1 KB, one wave-wide 16-byte-per-lane load per row
+  // W_UK[h][:, 128 q .. 128 q + 127]: wave w loads rows 32w..32w+31, four
+  // rows (4 x 256 B) per wave-wide load; lane l fills LDS slot l & 15 of row
+  // 4k + (l >> 4), which holds the chunk the swizzle places there
   {
     const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uk + (int64_t)head * D_N * D_C, D_N * D_C * 2);
 #pragma unroll
-    for (int k = 0; k < D_N / 4; ++k) {
-      const int row = w * (D_N / 4) + k;
+    for (int k = 0; k < 8; ++k) {
+      const int row0 = w * 32 + 4 * k, row = row0 + (l >> 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(w_lds + row * 1024), 16,
-          16 * (l ^ wrow_swizzle(row)), row * 1024, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(w_lds + row0 * AB_ROW), 16,
+          row * (D_C * 2) + quarter * AB_ROW + 16 * ((l & 15) ^ wrow_swizzle(row)), 0, 0, 0);
     }
   }
   // tr-read bases for this lane's B operand
   const int r1 = 8 * h + (jj >> 2);                    // + 16 ks, and + 4 for the upper half
-  const int cx = (2 * (g16 & 1) + ((jj & 3) >> 1));    // chunk low bits before the swizzle
+  const int chunk = 4 * w + (2 * (g16 & 1) + ((jj & 3) >> 1));
+  const int off = 8 * (jj & 1);
   for (int b0 = 0; b0 < p.B; b0 += 32) {
     // q_nope rows of the chunk -> LDS (zero rows past B); q_pe scaled copy
     for (int i = tid; i < 32 * (D_N / 8); i += 256) {
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
       if (b0 + r < p.B) v = *(const u32x4*)(p.q_nope + ((int64_t)(b0 + r) * p.H + head) * D_N + 8 * c);
       *(u32x4*)(a_lds + r * AB_APITCH + 16 * c) = v;
     }
-    {
+    if (quarter == 0) {
       // q_pe: 8 consecutive values per thread (32 rows x 64)
       const int r = tid >> 3, c = 8 * (tid & 7);
       if (b0 + r < p.B) {
@@ -98,33 +104,23 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
         *(bf16x8*)(p.q + bh * D_QK + D_C + c) = o;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK landed (first chunk)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK slice landed (first chunk)
     __syncthreads();
-    f32x16 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D_N / 16; ++ks) {
       const bf16x8 a = *(const bf16x8*)(a_lds + l32 * AB_APITCH + 2 * (16 * ks + 8 * h));
       const int ra = 16 * ks + r1, rb = ra + 4;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int chunk = 4 * (4 * w + nt) + cx;
-        const int off = 8 * (jj & 1);
-        const bf16x8 bop = tr_read_8(w_lds + ra * 1024 + 16 * (chunk ^ wrow_swizzle(ra)) + off,
-                                     w_lds + rb * 1024 + 16 * (chunk ^ wrow_swizzle(rb)) + off);
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[nt], 0, 0, 0);
-      }
+      const bf16x8 bop = tr_read_8(w_lds + ra * AB_ROW + 16 * (chunk ^ wrow_swizzle(ra)) + off,
+                                   w_lds + rb * AB_ROW + 16 * (chunk ^ wrow_swizzle(rb)) + off);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
     }
     // lane holds column n, rows b = 8(r/4) + 4h + r%4
+    const int n = quarter * AB_COLS + 32 * w + l32;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = 32 * (4 * w + nt) + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (bb < p.B) p.q[((int64_t)bb * p.H + head) * D_QK + n] = (bf16)(acc[nt][r] * p.c);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (bb < p.B) p.q[((int64_t)bb * p.H + head) * D_QK + n] = (bf16)(acc[r] * p.c);
     }
     __syncthreads();   // a_lds is rewritten by the next chunk
   }
@@ -136,8 +132,9 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
 // first chunk of 32 sequences are merged.
 // ----------------------------------------------------------------------------
 struct CombineParams {
-  const float* part_o;    // [B, S, H, 512]
-  const float* part_lse;  // [B, S, H] log2 domain
+  const _Float16* part_o;   // [B, S, H, 512] fp16, relative to part_scale
+  const float* part_scale;  // [B, S, H]
+  const float* part_lse;    // [B, S, H] log2 domain
   const bf16* w_uv;       // [H, 512, 128]
   bf16* out;              // [B, H, 128]
   float* lse;             // [B, H] natural log, or nullptr
@@ -194,27 +191,31 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
     __syncthreads();
     f32x16 acc = f32x16{};
     for (int half = 0; half < 2; ++half) {
-      // thread: dims half*256 + 4*(tid%64) .. +3 of sequences b0 + tid/64 + 4i
-      const int d4 = tid & 63;
-#pragma unroll 2
-      for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 6) + 4 * i;
+      // thread: dims half*256 + 8*(tid%32) .. +7 of sequences b0 + tid/32 + 8i
+      const int d8 = tid & 31;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 5) + 8 * i;
         const int b = b0 + r;
-        f32x4 m = {0.f, 0.f, 0.f, 0.f};
+        f32x8 m = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (b < p.B && winv[r] > 0.f) {
           const float L = lmax[r];
-          const float* ls = p.part_lse + (int64_t)b * p.S * p.H + head;
-          const float* po = p.part_o + ((int64_t)b * p.S * p.H + head) * D_C + half * 256 + 4 * d4;
+          const int64_t row0 = (int64_t)b * p.S * p.H + head;
+          const _Float16* po = p.part_o + row0 * D_C + half * 256 + 8 * d8;
 #pragma unroll 4
           for (int s = 0; s < p.S; ++s) {
-            const float wgt = fast_exp2(ls[(int64_t)s * p.H] - L);
-            const f32x4 v = *(const f32x4*)(po + (int64_t)s * p.H * D_C);
-            m += wgt * v;
+            const int64_t rs_ = row0 + (int64_t)s * p.H;
+            const float wgt = fast_exp2(p.part_lse[rs_] - L) * p.part_scale[rs_];
+            const f16x8 v = *(const f16x8*)(po + (int64_t)s * p.H * D_C);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m[k] += wgt * (float)v[k];
           }
           m *= winv[r];
         }
-        bf16x4 pk = {(bf16)m[0], (bf16)m[1], (bf16)m[2], (bf16)m[3]};
-        *(bf16x4*)(a_lds + r * CB_APITCH + 8 * d4) = pk;
+        bf16x8 pk;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pk[k] = (bf16)m[k];
+        *(bf16x8*)(a_lds + r * CB_APITCH + 16 * d8) = pk;
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UV landed (first pass)
       __syncthreads();
