@@ -61,4 +61,14 @@ __device__ __forceinline__ int64_t cache_row(int b, int t, int64_t seq_capacity,
   return (r >= 0 && r < rows) ? r : 0;
 }
 
+// Absorbed-query layout in the workspace (written by the absorb kernel,
+// read by the attention kernels): per (sequence, group of 32 heads), the 36
+// k-steps of the QK^T B operand in lane order, so that a wave loads k-step j
+// as one contiguous 1 KB. Lane l holds head 32 g + (l % 32), dims
+// 16 j + 8 (l / 32) .. +7. Element n (0..575) of head hd of sequence b:
+__device__ __forceinline__ int64_t qop_index(int b, int hd, int n, int H) {
+  const int lane = (hd & 31) + 32 * ((n >> 3) & 1);
+  return ((((int64_t)b * (H >> 5) + (hd >> 5)) * (D_QK / 16) + (n >> 4)) * 64 + lane) * 8 + (n & 7);
+}
+
 }  // namespace mla

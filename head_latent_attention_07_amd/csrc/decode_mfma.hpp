@@ -279,6 +279,29 @@ __device__ __forceinline__ int load_block_table(const DecodeParams& p, int b, in
   return first;
 }
 
+__device__ __forceinline__ int first_blk_of(const DecodeParams& p, int t0) {
+  return p.block_table ? t0 / p.block_size : 0;
+}
+
+// Scalar (SMEM) load of a wave-uniform int, waited for inside the asm block
+// (counted on lgkmcnt, so it does not wait for tile loads in flight).
+__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// Physical row of the first token of a tile, reading the block entry from
+// global memory (before the split's table is in LDS).
+__device__ __forceinline__ int64_t tile_base_row_direct(const DecodeParams& p, int b, int tile_t0) {
+  if (p.block_table) {
+    const int idx = __builtin_amdgcn_readfirstlane(b * p.max_blocks + tile_t0 / p.block_size);
+    const int blk = scalar_load_i32(p.block_table + idx);
+    return (int64_t)blk * p.block_size + (tile_t0 % p.block_size);
+  }
+  return (int64_t)b * p.seq_capacity + tile_t0;
+}
+
 // Physical row of the first token of a tile (tiles never cross a block:
 // block_size is a multiple of 32). `tab` is the split's block table in LDS.
 __device__ __forceinline__ int64_t tile_base_row(const DecodeParams& p, int b, int tile_t0,
@@ -591,15 +614,21 @@ __device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveStat
   }
 }
 
-// qpe: this wave's 4 KB of LDS, [k-step][lane][16 bytes]
-__device__ __forceinline__ void load_q(const DecodeParams& p, const WorkItem& wi, int h, int l,
-                                       bf16x8 (&qreg)[QREG], char* qpe) {
-  const bf16* qp = p.q + ((int64_t)wi.b * p.H + wi.head) * D_QK + 8 * h;
+// Queries of this wave's 32 heads (operand layout, see qop_index): the 32
+// latent k-steps into registers, the 4 RoPE k-steps into `qtmp` (written to
+// this wave's 4 KB of LDS, [k-step][lane][16 bytes], once they landed).
+__device__ __forceinline__ void load_q(const DecodeParams& p, const WorkItem& wi, int l,
+                                       bf16x8 (&qreg)[QREG], bf16x8 (&qtmp)[QLDS]) {
+  const bf16* qp = p.q + qop_index(wi.b, wi.head - (l & 31), 0, p.H) + 8 * l;
 #pragma unroll
-  for (int j = 0; j < QREG; ++j) qreg[j] = *(const bf16x8*)(qp + 16 * j);
+  for (int j = 0; j < QREG; ++j) qreg[j] = *(const bf16x8*)(qp + 512 * j);
 #pragma unroll
-  for (int j = QREG; j < D_QK / 16; ++j)
-    *(bf16x8*)(qpe + (j - QREG) * 1024 + 16 * l) = *(const bf16x8*)(qp + 16 * j);
+  for (int j = 0; j < QLDS; ++j) qtmp[j] = *(const bf16x8*)(qp + 512 * (QREG + j));
+}
+
+__device__ __forceinline__ void store_qpe(const bf16x8 (&qtmp)[QLDS], char* qpe, int l) {
+#pragma unroll
+  for (int j = 0; j < QLDS; ++j) *(bf16x8*)(qpe + j * 1024 + 16 * l) = qtmp[j];
 }
 
 __device__ __forceinline__ void reset_state(WaveState& st, float m_ref) {
@@ -632,27 +661,30 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     return;
   }
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
-  const int first_blk = load_block_table<64 * NW>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
   // loads of tile k into `tile`; tiles past the split are issued as empty loads
-  auto load = [&](char* tile, int k) {
-    const bool valid = k < ntiles;
+  auto load_at = [&](char* tile, int k, int64_t base_row) {
     const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    return tile_load<NW>(p, tile, tile_base_row(p, wi.b, tt0, blk_tab, first_blk),
-                         wi.t1 - 1 - tt0, w, l, valid);
+    return tile_load<NW>(p, tile, base_row, wi.t1 - 1 - tt0, w, l, k < ntiles);
+  };
+  auto load = [&](char* tile, int k) {
+    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
+    return load_at(tile, k, tile_base_row(p, wi.b, tt0, blk_tab, first_blk_of(p, wi.t0)));
   };
   auto dma = [&](char* tile, int k) { load(tile, k).all(); };
   const auto no_issue = [](int) {};
 
-  // tiles 0 and 1 first, then the queries, then one wait for all of it: the
-  // compiler does not count the tile loads, so a wait it placed for the
-  // query loads inside the loop would drain every tile load in flight
-  dma(buf0, 0);
-  dma(buf1, 1);
-  bf16x8 qreg[QREG];
+  // Prologue, in order of latency: tiles 0 and 1 (their block entries read
+  // on the scalar path), the queries, the rest of the split's block table;
+  // then one wait for all of it. The compiler does not count the tile loads,
+  // so a wait it placed for the query loads inside the loop would drain
+  // every tile load in flight.
+  load_at(buf0, 0, tile_base_row_direct(p, wi.b, wi.t0)).all();
+  load_at(buf1, 1, tile_base_row_direct(p, wi.b, wi.t0 + min(1, ntiles - 1) * TILE)).all();
+  bf16x8 qreg[QREG], qtmp[QLDS];
+  load_q(p, wi, l, qreg, qtmp);
+  load_block_table<64 * NW>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
   char* qpe = qpe_all + w * 4096;
-  load_q(p, wi, h, l, qreg, qpe);
+  store_qpe(qtmp, qpe, l);
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
@@ -749,9 +781,10 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     write_empty(wi, h);
     return;
   }
-  bf16x8 qreg[QREG];
+  bf16x8 qreg[QREG], qtmp[QLDS];
   char* qpe = qpe_all + w * 4096;
-  load_q(p, wi, h, l, qreg, qpe);
+  load_q(p, wi, l, qreg, qtmp);
+  store_qpe(qtmp, qpe, l);
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);

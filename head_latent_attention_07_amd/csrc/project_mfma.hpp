@@ -49,7 +49,7 @@ struct AbsorbParams {
   const bf16* q_nope;  // [B, H, 128]
   const bf16* q_pe;    // [B, H, 64]
   const bf16* w_uk;    // [H, 128, 512]
-  bf16* q;             // [B, H, 576]
+  bf16* q;             // [B, H, 576] in the operand layout of qop_index
   int B, H, nbc;       // nbc: unused (kept for the launch code)
   float c;             // softmax_scale * log2(e)
 };
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
         bf16x8 o;
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = (bf16)((float)v[k] * p.c);
-        *(bf16x8*)(p.q + bh * D_QK + D_C + c) = o;
+        *(bf16x8*)(p.q + qop_index(b0 + r, head, D_C + c, p.H)) = o;
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK slice landed (first chunk)
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (bb < p.B) p.q[((int64_t)bb * p.H + head) * D_QK + n] = (bf16)(acc[r] * p.c);
+      if (bb < p.B) p.q[qop_index(bb, head, n, p.H)] = (bf16)(acc[r] * p.c);
     }
     __syncthreads();   // a_lds is rewritten by the next chunk
   }
