@@ -216,7 +216,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   bf16* q = (bf16*)(ws + wl.q_off);
   const int nbc = ceil_div(B, 32);
   AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c};
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(H * 4), dim3(256), 0, stream, ap);
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(ceil_div(H, 32) * 128), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());
 
   DecodeParams dp;

@@ -57,14 +57,26 @@ struct AbsorbParams {
 constexpr int AB_APITCH = D_N * 2 + 16;    // 272 B: 8 rows' 16-byte chunks hit distinct banks
 constexpr int AB_COLS = 128;               // output columns per workgroup
 constexpr int AB_ROW = AB_COLS * 2;        // 256 B per W row slice in LDS
+constexpr int AB_OPITCH = 32 * 2 + 16;     // 80 B: output staging row (32 bf16 + pad)
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
   __shared__ __attribute__((aligned(1024))) char w_lds[D_N * AB_ROW];   // 32 KB
   __shared__ __attribute__((aligned(16))) char a_lds[32 * AB_APITCH];
+  __shared__ __attribute__((aligned(16))) char o_lds[4][32 * AB_OPITCH];  // per wave: 32 seq x 32 cols
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
-  const int head = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  // (head, quarter) from the flat id: workgroups are dispatched round-robin
+  // over the 8 XCDs; the 16 workgroups of 4 consecutive heads (which write
+  // interleaved 16-byte pieces of the same lines of the query layout) share
+  // one XCD, so its L2 merges them into whole lines
+  int head, quarter;
+  {
+    const int x = blockIdx.x, xcd = x & 7, i = x >> 3;
+    const int cluster = (i >> 4) * 8 + xcd;
+    head = cluster * 4 + ((i & 15) >> 2);
+    quarter = i & 3;
+  }
   if (head >= p.H) return;
 
   // W_UK[h][:, 128 q .. 128 q + 127]: wave w loads rows 32w..32w+31, four
@@ -115,12 +127,19 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
                                    w_lds + rb * AB_ROW + 16 * (chunk ^ wrow_swizzle(rb)) + off);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
     }
-    // lane holds column n, rows b = 8(r/4) + 4h + r%4
-    const int n = quarter * AB_COLS + 32 * w + l32;
+    // lane holds column 32w + l32 of the slice, rows b = 8(r/4) + 4h + r%4:
+    // transpose through LDS so each lane stores 8 consecutive columns of one
+    // sequence (one 16-byte piece of the query layout)
+    char* ol = o_lds[w];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int bb = b0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (bb < p.B) p.q[qop_index(bb, head, n, p.H)] = (bf16)(acc[r] * p.c);
+    for (int r = 0; r < 16; ++r)
+      *(bf16*)(ol + (8 * (r >> 2) + 4 * h + (r & 3)) * AB_OPITCH + 2 * l32) = (bf16)(acc[r] * p.c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = l + 64 * i, r = id >> 2, c8 = id & 3;
+      const u32x4 v = *(const u32x4*)(ol + r * AB_OPITCH + 16 * c8);
+      if (b0 + r < p.B)
+        *(u32x4*)(p.q + qop_index(b0 + r, head, quarter * AB_COLS + 32 * w + 8 * c8, p.H)) = v;
     }
     __syncthreads();   // a_lds is rewritten by the next chunk
   }
