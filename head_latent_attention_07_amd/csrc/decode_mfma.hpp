@@ -266,7 +266,7 @@ __device__ __forceinline__ void xcd_map(int x, int G, int per, int& q, int& g) {
 // once (at most MAX_SPLIT_BLOCKS; the split planner keeps every split within
 // that), so finding a tile's physical row is an LDS read instead of a global
 // or scalar load in the loop. Returns the first block index of the split.
-constexpr int MAX_SPLIT_BLOCKS = 2048;
+constexpr int MAX_SPLIT_BLOCKS = 64;
 
 template <int NT>
 __device__ __forceinline__ int load_block_table(const DecodeParams& p, int b, int t0, int t1,
@@ -300,6 +300,17 @@ __device__ __forceinline__ int64_t tile_base_row_direct(const DecodeParams& p, i
     return (int64_t)blk * p.block_size + (tile_t0 % p.block_size);
   }
   return (int64_t)b * p.seq_capacity + tile_t0;
+}
+
+// Physical rows of the first token of each tile of a split, tile i in lane
+// i (a split has at most 63 tiles: the split planner keeps it so), so a
+// tile's row in the loop is one v_readlane. Rows fit in 32 bits (the ABI
+// rejects larger caches). `tab` is the split's block table in LDS.
+__device__ __forceinline__ int tile_rows_lanes(const DecodeParams& p, int b, int t0, int t1,
+                                               const int* tab, int first_blk, int l) {
+  const int t = t0 + TILE * min(l, max((t1 - t0 + TILE - 1) / TILE - 1, 0));
+  if (p.block_table) return tab[t / p.block_size - first_blk] * p.block_size + (t % p.block_size);
+  return (int)((int64_t)b * p.seq_capacity + t);
 }
 
 // Physical row of the first token of a tile (tiles never cross a block:
@@ -666,9 +677,9 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
     return tile_load<NW>(p, tile, base_row, wi.t1 - 1 - tt0, w, l, k < ntiles);
   };
+  int trow = 0;   // lane i: physical row of tile i's first token (set in the prologue)
   auto load = [&](char* tile, int k) {
-    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    return load_at(tile, k, tile_base_row(p, wi.b, tt0, blk_tab, first_blk_of(p, wi.t0)));
+    return load_at(tile, k, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)));
   };
   auto dma = [&](char* tile, int k) { load(tile, k).all(); };
   const auto no_issue = [](int) {};
@@ -692,6 +703,7 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
+  trow = tile_rows_lanes(p, wi.b, wi.t0, wi.t1, blk_tab, first_blk_of(p, wi.t0), l);
 
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (attempt > 0) {

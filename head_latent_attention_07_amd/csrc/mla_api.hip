@@ -84,10 +84,9 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   int forced = (opts && opts->num_splits > 0) ? opts->num_splits : env_int("MLA_SPLITS");
   if (forced > 0) S = forced;
   S = std::max(1, std::min(S, ceil_div(len, TILE)));
-  // a split of a paged cache touches at most MAX_SPLIT_BLOCKS blocks (its
-  // table is staged in LDS): with the smallest block size (32) and tokens
-  // per split rounded up to 32, TS <= 2046*32 + 31 keeps ceil(TS/32)+1 <= 2048
-  if (act != MLA_F32) S = std::max(S, ceil_div(len, (MAX_SPLIT_BLOCKS - 2) * TILE));
+  // a split has at most 63 tiles (the attention kernel keeps one tile row per
+  // lane): tokens per split, rounded up to 32, stay <= 62*32 + 31
+  if (act != MLA_F32) S = std::max(S, ceil_div(len, 62 * TILE));
   int ts = ceil_div(len, S);
   ts = ceil_div(ts, TILE) * TILE;
   if (act == MLA_F32) ts = std::min(ts, F32_MAX_SPLIT);
@@ -148,6 +147,7 @@ mla_status check_decode(const mla_dims* dims, const void* q_nope, const void* q_
   if (cdt == MLA_FP8_E4M3 && !scales) return MLA_ERR_INVALID_ARG;
   const size_t ce = elem_size(cdt);
   if (ls < D_C || rs < D_R || rows < 1) return MLA_ERR_INVALID_ARG;
+  if (rows > INT32_MAX) return MLA_ERR_UNSUPPORTED;   // row indices are 32-bit in the kernels
   if (!aligned16(latent) || !aligned16(rope) || (ls * ce) % 16 != 0 || (rs * ce) % 16 != 0)
     return MLA_ERR_INVALID_ARG;
   const size_t ae = elem_size(act);

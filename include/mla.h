@@ -166,7 +166,8 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t ma
  *   act_dtype   MLA_F32 (requires an MLA_F32 cache) or MLA_BF16 (bf16 or fp8
  *               cache); bf16 math uses bf16 MFMA operands, fp32 accumulation
  *   latent, rope, strides, scales (fp8 only), cache_dtype: the cache
- *   cache_rows  total rows of the cache arrays
+ *   cache_rows  total rows of the cache arrays, at most 2^31 - 1
+ *               (MLA_ERR_UNSUPPORTED otherwise)
  *   lengths     [batch] int32 (device)
  *   max_len     host upper bound of lengths (sizes the split plan)
  *   softmax_scale  usually 1/sqrt(d_nope + d_rope)
