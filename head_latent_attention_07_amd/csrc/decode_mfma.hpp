@@ -190,11 +190,18 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
     __builtin_amdgcn_sched_barrier(0);
   }
   // accumulator row r of this lane is token 8(r/4) + 4h + r%4 of the tile
+  // fp8 cache: the row scales of this lane's 16 rows, 4 consecutive rows per
+  // 16-byte read
+  f32x4 sc4[4];
+  if (CK == CACHE_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc4[i] = *(const f32x4*)(scale + 8 * i + 4 * h);
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = 8 * (r >> 2) + 4 * h + (r & 3);
     float v = sacc[r];
-    if (CK == CACHE_FP8) v *= scale[row];
+    if (CK == CACHE_FP8) v *= sc4[r >> 2][r & 3];
     sv[r] = (tile_t0 + row < t1) ? v : -INFINITY;
   }
   float m4[4];
@@ -229,10 +236,15 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
   for (int s = 0; s < AHEAD; ++s) ring[s] = v_op(s);
   st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
   const float mref = st.m_ref;
+  f32x4 sc4[4];
+  if (CK == CACHE_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc4[i] = *(const f32x4*)(scale + 8 * i + 4 * h);
+  }
   auto weight = [&](int r) {
     float e = fast_exp2(sv[r] - mref);
     st.lsum += e;
-    if (CK == CACHE_FP8) e *= scale[8 * (r >> 2) + 4 * h + (r & 3)];
+    if (CK == CACHE_FP8) e *= sc4[r >> 2][r & 3];
     return (bf16)e;
   };
   bf16x8 pb[2];
@@ -303,7 +315,7 @@ __device__ __forceinline__ int64_t tile_base_row_direct(const DecodeParams& p, i
 }
 
 // Physical rows of the first token of each tile of a split, tile i in lane
-// i (a split has at most 63 tiles: the split planner keeps it so), so a
+// i (a split has at most 64 tiles: the split planner keeps it so), so a
 // tile's row in the loop is one v_readlane. Rows fit in 32 bits (the ABI
 // rejects larger caches). `tab` is the split's block table in LDS.
 __device__ __forceinline__ int tile_rows_lanes(const DecodeParams& p, int b, int t0, int t1,
@@ -449,58 +461,76 @@ __device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* t
 // shared. Staging layout: latent [32][512], RoPE key [32][64], scales [32].
 constexpr int STG_ROPE = TILE * D_C;                 // 16384
 constexpr int STG_SCALE = STG_ROPE + TILE * D_R;     // 18432
-constexpr int STG_BYTES = STG_SCALE + TILE * 4;      // scales as fp32
+constexpr int STG_BYTES = STG_SCALE;                 // codes only (18 KB)
 
-// Per wave: 16/NW latent loads (two 512-byte rows each) and the RoPE-key
-// halves (rows 0-15, rows 16-31) spread over the waves. The bf16 row scales
-// are not DMA'd (a dword load could cross the end of an odd-length scale
-// array); lanes 0..31 load them as 2-byte values into a register instead.
+// Per tile and wave: 16/NW latent pieces (two 512-byte rows each) and
+// ceil(2/NW) RoPE-key pieces (16 rows each; with four waves, waves 2 and 3
+// issue an empty load into a dummy area instead, so every wave issues the
+// same number and the vmcnt waits stay exact). Loads are the inline-asm
+// direct-to-LDS loads of the bf16 kernel; the row scales of the whole split
+// are loaded into LDS by the prologue.
 template <int NW>
-struct Fp8Dma {
+struct Fp8Load {
   static constexpr int LAT = 16 / NW;
-  static constexpr int MISC = (2 + NW - 1) / NW;
+  static constexpr int ROPE = (2 + NW - 1) / NW;
+  static constexpr int PIECES = LAT + ROPE;
+  TileRsrc rs;
+  __amdgpu_buffer_rsrc_t none;
+  char* stage;
+  char* dummy;
+  int lsb, rsb, last_row, w, l;
+
+  __device__ __forceinline__ void piece(int i) const {
+    if (i < LAT) {
+      const int pair = __builtin_amdgcn_readfirstlane(w * LAT + i);   // rows 2 pair, 2 pair + 1
+      const int row = 2 * pair + (l >> 5);
+      dma16(rs.lat, lds_u32(stage + pair * 2 * D_C), min(row, last_row) * lsb + 16 * (l & 31), 0);
+    } else {
+      const int pc = __builtin_amdgcn_readfirstlane(w * ROPE + (i - LAT));  // 0, 1 real, >= 2 empty
+      const bool real = pc < 2;
+      const int row = 16 * min(pc, 1) + (l >> 2);
+      dma16(real ? rs.rope : none,
+            lds_u32(real ? stage + STG_ROPE + min(pc, 1) * 16 * D_R : dummy),
+            real ? min(row, last_row) * rsb + 16 * (l & 3) : 0, 0);
+    }
+  }
+  __device__ __forceinline__ void all() const {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) piece(i);
+  }
+  // after MFMA t (0..67) of the tile being computed
+  __device__ __forceinline__ void step(int t) const {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i)
+      if (t == 2 + (64 * i) / PIECES) piece(i);
+  }
 };
 
 template <int NW>
-__device__ __forceinline__ float fp8_tile_dma(const DecodeParams& p, char* stage,
-                                              int64_t base_row, int last_row, int w, int l,
-                                              bool valid) {
-  const TileRsrc rs = tile_rsrc(p, base_row, 1, valid);
-  const int lsb = (int)p.latent_stride, rsb = (int)p.rope_stride;
-#pragma unroll
-  for (int k = 0; k < Fp8Dma<NW>::LAT; ++k) {
-    const int pair = w * Fp8Dma<NW>::LAT + k;          // rows 2*pair, 2*pair+1
-    const int row = 2 * pair + (l >> 5);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs.lat, (__attribute__((address_space(3))) void*)(stage + pair * 2 * D_C), 16,
-        min(row, last_row) * lsb + 16 * (l & 31), 0, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < Fp8Dma<NW>::MISC; ++k) {
-    const int piece = w * Fp8Dma<NW>::MISC + k;          // RoPE rows 16*piece ..
-    if (piece < 2) {
-      const int row = 16 * piece + (l >> 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs.rope, (__attribute__((address_space(3))) void*)(stage + STG_ROPE + piece * 16 * D_R), 16,
-          min(row, last_row) * rsb + 16 * (l & 3), 0, 0, 0);
-    }
-  }
-  // scale of row (lane) of the tile, wave 0 lanes 0..31
-  float sc = 1.0f;
-  if (w == 0 && l < TILE) {
-    int64_t r = base_row + min(l, last_row);
-    r = (r >= 0 && r < p.rows) ? r : 0;
-    sc = (float)p.scales[r];
-  }
-  return sc;
+__device__ __forceinline__ Fp8Load<NW> fp8_load(const DecodeParams& p, char* stage, char* dummy,
+                                                int64_t base_row, int last_row, int w, int l,
+                                                bool valid) {
+  Fp8Load<NW> t;
+  t.rs = tile_rsrc(p, base_row, 1, valid);
+  t.none = make_rsrc(p.latent, 0);
+  t.stage = stage;
+  t.dummy = dummy;
+  t.lsb = (int)p.latent_stride;
+  t.rsb = (int)p.rope_stride;
+  t.last_row = last_row;
+  t.w = w;
+  t.l = l;
+  return t;
 }
 
-// Widen one staged tile into a bf16 tile; `scale` receives the row scales.
+// Widen one staged tile into a bf16 tile (all NT threads of the workgroup):
+// e4m3 codes convert to bf16 exactly; the row scales are applied in the
+// attention math (to the scores and to the weights).
 template <int NT>
-__device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, float* scale,
-                                               int tid) {
+__device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, int tid) {
   constexpr int CHUNKS = TILE * (D_QK / 16);  // 1152 chunks of 16 codes
-#pragma unroll
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
   for (int i = 0; i < (CHUNKS + NT - 1) / NT; ++i) {
     const int q = i * NT + tid;
     if (CHUNKS % NT == 0 || q < CHUNKS) {
@@ -533,7 +563,7 @@ __device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, fl
       *(u32x4*)(dst + 16 * ((2 * c + 1) ^ sw)) = hi;
     }
   }
-  if (tid < TILE) scale[tid] = ((const float*)(stage + STG_SCALE))[tid];
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Common prologue: work item of this workgroup, the empty-split case, the
@@ -778,12 +808,15 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(1024))) char tiles[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage[STG_BYTES];
+  constexpr int P = Fp8Load<NW>::PIECES;   // wave-wide loads per tile per wave
+  // raw fp8 tiles k+1 .. k+3 in three stages, bf16 tiles k, k+1 in two buffers
+  __shared__ __attribute__((aligned(1024))) char stage[3][STG_BYTES];
+  __shared__ __attribute__((aligned(1024))) char tbuf[2][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
-  __shared__ float scl[2][TILE];
+  __shared__ __attribute__((aligned(1024))) char dummy[1024];
+  __shared__ float scl_all[64 * TILE];   // row scales of the split, tile i at 32 i
   __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
-  __shared__ int overflow;
+  __shared__ int flags[4];
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -793,67 +826,103 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     write_empty(wi, h);
     return;
   }
+  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  auto load_at = [&](int k, int64_t base_row) {
+    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
+    return fp8_load<NW>(p, stage[k % 3], dummy, base_row, wi.t1 - 1 - tt0, w, l, k < ntiles);
+  };
+  int trow = 0;   // lane i: physical row of tile i's first token (set in the prologue)
+  auto load = [&](int k) { return load_at(k, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1))); };
+
+  // Prologue: raw tiles 0..2 (block entries on the scalar path), the queries,
+  // the split's block table; one wait; then the per-tile rows and the scales
+  // of the whole split; widen tile 0.
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    load_at(k, tile_base_row_direct(p, wi.b, wi.t0 + min(k, ntiles - 1) * TILE)).all();
   bf16x8 qreg[QREG], qtmp[QLDS];
-  char* qpe = qpe_all + w * 4096;
   load_q(p, wi, l, qreg, qtmp);
+  load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
+  char* qpe = qpe_all + w * 4096;
   store_qpe(qtmp, qpe, l);
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
-  if (tid == 0) overflow = 0;
-
-  const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
-  const int first_blk = load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
-  float sc_next = 1.0f;
-  auto dma = [&](int k) {
-    const bool valid = k < ntiles;
-    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    sc_next = fp8_tile_dma<NW>(p, stage, tile_base_row(p, wi.b, tt0, blk_tab, first_blk),
-                               wi.t1 - 1 - tt0, w, l, valid);
-  };
-  // the staged tile is complete once the loads landed and the scales are in LDS
-  auto finish_stage = [&]() {
-    wait_vm_lgkm0<0>();
-    if (tid < TILE) ((float*)(stage + STG_SCALE))[tid] = sc_next;
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-  };
+  compiler_fence();
+  trow = tile_rows_lanes(p, wi.b, wi.t0, wi.t1, blk_tab, first_blk_of(p, wi.t0), l);
+  for (int i = tid; i < ntiles * TILE; i += NT) {
+    const int k = i >> 5, r = i & 31;
+    const int last = wi.t1 - 1 - (wi.t0 + k * TILE);
+    int64_t row = (int64_t)__shfl(trow, k, 64) + min(r, last);
+    row = (row >= 0 && row < p.rows) ? row : 0;
+    scl_all[i] = (float)p.scales[row];
+  }
+  fp8_tile_widen<NT>(stage[0], tbuf[0], tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+
   for (int attempt = 0; attempt < 2; ++attempt) {
-    dma(0);
-    finish_stage();
-    for (int k = 0; k < ntiles; ++k) {
-      // the stage holds tile k: widen it, then refill the stage with tile k+1
-      // while tile k is computed
-      fp8_tile_widen<NT>(stage, tiles[k & 1], scl[k & 1], tid);
+    if (attempt > 0) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) load(k).all();
+      wait_vm_lgkm0<0>();   // raw tiles 0..2 landed (rare path: no overlap needed)
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      fp8_tile_widen<NT>(stage[0], tbuf[0], tid);
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
-      dma(k + 1);
-      if (tile_compute<CACHE_FP8>(tiles[k & 1], scl[k & 1], wi.t0 + k * TILE, wi.t1, qreg,
-                                  qpe + 16 * l, la, h, st, [](int) {}) && l == 0)
-        overflow = 1;
-      finish_stage();
+      compiler_fence();
     }
-    if (overflow == 0) break;
+    // phase k: widen raw tile k+1 into the other bf16 buffer (landed and
+    // published by the previous barrier), compute tile k while loading raw
+    // tile k+3 into the stage tile k came from, wait for raw tile k+2,
+    // barrier
+    bool ovf = false;
+    for (int k = 0; k < ntiles; ++k) {
+      fp8_tile_widen<NT>(stage[(k + 1) % 3], tbuf[(k + 1) & 1], tid);
+      const Fp8Load<NW> next = load(k + 3);
+      ovf |= tile_compute<CACHE_FP8>(tbuf[k & 1], scl_all + TILE * k, wi.t0 + k * TILE, wi.t1, qreg,
+                                     qpe + 16 * l, la, h, st, [&](int j) { next.step(j); });
+      wait_vm_lgkm0<P>();   // raw tile k+2 landed, k+3 may be in flight
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+    }
+    wait_vm_lgkm0<0>();
+    if (l == 0) flags[w] = ovf ? 1 : 0;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    int any_ovf = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any_ovf |= flags[i];
+    any_ovf = __builtin_amdgcn_readfirstlane(any_ovf);
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (any_ovf == 0) break;
     // rare path (see the bf16 kernel): true maximum, then recompute
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
-      dma(k);
-      finish_stage();
-      fp8_tile_widen<NT>(stage, tiles[0], scl[0], tid);
+      load(k).all();
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
-      float sv[16];
-      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8>(tiles[0], scl[0], wi.t0 + k * TILE, wi.t1,
-                                                   qreg, qpe + 16 * l, la, h, sv, [](int) {}));
+      compiler_fence();
+      fp8_tile_widen<NT>(stage[k % 3], tbuf[0], tid);
+      wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      float sv[16];
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8>(tbuf[0], scl_all + TILE * k, wi.t0 + k * TILE,
+                                                   wi.t1, qreg, qpe + 16 * l, la, h, sv, [](int) {}));
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
     }
     reset_state(st, mtrue);
-    if (tid == 0) overflow = 0;
   }
-  // finish_stage ended with a barrier: no load in flight, no wave reading
-  write_partial(wi, st, h, l, tiles[w >> 1] + (w & 1) * PART_SCR_BYTES);
+  write_partial(wi, st, h, l, tbuf[w >> 1] + (w & 1) * PART_SCR_BYTES);
 }
 
 }  // namespace mla

@@ -84,9 +84,9 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   int forced = (opts && opts->num_splits > 0) ? opts->num_splits : env_int("MLA_SPLITS");
   if (forced > 0) S = forced;
   S = std::max(1, std::min(S, ceil_div(len, TILE)));
-  // a split has at most 63 tiles (the attention kernel keeps one tile row per
-  // lane): tokens per split, rounded up to 32, stay <= 62*32 + 31
-  if (act != MLA_F32) S = std::max(S, ceil_div(len, 62 * TILE));
+  // a split has at most 64 tiles (the attention kernel keeps one tile row per
+  // lane): ceil(len / S) <= 2048, which stays <= 2048 when rounded up to 32
+  if (act != MLA_F32) S = std::max(S, ceil_div(len, 64 * TILE));
   int ts = ceil_div(len, S);
   ts = ceil_div(ts, TILE) * TILE;
   if (act == MLA_F32) ts = std::min(ts, F32_MAX_SPLIT);
