@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,16 +35,113 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
+def m0_conflicts(asm_text: str) -> list:
+    """Kernels whose inline assembly writes M0 without saving it (the decode
+    kernels' direct-to-LDS loads) must not use M0 anywhere else: returns the
+    names of those that do, from the device assembly of the library."""
+    bad, fn, in_asm, asm_m0, other_m0 = [], None, False, False, False
+
+    def close():
+        if fn and asm_m0 and other_m0:
+            bad.append(fn)
+
+    for line in asm_text.splitlines():
+        s = line.strip()
+        m = re.match(r"^([A-Za-z_][\w.$]*):\s*(;.*)?$", s)
+        if m and not s.startswith(".") and m.group(1).startswith("_Z"):
+            close()
+            fn, asm_m0, other_m0 = m.group(1), False, False
+            continue
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if not s or s.startswith(";") or s.startswith("."):
+            continue
+        if re.search(r"\bm0\b", s):
+            if in_asm:
+                asm_m0 = True
+            else:
+                other_m0 = True
+    close()
+    return bad
+
+
+_SCC_WRITE = re.compile(r"^s_(cmp|and|or|xor|andn2|orn2|nand|nor|xnor|add_|sub_|addk|lshl|lshr|"
+                        r"ashr|bfe|min|max|not|abs|bcnt|absdiff)")
+_SCC_READ = re.compile(r"^s_(cselect|cbranch_scc|addc|subb|cmov)")
+
+
+def scc_conflicts(asm_text: str) -> list:
+    """Places where the compiler reads SCC after an inline-assembly block that
+    writes it and before anything redefines it (an undeclared SCC clobber):
+    (kernel, instruction) pairs from the device assembly of the library."""
+    bad, fn, in_asm, asm_writes, pending = [], None, False, False, False
+    for line in asm_text.splitlines():
+        s = line.strip()
+        m = re.match(r"^(_Z[\w.$]*):", s)
+        if m:
+            fn, pending = m.group(1), False
+            continue
+        if s.startswith(";;#ASMSTART"):
+            in_asm, asm_writes = True, False
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            pending = pending or asm_writes
+            continue
+        if not s or s.startswith(";") or s.startswith("."):
+            if s.startswith(".LBB"):
+                pending = False
+            continue
+        op = s.split()[0]
+        if in_asm:
+            asm_writes = asm_writes or bool(_SCC_WRITE.match(op))
+            continue
+        if pending:
+            if _SCC_READ.match(op):
+                bad.append((fn, s))
+                pending = False
+            elif _SCC_WRITE.match(op) or op.startswith("s_cbranch") or op.startswith("s_branch"):
+                pending = False
+    return bad
+
+
 def build(verbose: bool = False) -> str:
-    """Compile the library; returns the path of the built .so."""
+    """Compile the library (and, alongside, the device assembly for the M0
+    check); returns the path of the built .so."""
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+    asm_path = LIB_PATH + ".s.tmp"
+    asm_flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    asm_cmd = [hipcc(), *asm_flags, "--cuda-device-only", "-S", *SOURCES, "-o", asm_path]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    lib_proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    asm_proc = subprocess.Popen(asm_cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    lib_out = lib_proc.communicate()
+    asm_out = asm_proc.communicate()
+    if lib_proc.returncode != 0:
+        sys.stderr.write(lib_out[0] + lib_out[1])
+        raise RuntimeError(f"hipcc failed with status {lib_proc.returncode}")
+    if asm_proc.returncode != 0:
+        sys.stderr.write(asm_out[0] + asm_out[1])
+        raise RuntimeError(f"hipcc -S failed with status {asm_proc.returncode}")
+    with open(asm_path) as f:
+        asm_text = f.read()
+    os.remove(asm_path)
+    bad = m0_conflicts(asm_text)
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("the compiler uses M0 in kernels whose direct-to-LDS loads assume it "
+                           "does not: " + ", ".join(bad))
+    bad_scc = scc_conflicts(asm_text)
+    if bad_scc:
+        os.remove(tmp)
+        raise RuntimeError("SCC read after an inline-assembly block that writes it: " +
+                           "; ".join(f"{f}: {i}" for f, i in bad_scc[:5]))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -37,6 +37,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -160,13 +161,33 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
 }
 
-// S^T = K Q^T for one tile; returns this lane's 16 scores (masked, scaled
-// for fp8) and the tile max of this lane's head. The A operands are read from
-// LDS three k-steps ahead of the MFMA that consumes them (a software pipeline
-// pinned with scheduling barriers), so LDS latency overlaps the MFMA chain.
-// `issue(j)` runs after k-step j's MFMA (the main loop issues the next
-// tile's loads there).
-template <int CK, typename Issue>
+// The S^T accumulator of the QK^T chain is kept in VGPRs (the 256 AGPRs
+// hold O^T; the compiler would otherwise park an O^T tile in VGPRs and copy
+// it back and forth around every tile, and copy S^T out of AGPRs). Inline
+// assembly fixes the register class; the compiler does not see these as
+// MFMAs, so the wait states an XDL result needs before a vector ALU read are
+// inserted explicitly (mfma_vgpr_settle, bound to the accumulator so no read
+// moves above it). Back-to-back MFMAs accumulating into the same registers
+// need none.
+__device__ __forceinline__ void mfma_vgpr_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_settle(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+}
+
+// S^T = K Q^T for one tile: this lane's 16 scores (scaled for fp8; masked
+// past the split's end, which only its last tile reaches). With FIRST the
+// tile's max of this lane's head is returned (the exponent reference comes
+// from the first tile); otherwise no max is taken. The A operands are read
+// from LDS three k-steps ahead of the MFMA that consumes them (a software
+// pipeline pinned with scheduling barriers), so LDS latency overlaps the
+// MFMA chain. `issue(j)` runs after k-step j's MFMA (the main loop issues
+// the next tile's loads there).
+template <int CK, bool FIRST, typename Issue>
 __device__ __forceinline__ float tile_scores(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG],
                                              const char* qpe, const LaneAddr& la, int h,
@@ -178,17 +199,19 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
   bf16x8 qring[QLDS];
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j) ring[j] = *(const bf16x8*)(tile + a_off(j));
-  f32x16 sacc = f32x16{};
+  f32x16 sacc;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     if (j + AHEAD < NJ) ring[(j + AHEAD) % (AHEAD + 1)] = *(const bf16x8*)(tile + a_off(j + AHEAD));
     if (j + AHEAD >= QREG && j + AHEAD < NJ)
       qring[j + AHEAD - QREG] = *(const bf16x8*)(qpe + (j + AHEAD - QREG) * 1024);
     const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : qring[j < QREG ? 0 : j - QREG];
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[j % (AHEAD + 1)], bq, sacc, 0, 0, 0);
+    if (j == 0) mfma_vgpr_first(sacc, ring[0], bq);
+    else mfma_vgpr_acc(sacc, ring[j % (AHEAD + 1)], bq);
     issue(j);
     __builtin_amdgcn_sched_barrier(0);
   }
+  mfma_vgpr_settle(sacc);
   // accumulator row r of this lane is token 8(r/4) + 4h + r%4 of the tile
   // fp8 cache: the row scales of this lane's 16 rows, 4 consecutive rows per
   // 16-byte read
@@ -198,12 +221,13 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
     for (int i = 0; i < 4; ++i) sc4[i] = *(const f32x4*)(scale + 8 * i + 4 * h);
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-    float v = sacc[r];
-    if (CK == CACHE_FP8) v *= sc4[r >> 2][r & 3];
-    sv[r] = (tile_t0 + row < t1) ? v : -INFINITY;
+  for (int r = 0; r < 16; ++r) sv[r] = (CK == CACHE_FP8) ? sacc[r] * sc4[r >> 2][r & 3] : sacc[r];
+  if (tile_t0 + TILE > t1) {   // wave-uniform: the split's last tile only
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (tile_t0 + 8 * (r >> 2) + 4 * h + (r & 3) >= t1) sv[r] = -INFINITY;
   }
+  if (!FIRST) return 0.f;
   float m4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -212,18 +236,20 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
 }
 
 // One 32-token tile: scores, softmax weights against m_ref, O^T += C^T P^T.
-// Returns true if some score of this wave exceeded m_ref + OVERFLOW_SLACK.
-// The weights of the first 16 tokens (B operand of the first 16 PV MFMAs)
-// are computed before the PV chain, those of the last 16 between its first
-// MFMAs, where the vector ALU work overlaps the matrix pipe. `issue(t)` runs
-// after MFMA t of the tile's 68 (36 for S, 32 for PV).
-template <int CK, typename Issue>
-__device__ __forceinline__ bool tile_compute(const char* tile, const float* scale, int tile_t0,
+// With FIRST (the split's first tile) an unset reference (-inf) becomes the
+// tile's max. The weights of the first 16 tokens (B operand of the first 16
+// PV MFMAs) are computed before the PV chain, those of the last 16 between
+// its first MFMAs, where the vector ALU work overlaps the matrix pipe.
+// `issue(t)` runs after MFMA t of the tile's 68 (36 for S, 32 for PV).
+// Scores far above the reference are caught once per split, from the sum
+// of the weights (see split_overflowed).
+template <int CK, bool FIRST, typename Issue>
+__device__ __forceinline__ void tile_compute(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG], const char* qpe,
                                              const LaneAddr& la, int h, WaveState& st,
                                              const Issue& issue) {
   float sv[16];
-  const float tmax = tile_scores<CK>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv, issue);
+  const float tmax = tile_scores<CK, FIRST>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv, issue);
   // PV operands: 32 steps (2 k-steps x 16 dim tiles), two ahead
   constexpr int NS = 32, AHEAD = 2;
   auto v_op = [&](int s) {
@@ -234,33 +260,60 @@ __device__ __forceinline__ bool tile_compute(const char* tile, const float* scal
   bf16x8 ring[AHEAD + 1];
 #pragma unroll
   for (int s = 0; s < AHEAD; ++s) ring[s] = v_op(s);
-  st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
+  if (FIRST) st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
   const float mref = st.m_ref;
   f32x4 sc4[4];
   if (CK == CACHE_FP8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc4[i] = *(const f32x4*)(scale + 8 * i + 4 * h);
   }
-  auto weight = [&](int r) {
-    float e = fast_exp2(sv[r] - mref);
-    st.lsum += e;
-    if (CK == CACHE_FP8) e *= sc4[r >> 2][r & 3];
-    return (bf16)e;
+  // weights in place of the scores; the sum of the tile's 16 weights of this
+  // lane as a pairwise tree per half, pinned where it is formed (the
+  // compiler would otherwise sink a serial chain of adds past the PV chain)
+  auto weights = [&](int r0) {
+#pragma unroll
+    for (int r = r0; r < r0 + 8; ++r) sv[r] = fast_exp2(sv[r] - mref);
+    float half = ((sv[r0] + sv[r0 + 1]) + (sv[r0 + 2] + sv[r0 + 3])) +
+                 ((sv[r0 + 4] + sv[r0 + 5]) + (sv[r0 + 6] + sv[r0 + 7]));
+    asm volatile("" : "+v"(half));
+    st.lsum += half;
+  };
+  auto pbf = [&](int r) {
+    return (CK == CACHE_FP8) ? (bf16)(sv[r] * sc4[r >> 2][r & 3]) : (bf16)sv[r];
   };
   bf16x8 pb[2];
+  weights(0);
 #pragma unroll
-  for (int r = 0; r < 8; ++r) pb[0][r] = weight(r);
+  for (int r = 0; r < 8; ++r) pb[0][r] = pbf(r);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s + AHEAD < NS) ring[(s + AHEAD) % (AHEAD + 1)] = v_op(s + AHEAD);
     const int dt = s & 15;
     st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % (AHEAD + 1)], pb[s >> 4], st.o[dt], 0, 0, 0);
-    if (s < 8) pb[1][s] = weight(8 + s);
+    // second half of the weights, a little per MFMA: exps, sum, packing
+    if (s < 8) sv[8 + s] = fast_exp2(sv[8 + s] - mref);
+    if (s == 8) {
+      float half = ((sv[8] + sv[9]) + (sv[10] + sv[11])) + ((sv[12] + sv[13]) + (sv[14] + sv[15]));
+      asm volatile("" : "+v"(half));
+      st.lsum += half;
+    }
+    if (s >= 9 && s < 13) {
+      pb[1][2 * (s - 9)] = pbf(8 + 2 * (s - 9));
+      pb[1][2 * (s - 9) + 1] = pbf(9 + 2 * (s - 9));
+    }
     issue(36 + s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  return __any(tmax > mref + OVERFLOW_SLACK);
+}
+
+// Every weight of a split is 2^(score - m_ref) <= its lane's share of the
+// softmax denominator, so a share below 2^64 bounds every weight (and the
+// accumulators) far from fp32 and bf16 overflow. A share at or above it
+// (or NaN) can only come from a score well above the first tile's max: the
+// workgroup then recomputes the split against the true max.
+__device__ __forceinline__ bool split_overflowed(const WaveState& st) {
+  return __any(!(st.lsum < 0x1p64f));
 }
 
 // Map a flat workgroup id to (sequence*split index q, head group g).
@@ -343,49 +396,57 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
 }
 
-// Buffer resources of one tile's rows: latent and RoPE-key arrays rebased at
-// the tile's first physical row (row offsets inside a tile fit in 32 bits).
+// Buffer resources of one tile: the latent and RoPE-key arrays rebased at the
+// tile's first physical row, with a record count of `nvalid` rows, so rows
+// past the split's end (all rows of a tile past the split: nvalid = 0) read
+// as zeros. A row index outside the cache reads row 0 instead (never faults).
+// Row strides are below 2^24 bytes (the ABI checks), so every offset inside
+// a tile fits in 32 bits.
 struct TileRsrc {
   __amdgpu_buffer_rsrc_t lat, rope;
 };
 
-__device__ __forceinline__ TileRsrc tile_rsrc(const DecodeParams& p, int64_t base_row, int esize,
-                                              bool valid = true) {
+__device__ __forceinline__ TileRsrc tile_rsrc(const DecodeParams& p, int row0, int nvalid,
+                                              int esize) {
   TileRsrc t;
-  base_row = (base_row >= 0 && base_row < p.rows) ? base_row : 0;
-  const int64_t left = valid ? p.rows - base_row : 0;  // 0: every load returns zeros
-  t.lat = make_rsrc((const char*)p.latent + base_row * p.latent_stride * esize,
-                    left * p.latent_stride * esize);
-  t.rope = make_rsrc((const char*)p.rope + base_row * p.rope_stride * esize,
-                     left * p.rope_stride * esize);
+  const int rows = (int)p.rows;   // below 2^31 (the ABI checks)
+  row0 = __builtin_amdgcn_readfirstlane((row0 >= 0 && row0 < rows) ? row0 : 0);
+  nvalid = __builtin_amdgcn_readfirstlane(max(min(nvalid, rows - row0), 0));
+  const int lsb = (int)p.latent_stride * esize, rsb = (int)p.rope_stride * esize;
+  t.lat = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.latent + (int64_t)row0 * lsb),
+                                            (short)0, nvalid * lsb, 0x00020000);
+  t.rope = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.rope + (int64_t)row0 * rsb),
+                                             (short)0, nvalid * rsb, 0x00020000);
   return t;
 }
 
-// One wave-wide direct-to-LDS load: 16 bytes per lane from
-// rsrc + soffset + voffset (bounds-checked against the resource: zeros past
-// its end) to LDS at lds_addr + 16 * lane (lds_addr wave-uniform, in M0).
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave-wide direct-to-LDS load: 16 bytes per lane from rsrc + voffset
+// (zeros past the resource's records) to LDS at m0_base + IMM + 16 * lane
+// (m0_base wave-uniform).
+//
 // Written as inline assembly so that the compiler's wait-count tracking does
 // not see it: it cannot tell which LDS buffer each pending load targets once
 // control flow merges, and would then wait for every load in flight before
 // each LDS read. The kernels wait for these loads themselves (vmcnt) before
 // the barrier that publishes a tile, and fence the compiler there.
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// M0 is reserved by the compiler, so the block saves and restores it.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voffset,
-                                      int soffset) {
-  int saved_m0;
+//
+// M0 is written without being saved: the compiler uses M0 for nothing in the
+// decode kernels (the library build checks the generated code for this and
+// fails otherwise). The s_nop covers the M0-write hazard; the add writes SCC
+// (declared, so no scalar condition is kept across the block).
+template <int IMM>
+__device__ __forceinline__ void dma16_m0(__amdgpu_buffer_rsrc_t rsrc, uint32_t m0_base, int voffset) {
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 m0, %0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
-      : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
-      : "memory");
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0_base), "v"(voffset), "s"(rsrc), "n"(IMM)
+      : "memory", "scc");
 }
 
 // Compiler-only fence: no memory access moves across it (emits nothing).
@@ -394,64 +455,83 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // bf16 cache: direct global->LDS loads (16 bytes per lane), 36 wave-wide
 // loads per tile (32 latent rows of 1 KB, 4 groups of 8 RoPE-key rows), of
 // which each of the NW waves issues PIECES: piece i < RPW is latent row
-// w*RPW + i, the others are RoPE-key groups. Lane i writes LDS slot i of its
-// 1 KB, so it fetches the chunk that the swizzle places there. Rows past the
-// split's last token re-read the last token (their scores are masked).
-// With valid == false the loads are still issued (so every wave's count of
-// loads in flight stays the same on every path) but read nothing from memory.
+// u = w*RPW + i, the others are RoPE-key groups. Lane i writes LDS slot i of
+// its 1 KB, so it fetches the chunk that the swizzle places there. The lane
+// offsets of a wave's pieces relative to a tile's first row are the same for
+// every tile (tile_piece_offsets, kept in registers); a tile only brings its
+// two buffer resources.
 //
 // A wave that issues several direct-to-LDS loads back to back stalls at issue
-// until the CU's memory pipeline accepts them (about a thousand cycles for a
-// tile's worth), and issues nothing else meanwhile. The main loop therefore
-// spreads the next tile's pieces through the MFMA chains of the current one
-// (step(t) after MFMA t), where a stall only delays MFMAs already queued.
+// until the CU's memory pipeline accepts them, and issues nothing else
+// meanwhile. The main loop therefore spreads the next tile's pieces through
+// the MFMA chains of the current one (step(t) after MFMA t), where a stall
+// only delays MFMAs already queued.
 template <int NW>
 struct TileLoad {
   static constexpr int RPW = TILE / NW;          // latent rows per wave
   static constexpr int GPW = 4 / NW;             // RoPE-key row groups per wave
   static constexpr int PIECES = RPW + GPW;       // 9, 18, 36
   TileRsrc rs;
-  char* tile;
-  int lsb, rsb, last_row, w, l;
+  uint32_t m_lat, m_rope;   // LDS address of this wave's first latent row / RoPE group
+  const int* voff;          // lane offsets of the pieces
 
-  __device__ __forceinline__ void piece(int i) const {
-    if (i < RPW) {
-      const int u = __builtin_amdgcn_readfirstlane(w * RPW + i);
-      dma16(rs.lat, lds_u32(tile + u * LAT_ROW), 16 * (l ^ lat_swz(u)),
-            __builtin_amdgcn_readfirstlane(min(u, last_row) * lsb));
-    } else {
-      const int v = w * GPW + (i - RPW);
-      const int row = 8 * v + (l >> 3);
-      dma16(rs.rope, lds_u32(tile + ROPE_OFF + v * 8 * ROPE_ROW),
-            min(row, last_row) * rsb + 16 * ((l & 7) ^ rope_swz(row)), 0);
-    }
+  template <int I>
+  __device__ __forceinline__ void piece() const {
+    if constexpr (I < RPW) dma16_m0<I * LAT_ROW>(rs.lat, m_lat, voff[I]);
+    else dma16_m0<(I - RPW) * 8 * ROPE_ROW>(rs.rope, m_rope, voff[I]);
   }
-  __device__ __forceinline__ void all() const {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) piece(i);
+  template <int... I>
+  __device__ __forceinline__ void all_(std::integer_sequence<int, I...>) const {
+    (piece<I>(), ...);
   }
+  __device__ __forceinline__ void all() const { all_(std::make_integer_sequence<int, PIECES>{}); }
   // after MFMA t (0..67) of the tile being computed: piece i goes out at
   // t = 2 + 64 i / PIECES, spread over both MFMA chains
+  template <int... I>
+  __device__ __forceinline__ void step_(int t, std::integer_sequence<int, I...>) const {
+    ((t == 2 + (64 * I) / PIECES ? piece<I>() : void()), ...);
+  }
   __device__ __forceinline__ void step(int t) const {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i)
-      if (t == 2 + (64 * i) / PIECES) piece(i);
+    step_(t, std::make_integer_sequence<int, PIECES>{});
   }
 };
 
 template <int NW>
-__device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* tile,
-                                                  int64_t base_row, int last_row, int w, int l,
-                                                  bool valid) {
+__device__ __forceinline__ void tile_piece_offsets(const DecodeParams& p, int w, int l,
+                                                   int (&voff)[TileLoad<NW>::PIECES]) {
+  constexpr int RPW = TileLoad<NW>::RPW, GPW = TileLoad<NW>::GPW;
+  const int lsb = (int)p.latent_stride * 2, rsb = (int)p.rope_stride * 2;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int u = w * RPW + i;
+    voff[i] = u * lsb + 16 * (l ^ lat_swz(u));
+  }
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int row = 8 * (w * GPW + i) + (l >> 3);
+    voff[RPW + i] = row * rsb + 16 * ((l & 7) ^ rope_swz(row));
+  }
+}
+
+// Loads of one tile (first physical row row0, nvalid valid rows) into `tile`.
+template <int NW>
+__device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* tile, int row0,
+                                                  int nvalid, int w, const int* voff) {
   TileLoad<NW> t;
-  t.rs = tile_rsrc(p, base_row, 2, valid);
-  t.tile = tile;
-  t.lsb = (int)(p.latent_stride * 2);
-  t.rsb = (int)(p.rope_stride * 2);
-  t.last_row = last_row;
-  t.w = w;
-  t.l = l;
+  t.rs = tile_rsrc(p, row0, nvalid, 2);
+  t.m_lat = __builtin_amdgcn_readfirstlane(lds_u32(tile) + w * TileLoad<NW>::RPW * LAT_ROW);
+  t.m_rope = __builtin_amdgcn_readfirstlane(lds_u32(tile) + ROPE_OFF +
+                                            w * TileLoad<NW>::GPW * 8 * ROPE_ROW);
+  t.voff = voff;
   return t;
+}
+
+// Zero a workgroup's LDS tile buffers (before their first loads): lanes past
+// a split's end are written with zeros by the loads, and this keeps every
+// byte a tile's masked rows could hold finite in any case.
+template <int NT>
+__device__ __forceinline__ void zero_lds(char* buf, int bytes, int tid) {
+  for (int i = tid * 16; i < bytes; i += NT * 16) *(u32x4*)(buf + i) = u32x4{0, 0, 0, 0};
 }
 
 // fp8 cache: the raw codes of a tile (32 rows x 576 bytes) and its 32 bf16
@@ -466,60 +546,64 @@ constexpr int STG_BYTES = STG_SCALE;                 // codes only (18 KB)
 // Per tile and wave: 16/NW latent pieces (two 512-byte rows each) and
 // ceil(2/NW) RoPE-key pieces (16 rows each; with four waves, waves 2 and 3
 // issue an empty load into a dummy area instead, so every wave issues the
-// same number and the vmcnt waits stay exact). Loads are the inline-asm
-// direct-to-LDS loads of the bf16 kernel; the row scales of the whole split
-// are loaded into LDS by the prologue.
+// same number and the vmcnt waits stay exact). Loads are the direct-to-LDS
+// loads of the bf16 kernel (resources rebased per tile, zeros past the
+// split's end, per-piece lane offsets kept in registers); the row scales of
+// the whole split are loaded into LDS by the prologue.
 template <int NW>
 struct Fp8Load {
   static constexpr int LAT = 16 / NW;
   static constexpr int ROPE = (2 + NW - 1) / NW;
   static constexpr int PIECES = LAT + ROPE;
-  TileRsrc rs;
-  __amdgpu_buffer_rsrc_t none;
-  char* stage;
-  char* dummy;
-  int lsb, rsb, last_row, w, l;
+  TileRsrc rs;                // rope: an empty resource on waves that only issue dummy loads
+  uint32_t m_lat, m_rope;
+  const int* voff;
 
-  __device__ __forceinline__ void piece(int i) const {
-    if (i < LAT) {
-      const int pair = __builtin_amdgcn_readfirstlane(w * LAT + i);   // rows 2 pair, 2 pair + 1
-      const int row = 2 * pair + (l >> 5);
-      dma16(rs.lat, lds_u32(stage + pair * 2 * D_C), min(row, last_row) * lsb + 16 * (l & 31), 0);
-    } else {
-      const int pc = __builtin_amdgcn_readfirstlane(w * ROPE + (i - LAT));  // 0, 1 real, >= 2 empty
-      const bool real = pc < 2;
-      const int row = 16 * min(pc, 1) + (l >> 2);
-      dma16(real ? rs.rope : none,
-            lds_u32(real ? stage + STG_ROPE + min(pc, 1) * 16 * D_R : dummy),
-            real ? min(row, last_row) * rsb + 16 * (l & 3) : 0, 0);
-    }
+  template <int I>
+  __device__ __forceinline__ void piece() const {
+    if constexpr (I < LAT) dma16_m0<I * 2 * D_C>(rs.lat, m_lat, voff[I]);
+    else dma16_m0<(I - LAT) * 16 * D_R>(rs.rope, m_rope, voff[I]);
   }
-  __device__ __forceinline__ void all() const {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) piece(i);
+  template <int... I>
+  __device__ __forceinline__ void all_(std::integer_sequence<int, I...>) const {
+    (piece<I>(), ...);
+  }
+  __device__ __forceinline__ void all() const { all_(std::make_integer_sequence<int, PIECES>{}); }
+  template <int... I>
+  __device__ __forceinline__ void step_(int t, std::integer_sequence<int, I...>) const {
+    ((t == 2 + (64 * I) / PIECES ? piece<I>() : void()), ...);
   }
   // after MFMA t (0..67) of the tile being computed
   __device__ __forceinline__ void step(int t) const {
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i)
-      if (t == 2 + (64 * i) / PIECES) piece(i);
+    step_(t, std::make_integer_sequence<int, PIECES>{});
   }
 };
 
 template <int NW>
+__device__ __forceinline__ void fp8_piece_offsets(const DecodeParams& p, int w, int l,
+                                                  int (&voff)[Fp8Load<NW>::PIECES]) {
+  constexpr int LAT = Fp8Load<NW>::LAT, ROPE = Fp8Load<NW>::ROPE;
+  const int lsb = (int)p.latent_stride, rsb = (int)p.rope_stride;
+#pragma unroll
+  for (int i = 0; i < LAT; ++i) voff[i] = (2 * (w * LAT + i) + (l >> 5)) * lsb + 16 * (l & 31);
+#pragma unroll
+  for (int i = 0; i < ROPE; ++i) {
+    const int pc = min(w * ROPE + i, 1);
+    voff[LAT + i] = (16 * pc + (l >> 2)) * rsb + 16 * (l & 3);
+  }
+}
+
+template <int NW>
 __device__ __forceinline__ Fp8Load<NW> fp8_load(const DecodeParams& p, char* stage, char* dummy,
-                                                int64_t base_row, int last_row, int w, int l,
-                                                bool valid) {
+                                                int row0, int nvalid, int w, const int* voff) {
   Fp8Load<NW> t;
-  t.rs = tile_rsrc(p, base_row, 1, valid);
-  t.none = make_rsrc(p.latent, 0);
-  t.stage = stage;
-  t.dummy = dummy;
-  t.lsb = (int)p.latent_stride;
-  t.rsb = (int)p.rope_stride;
-  t.last_row = last_row;
-  t.w = w;
-  t.l = l;
+  t.rs = tile_rsrc(p, row0, nvalid, 1);
+  const bool real = w * Fp8Load<NW>::ROPE < 2;   // wave-uniform
+  if (!real) t.rs.rope = make_rsrc(p.rope, 0);
+  t.m_lat = __builtin_amdgcn_readfirstlane(lds_u32(stage) + w * Fp8Load<NW>::LAT * 2 * D_C);
+  t.m_rope = __builtin_amdgcn_readfirstlane(
+      real ? lds_u32(stage) + STG_ROPE + w * Fp8Load<NW>::ROPE * 16 * D_R : lds_u32(dummy));
+  t.voff = voff;
   return t;
 }
 
@@ -685,13 +769,15 @@ __device__ __forceinline__ void reset_state(WaveState& st, float m_ref) {
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_bf16_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char buf0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char buf1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char buf2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char bufs[3 * TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
   __shared__ int overflow;
+  constexpr int NT = 64 * NW;
   constexpr int DMA_PER_TILE = TileLoad<NW>::PIECES;  // wave-wide loads per tile per wave
+  char* const buf0 = bufs;
+  char* const buf1 = bufs + TILE_BYTES;
+  char* const buf2 = bufs + 2 * TILE_BYTES;
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -702,28 +788,33 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     return;
   }
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
-  // loads of tile k into `tile`; tiles past the split are issued as empty loads
-  auto load_at = [&](char* tile, int k, int64_t base_row) {
-    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    return tile_load<NW>(p, tile, base_row, wi.t1 - 1 - tt0, w, l, k < ntiles);
-  };
+  int voff[DMA_PER_TILE];
+  tile_piece_offsets<NW>(p, w, l, voff);
+  // valid rows of tile k (0 past the split: its loads read nothing)
+  auto nvalid = [&](int k) { return min(max(wi.t1 - (wi.t0 + k * TILE), 0), TILE); };
   int trow = 0;   // lane i: physical row of tile i's first token (set in the prologue)
   auto load = [&](char* tile, int k) {
-    return load_at(tile, k, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)));
+    return tile_load<NW>(p, tile, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)), nvalid(k),
+                         w, voff);
   };
-  auto dma = [&](char* tile, int k) { load(tile, k).all(); };
   const auto no_issue = [](int) {};
 
-  // Prologue, in order of latency: tiles 0 and 1 (their block entries read
-  // on the scalar path), the queries, the rest of the split's block table;
-  // then one wait for all of it. The compiler does not count the tile loads,
-  // so a wait it placed for the query loads inside the loop would drain
-  // every tile load in flight.
-  load_at(buf0, 0, tile_base_row_direct(p, wi.b, wi.t0)).all();
-  load_at(buf1, 1, tile_base_row_direct(p, wi.b, wi.t0 + min(1, ntiles - 1) * TILE)).all();
+  // Prologue, in order of latency: zero the tile buffers, tiles 0 and 1
+  // (their block entries read on the scalar path), the queries, the rest of
+  // the split's block table; then one wait for all of it. The compiler does
+  // not count the tile loads, so a wait it placed for the query loads inside
+  // the loop would drain every tile load in flight.
+  zero_lds<NT>(bufs, 3 * TILE_BYTES, tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  tile_load<NW>(p, buf0, (int)tile_base_row_direct(p, wi.b, wi.t0), nvalid(0), w, voff).all();
+  tile_load<NW>(p, buf1, (int)tile_base_row_direct(p, wi.b, wi.t0 + min(1, ntiles - 1) * TILE),
+                nvalid(1), w, voff)
+      .all();
   bf16x8 qreg[QREG], qtmp[QLDS];
   load_q(p, wi, l, qreg, qtmp);
-  load_block_table<64 * NW>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
+  load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
   char* qpe = qpe_all + w * 4096;
   store_qpe(qtmp, qpe, l);
   const LaneAddr la = lane_addr(l);
@@ -737,8 +828,8 @@ void mla_decode_bf16_kernel(DecodeParams p) {
 
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (attempt > 0) {
-      dma(buf0, 0);
-      dma(buf1, 1);
+      load(buf0, 0).all();
+      load(buf1, 1).all();
       wait_vm_lgkm0<DMA_PER_TILE>();   // tile 0 landed (tile 1 may be in flight)
       __builtin_amdgcn_s_barrier();
       compiler_fence();
@@ -749,48 +840,59 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     // k+1, barrier. Phases past the last tile only issue their (empty) loads,
     // so every phase issues the same number and the vmcnt waits stay exact;
     // they are predicated rather than exited early so the accumulators keep
-    // one register assignment.
-    auto phase = [&](char* X, char* Z, int k) {
-      const TileLoad<NW> next = load(Z, k + 2);
-      if (k < ntiles) {
-        if (tile_compute<CACHE_BF16>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l, la,
-                                     h, st, [&](int j) { next.step(j); }) &&
-            l == 0)
-          overflow = 1;
-      } else {
-        next.all();
-      }
+    // one register assignment. Tile 0 (which sets the exponent reference)
+    // is peeled off the loop.
+    auto phase_end = [&]() {
       wait_vm_lgkm0<DMA_PER_TILE>();  // tile k+1 landed, tile k+2 may be in flight
       __builtin_amdgcn_s_barrier();
       compiler_fence();               // no LDS read of tile k+1 moves above this
     };
-    for (int k = 0; k < ntiles; k += 3) {
-      phase(buf0, buf2, k);
-      phase(buf1, buf0, k + 1);
-      phase(buf2, buf1, k + 2);
+    {
+      const TileLoad<NW> next = load(buf2, 2);
+      tile_compute<CACHE_BF16, true>(buf0, nullptr, wi.t0, wi.t1, qreg, qpe + 16 * l, la, h, st,
+                                     [&](int j) { next.step(j); });
+      phase_end();
     }
-    if (overflow == 0) break;
-
-    // Rare path: some score exceeded its head's reference by more than
-    // 2^64. Drain the loads in flight, find each head's true maximum over the
-    // split (scores only), then recompute the split against it.
+    auto phase = [&](char* X, char* Z, int k) {
+      const TileLoad<NW> next = load(Z, k + 2);
+      if (k < ntiles) {
+        tile_compute<CACHE_BF16, false>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l,
+                                        la, h, st, [&](int j) { next.step(j); });
+      } else {
+        next.all();
+      }
+      phase_end();
+    };
+    for (int k = 1; k < ntiles; k += 3) {
+      phase(buf1, buf0, k);
+      phase(buf2, buf1, k + 1);
+      phase(buf0, buf2, k + 2);
+    }
+    if (split_overflowed(st) && l == 0) overflow = 1;
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
+    if (overflow == 0) break;
+
+    // Rare path: a weight reached 2^64 against the first tile's max (or the
+    // sum is NaN). Drain the loads in flight, find each head's true maximum
+    // over the split (scores only), then recompute the split against it.
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
-      dma(buf0, k);
+      load(buf0, k).all();
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
       float sv[16];
-      mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16>(buf0, nullptr, wi.t0 + k * TILE, wi.t1, qreg,
-                                                   qpe + 16 * l, la, h, sv, no_issue));
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16, true>(buf0, nullptr, wi.t0 + k * TILE, wi.t1,
+                                                         qreg, qpe + 16 * l, la, h, sv, no_issue));
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
     reset_state(st, mtrue);
     if (tid == 0) overflow = 0;
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
   }
   // loads of tiles past the end may still be landing in any buffer, and other
   // waves may still read the last tile: drain both before reusing the LDS
@@ -816,7 +918,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char dummy[1024];
   __shared__ float scl_all[64 * TILE];   // row scales of the split, tile i at 32 i
   __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
-  __shared__ int flags[4];
+  __shared__ int overflow;
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -827,19 +929,28 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     return;
   }
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
-  auto load_at = [&](int k, int64_t base_row) {
-    const int tt0 = wi.t0 + min(k, ntiles - 1) * TILE;
-    return fp8_load<NW>(p, stage[k % 3], dummy, base_row, wi.t1 - 1 - tt0, w, l, k < ntiles);
-  };
+  int voff[P];
+  fp8_piece_offsets<NW>(p, w, l, voff);
+  auto nvalid = [&](int k) { return min(max(wi.t1 - (wi.t0 + k * TILE), 0), TILE); };
   int trow = 0;   // lane i: physical row of tile i's first token (set in the prologue)
-  auto load = [&](int k) { return load_at(k, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1))); };
+  auto load = [&](int k) {
+    return fp8_load<NW>(p, stage[k % 3], dummy,
+                        __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)), nvalid(k), w, voff);
+  };
 
-  // Prologue: raw tiles 0..2 (block entries on the scalar path), the queries,
-  // the split's block table; one wait; then the per-tile rows and the scales
-  // of the whole split; widen tile 0.
+  // Prologue: zero the staging buffers; raw tiles 0..2 (block entries on the
+  // scalar path), the queries, the split's block table; one wait; then the
+  // per-tile rows and the scales of the whole split; widen tile 0.
+  zero_lds<NT>(&stage[0][0], 3 * STG_BYTES, tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 #pragma unroll
   for (int k = 0; k < 3; ++k)
-    load_at(k, tile_base_row_direct(p, wi.b, wi.t0 + min(k, ntiles - 1) * TILE)).all();
+    fp8_load<NW>(p, stage[k], dummy,
+                 (int)tile_base_row_direct(p, wi.b, wi.t0 + min(k, ntiles - 1) * TILE), nvalid(k),
+                 w, voff)
+        .all();
   bf16x8 qreg[QREG], qtmp[QLDS];
   load_q(p, wi, l, qreg, qtmp);
   load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
@@ -848,6 +959,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
+  if (tid == 0) overflow = 0;
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
@@ -879,30 +991,30 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     // phase k: widen raw tile k+1 into the other bf16 buffer (landed and
     // published by the previous barrier), compute tile k while loading raw
     // tile k+3 into the stage tile k came from, wait for raw tile k+2,
-    // barrier
-    bool ovf = false;
-    for (int k = 0; k < ntiles; ++k) {
+    // barrier. Tile 0 (which sets the exponent reference) is peeled off.
+    {
+      fp8_tile_widen<NT>(stage[1], tbuf[1], tid);
+      const Fp8Load<NW> next = load(3);
+      tile_compute<CACHE_FP8, true>(tbuf[0], scl_all, wi.t0, wi.t1, qreg, qpe + 16 * l, la, h, st,
+                                    [&](int j) { next.step(j); });
+      wait_vm_lgkm0<P>();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+    }
+    for (int k = 1; k < ntiles; ++k) {
       fp8_tile_widen<NT>(stage[(k + 1) % 3], tbuf[(k + 1) & 1], tid);
       const Fp8Load<NW> next = load(k + 3);
-      ovf |= tile_compute<CACHE_FP8>(tbuf[k & 1], scl_all + TILE * k, wi.t0 + k * TILE, wi.t1, qreg,
-                                     qpe + 16 * l, la, h, st, [&](int j) { next.step(j); });
+      tile_compute<CACHE_FP8, false>(tbuf[k & 1], scl_all + TILE * k, wi.t0 + k * TILE, wi.t1,
+                                     qreg, qpe + 16 * l, la, h, st, [&](int j) { next.step(j); });
       wait_vm_lgkm0<P>();   // raw tile k+2 landed, k+3 may be in flight
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
-    wait_vm_lgkm0<0>();
-    if (l == 0) flags[w] = ovf ? 1 : 0;
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    int any_ovf = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) any_ovf |= flags[i];
-    any_ovf = __builtin_amdgcn_readfirstlane(any_ovf);
+    if (split_overflowed(st) && l == 0) overflow = 1;
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    if (any_ovf == 0) break;
+    if (overflow == 0) break;
     // rare path (see the bf16 kernel): true maximum, then recompute
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
@@ -915,13 +1027,20 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
       float sv[16];
-      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8>(tbuf[0], scl_all + TILE * k, wi.t0 + k * TILE,
-                                                   wi.t1, qreg, qpe + 16 * l, la, h, sv, [](int) {}));
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8, true>(tbuf[0], scl_all + TILE * k,
+                                                        wi.t0 + k * TILE, wi.t1, qreg,
+                                                        qpe + 16 * l, la, h, sv, [](int) {}));
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
     reset_state(st, mtrue);
+    if (tid == 0) overflow = 0;
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
   }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
   write_partial(wi, st, h, l, tbuf[w >> 1] + (w & 1) * PART_SCR_BYTES);
 }
 
