@@ -70,11 +70,11 @@ constexpr int ROPE_ROW = D_R * 2;           // 128 B: bf16 RoPE-key row in LDS
 constexpr int ROPE_OFF = TILE * LAT_ROW;    // RoPE rows follow the 32 latent rows
 constexpr int TILE_BYTES = ROPE_OFF + TILE * ROPE_ROW;  // 36864
 
-// The absorbed query of a lane's head is the QK^T B operand: its 32 latent
-// k-steps stay in registers (128 VGPRs), its 4 RoPE k-steps are read from
-// LDS (4 KB per wave), which leaves the register file room for the rest.
-constexpr int QREG = D_C / 16;           // k-steps of Q held in registers
-constexpr int QLDS = D_QK / 16 - QREG;   // k-steps of Q read from LDS (the RoPE part)
+// The absorbed query of a lane's head is the QK^T B operand: all 36 k-steps
+// stay in registers (144 VGPRs: 32 latent k-steps in qreg, the 4 RoPE
+// k-steps in qpe), so the only LDS reads of the loop are the tile's.
+constexpr int QREG = D_C / 16;           // latent k-steps of Q
+constexpr int QLDS = D_QK / 16 - QREG;   // RoPE k-steps of Q
 
 // LDS swizzles (gfx950 LDS: 64 banks of 4 bytes, 256 bytes per cycle).
 // Latent rows are 1 KB (64 chunks of 16 bytes); chunk c of row r is stored at
@@ -190,22 +190,19 @@ __device__ __forceinline__ void mfma_vgpr_settle(f32x16& acc) {
 template <int CK, bool FIRST, typename Issue>
 __device__ __forceinline__ float tile_scores(const char* tile, const float* scale, int tile_t0,
                                              int t1, const bf16x8 (&qreg)[QREG],
-                                             const char* qpe, const LaneAddr& la, int h,
+                                             const bf16x8 (&qpe)[QLDS], const LaneAddr& la, int h,
                                              float (&sv)[16], const Issue& issue) {
   constexpr int NJ = D_QK / 16;   // 36 k-steps
   constexpr int AHEAD = 3;
   auto a_off = [&](int j) { return (j < 32) ? la.qb[j & 7] + 256 * (j >> 3) : la.rb[j - 32]; };
   bf16x8 ring[AHEAD + 1];
-  bf16x8 qring[QLDS];
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j) ring[j] = *(const bf16x8*)(tile + a_off(j));
   f32x16 sacc;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     if (j + AHEAD < NJ) ring[(j + AHEAD) % (AHEAD + 1)] = *(const bf16x8*)(tile + a_off(j + AHEAD));
-    if (j + AHEAD >= QREG && j + AHEAD < NJ)
-      qring[j + AHEAD - QREG] = *(const bf16x8*)(qpe + (j + AHEAD - QREG) * 1024);
-    const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : qring[j < QREG ? 0 : j - QREG];
+    const bf16x8 bq = (j < QREG) ? qreg[j < QREG ? j : 0] : qpe[j < QREG ? 0 : j - QREG];
     if (j == 0) mfma_vgpr_first(sacc, ring[0], bq);
     else mfma_vgpr_acc(sacc, ring[j % (AHEAD + 1)], bq);
     issue(j);
@@ -245,8 +242,9 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
 // of the weights (see split_overflowed).
 template <int CK, bool FIRST, typename Issue>
 __device__ __forceinline__ void tile_compute(const char* tile, const float* scale, int tile_t0,
-                                             int t1, const bf16x8 (&qreg)[QREG], const char* qpe,
-                                             const LaneAddr& la, int h, WaveState& st,
+                                             int t1, const bf16x8 (&qreg)[QREG],
+                                             const bf16x8 (&qpe)[QLDS], const LaneAddr& la, int h,
+                                             WaveState& st,
                                              const Issue& issue) {
   float sv[16];
   const float tmax = tile_scores<CK, FIRST>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv, issue);
@@ -316,6 +314,161 @@ __device__ __forceinline__ bool split_overflowed(const WaveState& st) {
   return __any(!(st.lsum < 0x1p64f));
 }
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_(const F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(const F& f) {
+  static_for_(f, std::make_integer_sequence<int, N>{});
+}
+
+// Slot schedule of a pipelined step with nq S^T MFMAs and np PV MFMAs
+// (both nonzero): two PV slots first (their operands were read before the
+// step's barrier; the step's own K operands are still in flight), then the
+// S^T chain spread evenly over the slots up to the last `tail` ones, which
+// are PV (they cover the softmax work after the chain's end).
+constexpr int SLOT_HEAD = 2, SLOT_TAIL = 6;
+constexpr bool slot_is_q(int t, int nq, int np) {
+  if (!nq) return false;
+  if (!np) return true;
+  const int span = nq + np - SLOT_HEAD - SLOT_TAIL;   // slots holding all S^T MFMAs
+  if (t < SLOT_HEAD || t >= SLOT_HEAD + span) return false;
+  const int u = t - SLOT_HEAD;
+  return ((u + 1) * nq) / span != (u * nq) / span;   // nq of the span's slots, evenly
+}
+constexpr int slot_q_index(int t, int nq, int np) {
+  int c = 0;
+  for (int i = 0; i < t; ++i) c += slot_is_q(i, nq, np) ? 1 : 0;
+  return c;
+}
+
+// Cross-tile software pipeline (bf16 kernel). Step j runs, in one stream of
+// MFMA slots,
+//   * O^T += C^T P^T of tile j-1 (32 MFMAs into 16 independent
+//     accumulators), with the weights of its last 16 tokens formed between
+//     the first of them (those of its first 16 came from step j-1);
+//   * S^T of tile j into sn (36 MFMAs, one dependent chain), and after it
+//     the first half of tile j's softmax (masked past the split's end on its
+//     last tile; on the split's first tile its max becomes the exponent
+//     reference) into pb[0], and the first PV operands of tile j into pring,
+//     all before the step's barrier.
+// The next step thus starts with PV MFMAs whose operands are in registers
+// while its K operands are read, and the matrix pipe stays fed through the
+// softmax and across step boundaries. The first step only computes S^T,
+// the last only PV. `issue(t, n)` runs after slot t of the step's n.
+template <bool DO_QK, bool DO_PV, bool K_FIRST, typename Issue>
+__device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_t0, int t1,
+                                          const bf16x8 (&qreg)[QREG], const char* qpe,
+                                          const LaneAddr& la, int h, WaveState& st,
+                                          f32x16& sn, f32x16& sp, bf16x8 (&pb)[2],
+                                          bf16x8 (&pring)[3], const Issue& issue) {
+  constexpr int NQ = DO_QK ? D_QK / 16 : 0, NP = DO_PV ? 32 : 0, NSLOT = NQ + NP;
+  constexpr int QA = 2, PA = 2;   // LDS read lookahead, in MFMAs of each chain
+  auto a_off = [&](int j) { return (j < 32) ? la.qb[j & 7] + 256 * (j >> 3) : la.rb[j - 32]; };
+  auto v_op = [&](const char* tile, int s) {
+    const int ks = s >> 4, dt = s & 15;
+    const int off = 256 * (dt >> 2) + ks * 16 * LAT_ROW;
+    return lds_tr8(tile + la.tb[0][dt & 3] + off, tile + la.tb[1][dt & 3] + off);
+  };
+  // qring: K operands; rring: the RoPE k-steps' query operands (from LDS,
+  // `qpe` is this lane's slot, k-step i at +1 KB i)
+  bf16x8 qring[QA + 1], rring[QA + 1];
+  if (DO_QK) {
+#pragma unroll
+    for (int j = 0; j < QA; ++j) qring[j] = *(const bf16x8*)(kt + a_off(j));
+  }
+  const float mref_pv = st.m_ref;
+  auto half_sum = [&](f32x16& v, int r0) {
+    float half = ((v[r0] + v[r0 + 1]) + (v[r0 + 2] + v[r0 + 3])) +
+                 ((v[r0 + 4] + v[r0 + 5]) + (v[r0 + 6] + v[r0 + 7]));
+    asm volatile("" : "+v"(half));
+    st.lsum += half;
+  };
+  auto pack = [&](const f32x16& v, int r) {   // rows r, r+1 into the B operand
+    pb[r >> 3][r & 7] = (bf16)v[r];
+    pb[r >> 3][(r & 7) + 1] = (bf16)v[r + 1];
+  };
+  // after the S^T chain (sn settled): mask, reference, first-half weights
+  float mref_k = 0.f;
+  auto softmax_head = [&]() {
+    if (k_t0 + TILE > t1) {   // wave-uniform: the split's last tile only
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k_t0 + 8 * (r >> 2) + 4 * h + (r & 3) >= t1) sn[r] = -INFINITY;
+    }
+    if (K_FIRST) {
+      float m4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m4[i] = fmaxf(fmaxf(sn[4 * i], sn[4 * i + 1]), fmaxf(sn[4 * i + 2], sn[4 * i + 3]));
+      const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
+    }
+    mref_k = st.m_ref;
+  };
+  // S^T-only step: everything after the chain
+  constexpr int HEAD_AT = DO_PV ? SLOT_HEAD + (NQ + NP - SLOT_HEAD - SLOT_TAIL) : NQ;
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<NSLOT>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    constexpr bool is_q = slot_is_q(t, NQ, NP);
+    constexpr int qi = slot_q_index(t, NQ, NP);
+    constexpr int pi = t - qi;
+    if constexpr (is_q) {
+      if constexpr (qi == 0) {
+        mfma_vgpr_first(sn, qring[0], qreg[0]);
+      } else if constexpr (qi < QREG) {
+        mfma_vgpr_acc(sn, qring[qi % (QA + 1)], qreg[qi]);
+      } else {
+        mfma_vgpr_acc(sn, qring[qi % (QA + 1)], rring[qi % (QA + 1)]);
+      }
+      if constexpr (qi + QA < NQ) qring[(qi + QA) % (QA + 1)] = *(const bf16x8*)(kt + a_off(qi + QA));
+      if constexpr (qi + QA >= QREG && qi + QA < NQ)
+        rring[(qi + QA) % (QA + 1)] = *(const bf16x8*)(qpe + 1024 * (qi + QA - QREG));
+      if constexpr (qi == NQ - 1) mfma_vgpr_settle(sn);
+    } else {
+      constexpr int dt = pi & 15;
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pring[pi % (PA + 1)], pb[pi >> 4], st.o[dt], 0, 0, 0);
+      if constexpr (pi + PA < NP) pring[(pi + PA) % (PA + 1)] = v_op(vt, pi + PA);
+      // second half of tile j-1's weights
+      if constexpr (pi < 8) sp[8 + pi] = fast_exp2(sp[8 + pi] - mref_pv);
+      if constexpr (pi == 8) half_sum(sp, 8);
+      if constexpr (pi >= 9 && pi < 13) pack(sp, 8 + 2 * (pi - 9));
+    }
+    // tile j's softmax head over the tail slots, and its first PV operands
+    // once the last two PV MFMAs have read the ring entries they replace
+    if constexpr (DO_QK && DO_PV) {
+      constexpr int u = t - (HEAD_AT - 1);   // 0 at the chain's last slot
+      if constexpr (u == 0) softmax_head();
+      if constexpr (u >= 0 && u < 4) {
+        sn[2 * u] = fast_exp2(sn[2 * u] - mref_k);
+        sn[2 * u + 1] = fast_exp2(sn[2 * u + 1] - mref_k);
+      }
+      if constexpr (u == 3) {
+        half_sum(sn, 0);
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) pack(sn, r);
+      }
+      if constexpr (t == NSLOT - 2) pring[0] = v_op(kt, 0);
+      if constexpr (t == NSLOT - 1) pring[1] = v_op(kt, 1);
+    }
+    issue(t, NSLOT);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  if constexpr (DO_QK && !DO_PV) {   // S^T-only step: the head after the chain
+    softmax_head();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sn[r] = fast_exp2(sn[r] - mref_k);
+    half_sum(sn, 0);
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) pack(sn, r);
+    pring[0] = v_op(kt, 0);
+    pring[1] = v_op(kt, 1);
+  }
+}
+
 // Map a flat workgroup id to (sequence*split index q, head group g).
 // Workgroups are dispatched round-robin over the 8 XCDs (x mod 8), each with
 // its own L2; every XCD gets a contiguous range of q, so the head groups and
@@ -354,6 +507,27 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
   int v;
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
   return v;
+}
+
+// Physical rows of the first tokens of two tiles, reading their block
+// entries from global memory with one wait (before the split's table is in
+// LDS).
+__device__ __forceinline__ void tile_base_rows_direct2(const DecodeParams& p, int b, int ta, int tb,
+                                                      int& ra, int& rb) {
+  if (p.block_table) {
+    const int ia = __builtin_amdgcn_readfirstlane(b * p.max_blocks + ta / p.block_size);
+    const int ib = __builtin_amdgcn_readfirstlane(b * p.max_blocks + tb / p.block_size);
+    int va, vb;
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(va), "=&s"(vb)
+                 : "s"(p.block_table + ia), "s"(p.block_table + ib)
+                 : "memory");
+    ra = va * p.block_size + (ta % p.block_size);
+    rb = vb * p.block_size + (tb % p.block_size);
+  } else {
+    ra = (int)((int64_t)b * p.seq_capacity + ta);
+    rb = (int)((int64_t)b * p.seq_capacity + tb);
+  }
 }
 
 // Physical row of the first token of a tile, reading the block entry from
@@ -449,6 +623,21 @@ __device__ __forceinline__ void dma16_m0(__amdgpu_buffer_rsrc_t rsrc, uint32_t m
       : "memory", "scc");
 }
 
+// One wave-wide direct-to-LDS load of 4 bytes per lane (to m0_base + IMM +
+// 4 * lane), used to pull cache lines into L2 ahead of their tile loads: the
+// LDS bytes it writes are never read.
+template <int IMM>
+__device__ __forceinline__ void dma4_m0(__amdgpu_buffer_rsrc_t rsrc, uint32_t m0_base, int voffset,
+                                        int soffset) {
+  asm volatile(
+      "s_add_u32 m0, %0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(m0_base), "v"(voffset), "s"(rsrc), "s"(soffset), "n"(IMM)
+      : "memory", "scc");
+}
+
 // Compiler-only fence: no memory access moves across it (emits nothing).
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -494,6 +683,18 @@ struct TileLoad {
   __device__ __forceinline__ void step(int t) const {
     step_(t, std::make_integer_sequence<int, PIECES>{});
   }
+  // after slot t of a pipelined step of n slots: piece i at
+  // t = 1 + i * span / PIECES, span = min(n - 2, 2 PIECES) (every other slot
+  // from the step's start while there is room), so the tile has most of two
+  // steps to land; every piece goes out for any n >= 3
+  template <int... I>
+  __device__ __forceinline__ void step_n_(int t, int n, std::integer_sequence<int, I...>) const {
+    const int span = min(n - 2, 2 * PIECES);
+    ((t == 1 + (I * span) / PIECES ? piece<I>() : void()), ...);
+  }
+  __device__ __forceinline__ void step_n(int t, int n) const {
+    step_n_(t, n, std::make_integer_sequence<int, PIECES>{});
+  }
 };
 
 template <int NW>
@@ -524,6 +725,37 @@ __device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* t
                                             w * TileLoad<NW>::GPW * 8 * ROPE_ROW);
   t.voff = voff;
   return t;
+}
+
+// L2 prefetch of a tile two steps before its loads are issued: each wave
+// touches one dword of every 128-byte line of its quarter of the tile (8
+// latent rows, 8 RoPE-key rows), through resources over the whole cache
+// arrays (every offset is range-checked against them, so a prefetch past
+// the arrays, or past 2^31 bytes, reads nothing). The 2 x 256 bytes per wave
+// land in an LDS area that is dead for the step (see the kernel).
+struct TilePrefetch {
+  __amdgpu_buffer_rsrc_t lat, rope;
+  int voff_lat, voff_rope, lsb, rsb;
+  __device__ __forceinline__ void issue_lat(int row0, uint32_t m0_base) const {
+    dma4_m0<0>(lat, m0_base, (int)((uint32_t)row0 * (uint32_t)lsb + (uint32_t)voff_lat), 0);
+  }
+  __device__ __forceinline__ void issue_rope(int row0, uint32_t m0_base) const {
+    dma4_m0<256>(rope, m0_base, (int)((uint32_t)row0 * (uint32_t)rsb + (uint32_t)voff_rope), 0);
+  }
+};
+
+template <int NW>
+__device__ __forceinline__ TilePrefetch tile_prefetch(const DecodeParams& p, int w, int l) {
+  static_assert(NW == 4, "prefetch layout assumes four waves");
+  TilePrefetch f;
+  f.lsb = (int)p.latent_stride * 2;
+  f.rsb = (int)p.rope_stride * 2;
+  const int64_t lat_bytes = p.rows * f.lsb, rope_bytes = p.rows * f.rsb;
+  f.lat = make_rsrc(p.latent, lat_bytes);
+  f.rope = make_rsrc(p.rope, rope_bytes);
+  f.voff_lat = (8 * w + (l >> 3)) * f.lsb + 128 * (l & 7);
+  f.voff_rope = (8 * w + (l & 7)) * f.rsb;
+  return f;
 }
 
 // Zero a workgroup's LDS tile buffers (before their first loads): lanes past
@@ -740,20 +972,14 @@ __device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveStat
 }
 
 // Queries of this wave's 32 heads (operand layout, see qop_index): the 32
-// latent k-steps into registers, the 4 RoPE k-steps into `qtmp` (written to
-// this wave's 4 KB of LDS, [k-step][lane][16 bytes], once they landed).
+// latent k-steps into qreg, the 4 RoPE k-steps into qpe.
 __device__ __forceinline__ void load_q(const DecodeParams& p, const WorkItem& wi, int l,
-                                       bf16x8 (&qreg)[QREG], bf16x8 (&qtmp)[QLDS]) {
+                                       bf16x8 (&qreg)[QREG], bf16x8 (&qpe)[QLDS]) {
   const bf16* qp = p.q + qop_index(wi.b, wi.head - (l & 31), 0, p.H) + 8 * l;
 #pragma unroll
   for (int j = 0; j < QREG; ++j) qreg[j] = *(const bf16x8*)(qp + 512 * j);
 #pragma unroll
-  for (int j = 0; j < QLDS; ++j) qtmp[j] = *(const bf16x8*)(qp + 512 * (QREG + j));
-}
-
-__device__ __forceinline__ void store_qpe(const bf16x8 (&qtmp)[QLDS], char* qpe, int l) {
-#pragma unroll
-  for (int j = 0; j < QLDS; ++j) *(bf16x8*)(qpe + j * 1024 + 16 * l) = qtmp[j];
+  for (int j = 0; j < QLDS; ++j) qpe[j] = *(const bf16x8*)(qp + 512 * (QREG + j));
 }
 
 __device__ __forceinline__ void reset_state(WaveState& st, float m_ref) {
@@ -769,15 +995,20 @@ __device__ __forceinline__ void reset_state(WaveState& st, float m_ref) {
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_bf16_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char bufs[3 * TILE_BYTES];
+  // four tile buffers and the RoPE k-steps of the queries (160 KB with four
+  // waves); the split's block table and the waves' overflow flags borrow tile
+  // buffer space while it is idle (the prologue, the end of a pass)
+  __shared__ __attribute__((aligned(1024))) char bufs[4 * TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
-  __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
-  __shared__ int overflow;
   constexpr int NT = 64 * NW;
   constexpr int DMA_PER_TILE = TileLoad<NW>::PIECES;  // wave-wide loads per tile per wave
+  constexpr int PF_PER_TILE = 0;                        // prefetch loads per step per wave
   char* const buf0 = bufs;
   char* const buf1 = bufs + TILE_BYTES;
   char* const buf2 = bufs + 2 * TILE_BYTES;
+  char* const buf3 = bufs + 3 * TILE_BYTES;
+  int* const blk_tab = (int*)buf3;   // prologue only (tile 3 is loaded after it is read)
+  int* const flags = (int*)buf0;     // end of a pass only (no load in flight, no reader)
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -798,32 +1029,50 @@ void mla_decode_bf16_kernel(DecodeParams p) {
                          w, voff);
   };
   const auto no_issue = [](int) {};
+  // L2 prefetch (four waves): step j touches tile j+4 (its loads go out in
+  // step j+2); the bytes land in the RoPE-key rows of tile j-1's buffer,
+  // which no one reads during step j and which tile j+3's loads, issued
+  // later, overwrite (loads complete in order)
+  TilePrefetch pf;
+  if constexpr (PF_PER_TILE > 0) pf = tile_prefetch<NW>(p, w, l);
+  auto prefetch_slot = [&](int t, int j, char* dead) {
+    if constexpr (PF_PER_TILE > 0) {
+      if (t < 2) {
+        const int row = __builtin_amdgcn_readlane(trow, min(j + 4, ntiles - 1));
+        const uint32_t m = __builtin_amdgcn_readfirstlane(lds_u32(dead + ROPE_OFF) + w * 512);
+        if (t == 0) pf.issue_lat(row, m);
+        else pf.issue_rope(row, m);
+      }
+    }
+  };
 
-  // Prologue, in order of latency: zero the tile buffers, tiles 0 and 1
-  // (their block entries read on the scalar path), the queries, the rest of
-  // the split's block table; then one wait for all of it. The compiler does
-  // not count the tile loads, so a wait it placed for the query loads inside
-  // the loop would drain every tile load in flight.
-  zero_lds<NT>(bufs, 3 * TILE_BYTES, tid);
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-  tile_load<NW>(p, buf0, (int)tile_base_row_direct(p, wi.b, wi.t0), nvalid(0), w, voff).all();
-  tile_load<NW>(p, buf1, (int)tile_base_row_direct(p, wi.b, wi.t0 + min(1, ntiles - 1) * TILE),
-                nvalid(1), w, voff)
-      .all();
+  // Prologue: the queries (independent of everything else), the block
+  // entries of tiles 0 and 1 (scalar path, one wait), their loads, the rest
+  // of the split's block table; then one wait for all of it. The compiler
+  // does not count the tile loads, so a wait it placed for the query loads
+  // inside the loop would drain every tile load in flight. The tile buffers
+  // need no clearing: a tile's loads write all of its bytes (zeros past the
+  // split's end).
   bf16x8 qreg[QREG], qtmp[QLDS];
   load_q(p, wi, l, qreg, qtmp);
+  {
+    int r0, r1;
+    tile_base_rows_direct2(p, wi.b, wi.t0, wi.t0 + min(1, ntiles - 1) * TILE, r0, r1);
+    tile_load<NW>(p, buf0, r0, nvalid(0), w, voff).all();
+    tile_load<NW>(p, buf1, r1, nvalid(1), w, voff).all();
+  }
   load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
-  char* qpe = qpe_all + w * 4096;
-  store_qpe(qtmp, qpe, l);
+  char* const qpe = qpe_all + w * (QLDS * 1024) + 16 * l;   // this lane's RoPE query slot
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
-  if (tid == 0) overflow = 0;
   wait_vm_lgkm0<0>();
+#pragma unroll
+  for (int j = 0; j < QLDS; ++j) *(bf16x8*)(qpe + 1024 * j) = qtmp[j];
   __builtin_amdgcn_s_barrier();
   compiler_fence();
+  // (buffer 3 holds the table until tile 3's loads, issued after every wave
+  // has passed step 0's barrier)
   trow = tile_rows_lanes(p, wi.b, wi.t0, wi.t1, blk_tab, first_blk_of(p, wi.t0), l);
 
   for (int attempt = 0; attempt < 2; ++attempt) {
@@ -834,45 +1083,77 @@ void mla_decode_bf16_kernel(DecodeParams p) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
-
-    // phase on buffer X (tile k): compute X while refilling buffer Z with
-    // tile k+2 (its loads spread through the MFMA chain), wait for tile
-    // k+1, barrier. Phases past the last tile only issue their (empty) loads,
-    // so every phase issues the same number and the vmcnt waits stay exact;
-    // they are predicated rather than exited early so the accumulators keep
-    // one register assignment. Tile 0 (which sets the exponent reference)
-    // is peeled off the loop.
-    auto phase_end = [&]() {
-      wait_vm_lgkm0<DMA_PER_TILE>();  // tile k+1 landed, tile k+2 may be in flight
+    // Tile t lives in buffer t mod 4. Step j computes S^T of tile j and PV of
+    // tile j-1 (see pipe_step) while tile j+2 loads into the buffer of tile
+    // j-2, then waits for tile j+1 and meets the other waves at the barrier,
+    // after which tile j-1's buffer is free. Every real step issues the same
+    // number of loads (those of tiles past the split read nothing), so the
+    // vmcnt waits stay exact; steps past the last tile, which only come
+    // after every real one, do nothing (a load there could land in the last
+    // tile's buffer before the final step reads it).
+    f32x16 s0, s1;    // scores of even / odd tiles
+    bf16x8 pb[2];     // PV B operand (weights of the tile whose PV is next)
+    bf16x8 pring[3];  // PV A operands in flight
+    auto step_end = [&]() {
+      // tile j+1 landed; tile j+2 and the step's prefetches may be in flight
+      wait_vm_lgkm0<DMA_PER_TILE + PF_PER_TILE>();
       __builtin_amdgcn_s_barrier();
-      compiler_fence();               // no LDS read of tile k+1 moves above this
+      compiler_fence();               // no LDS read of tile j+1 moves above this
     };
+    // the next tile's loader is set up after the step's first MFMA (its
+    // scalar work hides behind it; the first load goes out after slot 1)
     {
-      const TileLoad<NW> next = load(buf2, 2);
-      tile_compute<CACHE_BF16, true>(buf0, nullptr, wi.t0, wi.t1, qreg, qpe + 16 * l, la, h, st,
-                                     [&](int j) { next.step(j); });
-      phase_end();
+      TileLoad<NW> next;
+      pipe_step<true, false, true>(buf0, nullptr, wi.t0, wi.t1, qreg, qpe, la, h, st, s0, s1, pb,
+                                   pring, [&](int t, int n) {
+                               if (t == 0) next = load(buf2, 2);
+                               prefetch_slot(t, 0, buf3);
+                               next.step_n(t, n);
+                             });
+      step_end();
     }
-    auto phase = [&](char* X, char* Z, int k) {
-      const TileLoad<NW> next = load(Z, k + 2);
-      if (k < ntiles) {
-        tile_compute<CACHE_BF16, false>(X, nullptr, wi.t0 + k * TILE, wi.t1, qreg, qpe + 16 * l,
-                                        la, h, st, [&](int j) { next.step(j); });
-      } else {
-        next.all();
+    auto step = [&](char* K, char* V, char* Z, int j, f32x16& sn, f32x16& sp) {
+      if (j < ntiles) {
+        TileLoad<NW> next;
+        pipe_step<true, true, false>(K, V, wi.t0 + j * TILE, wi.t1, qreg, qpe, la, h, st, sn, sp,
+                                     pb, pring, [&](int t, int n) {
+                                if (t == 0) next = load(Z, j + 2);
+                                prefetch_slot(t, j, V);
+                                next.step_n(t, n);
+                              });
+        step_end();
       }
-      phase_end();
     };
-    for (int k = 1; k < ntiles; k += 3) {
-      phase(buf1, buf0, k);
-      phase(buf2, buf1, k + 1);
-      phase(buf0, buf2, k + 2);
+    for (int j = 1; j < ntiles; j += 4) {
+      step(buf1, buf0, buf3, j, s1, s0);
+      step(buf2, buf1, buf0, j + 1, s0, s1);
+      step(buf3, buf2, buf1, j + 2, s1, s0);
+      step(buf0, buf3, buf2, j + 3, s0, s1);
     }
-    if (split_overflowed(st) && l == 0) overflow = 1;
+    {   // softmax and PV of the last tile
+      const int last = ntiles - 1;
+      f32x16 sl = (last & 1) ? s1 : s0;
+      pipe_step<false, true, false>(nullptr, bufs + (last & 3) * TILE_BYTES, 0, wi.t1, qreg, qpe,
+                                    la, h, st, sl, sl, pb, pring, [](int, int) {});
+    }
+    // every load has landed and every wave is past its last LDS read: the
+    // waves' overflow flags go through buffer 0
+    const bool ovf = split_overflowed(st);
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    if (overflow == 0) break;
+    if (l == 0) flags[w] = ovf ? 1 : 0;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    int any_ovf = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any_ovf |= flags[i];
+    any_ovf = __builtin_amdgcn_readfirstlane(any_ovf);
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (any_ovf == 0) break;
 
     // Rare path: a weight reached 2^64 against the first tile's max (or the
     // sum is NaN). Drain the loads in flight, find each head's true maximum
@@ -884,15 +1165,15 @@ void mla_decode_bf16_kernel(DecodeParams p) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
       float sv[16];
+      bf16x8 qp[QLDS];
+#pragma unroll
+      for (int j = 0; j < QLDS; ++j) qp[j] = *(const bf16x8*)(qpe + 1024 * j);
       mtrue = fmaxf(mtrue, tile_scores<CACHE_BF16, true>(buf0, nullptr, wi.t0 + k * TILE, wi.t1,
-                                                         qreg, qpe + 16 * l, la, h, sv, no_issue));
+                                                         qreg, qp, la, h, sv, no_issue));
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
     reset_state(st, mtrue);
-    if (tid == 0) overflow = 0;
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
   }
   // loads of tiles past the end may still be landing in any buffer, and other
   // waves may still read the last tile: drain both before reusing the LDS
@@ -914,7 +1195,6 @@ void mla_decode_fp8_kernel(DecodeParams p) {
   // raw fp8 tiles k+1 .. k+3 in three stages, bf16 tiles k, k+1 in two buffers
   __shared__ __attribute__((aligned(1024))) char stage[3][STG_BYTES];
   __shared__ __attribute__((aligned(1024))) char tbuf[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   __shared__ __attribute__((aligned(1024))) char dummy[1024];
   __shared__ float scl_all[64 * TILE];   // row scales of the split, tile i at 32 i
   __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
@@ -951,11 +1231,9 @@ void mla_decode_fp8_kernel(DecodeParams p) {
                  (int)tile_base_row_direct(p, wi.b, wi.t0 + min(k, ntiles - 1) * TILE), nvalid(k),
                  w, voff)
         .all();
-  bf16x8 qreg[QREG], qtmp[QLDS];
-  load_q(p, wi, l, qreg, qtmp);
+  bf16x8 qreg[QREG], qpe[QLDS];
+  load_q(p, wi, l, qreg, qpe);
   load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
-  char* qpe = qpe_all + w * 4096;
-  store_qpe(qtmp, qpe, l);
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
@@ -995,7 +1273,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     {
       fp8_tile_widen<NT>(stage[1], tbuf[1], tid);
       const Fp8Load<NW> next = load(3);
-      tile_compute<CACHE_FP8, true>(tbuf[0], scl_all, wi.t0, wi.t1, qreg, qpe + 16 * l, la, h, st,
+      tile_compute<CACHE_FP8, true>(tbuf[0], scl_all, wi.t0, wi.t1, qreg, qpe, la, h, st,
                                     [&](int j) { next.step(j); });
       wait_vm_lgkm0<P>();
       __builtin_amdgcn_s_barrier();
@@ -1005,7 +1283,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       fp8_tile_widen<NT>(stage[(k + 1) % 3], tbuf[(k + 1) & 1], tid);
       const Fp8Load<NW> next = load(k + 3);
       tile_compute<CACHE_FP8, false>(tbuf[k & 1], scl_all + TILE * k, wi.t0 + k * TILE, wi.t1,
-                                     qreg, qpe + 16 * l, la, h, st, [&](int j) { next.step(j); });
+                                     qreg, qpe, la, h, st, [&](int j) { next.step(j); });
       wait_vm_lgkm0<P>();   // raw tile k+2 landed, k+3 may be in flight
       __builtin_amdgcn_s_barrier();
       compiler_fence();
@@ -1029,7 +1307,7 @@ void mla_decode_fp8_kernel(DecodeParams p) {
       float sv[16];
       mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8, true>(tbuf[0], scl_all + TILE * k,
                                                         wi.t0 + k * TILE, wi.t1, qreg,
-                                                        qpe + 16 * l, la, h, sv, [](int) {}));
+                                                        qpe, la, h, sv, [](int) {}));
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
