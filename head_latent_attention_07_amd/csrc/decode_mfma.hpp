@@ -623,21 +623,6 @@ __device__ __forceinline__ void dma16_m0(__amdgpu_buffer_rsrc_t rsrc, uint32_t m
       : "memory", "scc");
 }
 
-// One wave-wide direct-to-LDS load of 4 bytes per lane (to m0_base + IMM +
-// 4 * lane), used to pull cache lines into L2 ahead of their tile loads: the
-// LDS bytes it writes are never read.
-template <int IMM>
-__device__ __forceinline__ void dma4_m0(__amdgpu_buffer_rsrc_t rsrc, uint32_t m0_base, int voffset,
-                                        int soffset) {
-  asm volatile(
-      "s_add_u32 m0, %0, %4\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %1, %2, %3 offen lds"
-      :
-      : "s"(m0_base), "v"(voffset), "s"(rsrc), "s"(soffset), "n"(IMM)
-      : "memory", "scc");
-}
-
 // Compiler-only fence: no memory access moves across it (emits nothing).
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -727,44 +712,6 @@ __device__ __forceinline__ TileLoad<NW> tile_load(const DecodeParams& p, char* t
   return t;
 }
 
-// L2 prefetch of a tile two steps before its loads are issued: each wave
-// touches one dword of every 128-byte line of its quarter of the tile (8
-// latent rows, 8 RoPE-key rows), through resources over the whole cache
-// arrays (every offset is range-checked against them, so a prefetch past
-// the arrays, or past 2^31 bytes, reads nothing). The 2 x 256 bytes per wave
-// land in an LDS area that is dead for the step (see the kernel).
-struct TilePrefetch {
-  __amdgpu_buffer_rsrc_t lat, rope;
-  int voff_lat, voff_rope, lsb, rsb;
-  __device__ __forceinline__ void issue_lat(int row0, uint32_t m0_base) const {
-    dma4_m0<0>(lat, m0_base, (int)((uint32_t)row0 * (uint32_t)lsb + (uint32_t)voff_lat), 0);
-  }
-  __device__ __forceinline__ void issue_rope(int row0, uint32_t m0_base) const {
-    dma4_m0<256>(rope, m0_base, (int)((uint32_t)row0 * (uint32_t)rsb + (uint32_t)voff_rope), 0);
-  }
-};
-
-template <int NW>
-__device__ __forceinline__ TilePrefetch tile_prefetch(const DecodeParams& p, int w, int l) {
-  static_assert(NW == 4, "prefetch layout assumes four waves");
-  TilePrefetch f;
-  f.lsb = (int)p.latent_stride * 2;
-  f.rsb = (int)p.rope_stride * 2;
-  const int64_t lat_bytes = p.rows * f.lsb, rope_bytes = p.rows * f.rsb;
-  f.lat = make_rsrc(p.latent, lat_bytes);
-  f.rope = make_rsrc(p.rope, rope_bytes);
-  f.voff_lat = (8 * w + (l >> 3)) * f.lsb + 128 * (l & 7);
-  f.voff_rope = (8 * w + (l & 7)) * f.rsb;
-  return f;
-}
-
-// Zero a workgroup's LDS tile buffers (before their first loads): lanes past
-// a split's end are written with zeros by the loads, and this keeps every
-// byte a tile's masked rows could hold finite in any case.
-template <int NT>
-__device__ __forceinline__ void zero_lds(char* buf, int bytes, int tid) {
-  for (int i = tid * 16; i < bytes; i += NT * 16) *(u32x4*)(buf + i) = u32x4{0, 0, 0, 0};
-}
 
 // fp8 cache: the raw codes of a tile (32 rows x 576 bytes) and its 32 bf16
 // row scales are brought into an LDS staging area with direct global->LDS
@@ -1002,7 +949,6 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   constexpr int NT = 64 * NW;
   constexpr int DMA_PER_TILE = TileLoad<NW>::PIECES;  // wave-wide loads per tile per wave
-  constexpr int PF_PER_TILE = 0;                        // prefetch loads per step per wave
   char* const buf0 = bufs;
   char* const buf1 = bufs + TILE_BYTES;
   char* const buf2 = bufs + 2 * TILE_BYTES;
@@ -1029,22 +975,6 @@ void mla_decode_bf16_kernel(DecodeParams p) {
                          w, voff);
   };
   const auto no_issue = [](int) {};
-  // L2 prefetch (four waves): step j touches tile j+4 (its loads go out in
-  // step j+2); the bytes land in the RoPE-key rows of tile j-1's buffer,
-  // which no one reads during step j and which tile j+3's loads, issued
-  // later, overwrite (loads complete in order)
-  TilePrefetch pf;
-  if constexpr (PF_PER_TILE > 0) pf = tile_prefetch<NW>(p, w, l);
-  auto prefetch_slot = [&](int t, int j, char* dead) {
-    if constexpr (PF_PER_TILE > 0) {
-      if (t < 2) {
-        const int row = __builtin_amdgcn_readlane(trow, min(j + 4, ntiles - 1));
-        const uint32_t m = __builtin_amdgcn_readfirstlane(lds_u32(dead + ROPE_OFF) + w * 512);
-        if (t == 0) pf.issue_lat(row, m);
-        else pf.issue_rope(row, m);
-      }
-    }
-  };
 
   // Prologue: the queries (independent of everything else), the block
   // entries of tiles 0 and 1 (scalar path, one wait), their loads, the rest
@@ -1095,8 +1025,8 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     bf16x8 pb[2];     // PV B operand (weights of the tile whose PV is next)
     bf16x8 pring[3];  // PV A operands in flight
     auto step_end = [&]() {
-      // tile j+1 landed; tile j+2 and the step's prefetches may be in flight
-      wait_vm_lgkm0<DMA_PER_TILE + PF_PER_TILE>();
+      // tile j+1 landed, tile j+2 may be in flight
+      wait_vm_lgkm0<DMA_PER_TILE>();
       __builtin_amdgcn_s_barrier();
       compiler_fence();               // no LDS read of tile j+1 moves above this
     };
@@ -1107,7 +1037,6 @@ void mla_decode_bf16_kernel(DecodeParams p) {
       pipe_step<true, false, true>(buf0, nullptr, wi.t0, wi.t1, qreg, qpe, la, h, st, s0, s1, pb,
                                    pring, [&](int t, int n) {
                                if (t == 0) next = load(buf2, 2);
-                               prefetch_slot(t, 0, buf3);
                                next.step_n(t, n);
                              });
       step_end();
@@ -1118,7 +1047,6 @@ void mla_decode_bf16_kernel(DecodeParams p) {
         pipe_step<true, true, false>(K, V, wi.t0 + j * TILE, wi.t1, qreg, qpe, la, h, st, sn, sp,
                                      pb, pring, [&](int t, int n) {
                                 if (t == 0) next = load(Z, j + 2);
-                                prefetch_slot(t, j, V);
                                 next.step_n(t, n);
                               });
         step_end();
@@ -1218,13 +1146,10 @@ void mla_decode_fp8_kernel(DecodeParams p) {
                         __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)), nvalid(k), w, voff);
   };
 
-  // Prologue: zero the staging buffers; raw tiles 0..2 (block entries on the
+  // Prologue (a tile's loads write all its staging bytes, zeros past the
+  // split's end, so nothing is cleared): raw tiles 0..2 (block entries on the
   // scalar path), the queries, the split's block table; one wait; then the
   // per-tile rows and the scales of the whole split; widen tile 0.
-  zero_lds<NT>(&stage[0][0], 3 * STG_BYTES, tid);
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     fp8_load<NW>(p, stage[k], dummy,
