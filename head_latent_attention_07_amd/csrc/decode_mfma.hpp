@@ -4,36 +4,39 @@
 // "MLA: compress the pair, not the heads"): every head scores its absorbed
 // query q = [q_nope W_UK[h] | q_pe] against the same cached rows
 // [c_t | k^R_t] and mixes the same latent rows c_t, so the head dimension is
-// the M dimension of two dense contractions that share one operand stream:
+// the N dimension of two dense contractions that share one operand stream:
 //
 //   S^T[t, h]  = sum_d  K[t, d] Q^T[d, h]        (d over 576)
 //   O^T[d, h] += sum_t  C^T[d, t] P^T[t, h]      (d over 512)
 //
 // Work decomposition
-//   * workgroup = (sequence b, token split s, head group g), NW waves;
-//     wave w owns 32 heads; its absorbed queries live in registers as the
-//     MFMA B operand (36 k-steps x 8 bf16 per lane) and its output
-//     accumulator O^T (32 heads x 512 dims, fp32) in 16 32x32 tiles.
-//   * the workgroup streams its token range in tiles of 32 rows through LDS,
-//     double buffered: global loads of tile i+1 are in flight while tile i is
-//     computed. A tile is 32 rows x 1152 bytes, stored row-major with a
-//     16-byte-chunk XOR swizzle (see lds_off) so that both read patterns
-//     below are free of bank conflicts.
-//   * QK^T reads the tile with ds_read_b128 (token-major A operand); PV reads
+//   * workgroup = (sequence b, token split s, head group g), NW waves; wave
+//     w owns 32 heads: its absorbed queries are the S^T B operand (latent
+//     k-steps in registers, RoPE k-steps in LDS) and its O^T accumulator
+//     (32 heads x 512 dims, fp32) fills the 256 AGPRs as 16 32x32 tiles.
+//   * the workgroup streams its token range through LDS in tiles of 32 rows
+//     (32 x 1152 bytes, row-major, 16-byte chunks XOR-swizzled per row so
+//     both read patterns are free of bank conflicts), loaded with
+//     direct-to-LDS buffer loads issued between the MFMAs (two tiles ahead).
+//   * S^T reads the tile with ds_read_b128 (token-major A operand); PV reads
 //     the same bytes with ds_read_b64_tr_b16, the gfx950 transposing LDS
 //     read, which hands each lane 4 consecutive tokens of one latent column.
 //     The token order inside a 16-token k-step is permuted to match the
-//     32x32 accumulator layout of S^T, so P^T goes from the QK accumulator to
-//     the PV B operand without any cross-lane traffic.
-//   * online softmax in base 2 (the absorbed query is pre-scaled by
-//     softmax_scale * log2 e) with lazy rescaling: the running max used for
-//     exp2 moves only when a tile's max exceeds it by more than 8, which keeps
-//     every p <= 2^8 and skips most of the 256-register rescale.
-//   * fp8 cache: rows are converted to bf16 (exact) as they are written to
-//     LDS; the per-row scale multiplies the row's scores and, after the
-//     softmax sum, its probabilities, so both MFMAs see exact e4m3 values.
-//   * each split writes its normalised partial O (fp32) and its log2
-//     sum-exp; a separate kernel merges the splits and applies W_UV.
+//     32x32 accumulator layout of S^T, so P^T goes from the S^T accumulator
+//     to the PV B operand without any cross-lane traffic.
+//   * softmax in base 2 (the absorbed query is pre-scaled by softmax_scale *
+//     log2 e) against a fixed exponent reference, the split's first-tile
+//     max: the accumulators are never rescaled; a split whose weights reach
+//     2^64 is recomputed against its true max.
+//   * bf16 cache: a cross-tile software pipeline (pipe_step) interleaves the
+//     PV of tile j-1 with the S^T of tile j in one stream of MFMAs.
+//   * fp8 cache: raw e4m3 tiles are staged in LDS and widened (exactly) to
+//     the bf16 tile layout; the per-row scale multiplies the row's scores
+//     and, after the softmax sum, its weights, so both MFMAs see exact
+//     e4m3 values.
+//   * each split writes its normalised partial O (fp16 relative to the row
+//     max, with the fp32 factor) and its log2 sum-exp; a separate kernel
+//     merges the splits and applies W_UV.
 #pragma once
 
 #include <type_traits>

@@ -61,7 +61,7 @@ constexpr int AB_OPITCH = 32 * 2 + 16;     // 80 B: output staging row (32 bf16 
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
   __shared__ __attribute__((aligned(1024))) char w_lds[D_N * AB_ROW];   // 32 KB
-  __shared__ __attribute__((aligned(16))) char a_lds[32 * AB_APITCH];
+  __shared__ __attribute__((aligned(16))) char a_lds[2][32 * AB_APITCH];  // two chunks of 32 seq
   __shared__ __attribute__((aligned(16))) char o_lds[4][32 * AB_OPITCH];  // per wave: 32 seq x 32 cols
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,52 +96,67 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
   const int r1 = 8 * h + (jj >> 2);                    // + 16 ks, and + 4 for the upper half
   const int chunk = 4 * w + (2 * (g16 & 1) + ((jj & 3) >> 1));
   const int off = 8 * (jj & 1);
-  for (int b0 = 0; b0 < p.B; b0 += 32) {
-    // q_nope rows of the chunk -> LDS (zero rows past B); q_pe scaled copy
-    for (int i = tid; i < 32 * (D_N / 8); i += 256) {
-      const int r = i / (D_N / 8), c = i % (D_N / 8);
-      u32x4 v = {0, 0, 0, 0};
-      if (b0 + r < p.B) v = *(const u32x4*)(p.q_nope + ((int64_t)(b0 + r) * p.H + head) * D_N + 8 * c);
-      *(u32x4*)(a_lds + r * AB_APITCH + 16 * c) = v;
-    }
-    if (quarter == 0) {
-      // q_pe: 8 consecutive values per thread (32 rows x 64)
-      const int r = tid >> 3, c = 8 * (tid & 7);
-      if (b0 + r < p.B) {
-        const int64_t bh = (int64_t)(b0 + r) * p.H + head;
-        const bf16x8 v = *(const bf16x8*)(p.q_pe + bh * D_R + c);
-        bf16x8 o;
+  // passes of 64 sequences: both chunks' q_nope rows are loaded (one wait
+  // for them and the weight slice), then multiplied chunk by chunk
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    {
+      u32x4 v[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = (bf16)((float)v[k] * p.c);
-        *(bf16x8*)(p.q + qop_index(b0 + r, head, D_C + c, p.H)) = o;
+      for (int k = 0; k < 4; ++k) {   // 64 rows x 16 pieces of 16 bytes, 4 per thread
+        const int i = tid + 256 * k, r = i >> 4, c = i & 15;
+        v[k] = u32x4{0, 0, 0, 0};
+        if (b0 + r < p.B) v[k] = *(const u32x4*)(p.q_nope + ((int64_t)(b0 + r) * p.H + head) * D_N + 8 * c);
+      }
+      if (quarter == 0) {
+        // q_pe: 8 consecutive values per thread (64 rows x 64, two per thread)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int r = (tid >> 3) + 32 * k, c = 8 * (tid & 7);
+          if (b0 + r < p.B) {
+            const int64_t bh = (int64_t)(b0 + r) * p.H + head;
+            const bf16x8 x = *(const bf16x8*)(p.q_pe + bh * D_R + c);
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)x[e] * p.c);
+            *(bf16x8*)(p.q + qop_index(b0 + r, head, D_C + c, p.H)) = o;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid + 256 * k, r = i >> 4, c = i & 15;
+        *(u32x4*)(a_lds[r >> 5] + (r & 31) * AB_APITCH + 16 * c) = v[k];
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK slice landed (first chunk)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK slice landed (first pass)
     __syncthreads();
-    f32x16 acc = f32x16{};
+    for (int cb = 0; cb < 2 && b0 + 32 * cb < p.B; ++cb) {
+      const int bc0 = b0 + 32 * cb;
+      f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < D_N / 16; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(a_lds + l32 * AB_APITCH + 2 * (16 * ks + 8 * h));
-      const int ra = 16 * ks + r1, rb = ra + 4;
-      const bf16x8 bop = tr_read_8(w_lds + ra * AB_ROW + 16 * (chunk ^ wrow_swizzle(ra)) + off,
-                                   w_lds + rb * AB_ROW + 16 * (chunk ^ wrow_swizzle(rb)) + off);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+      for (int ks = 0; ks < D_N / 16; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(a_lds[cb] + l32 * AB_APITCH + 2 * (16 * ks + 8 * h));
+        const int ra = 16 * ks + r1, rb = ra + 4;
+        const bf16x8 bop = tr_read_8(w_lds + ra * AB_ROW + 16 * (chunk ^ wrow_swizzle(ra)) + off,
+                                     w_lds + rb * AB_ROW + 16 * (chunk ^ wrow_swizzle(rb)) + off);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+      }
+      // lane holds column 32w + l32 of the slice, rows b = 8(r/4) + 4h + r%4:
+      // transpose through LDS so each lane stores 8 consecutive columns of
+      // one sequence (one 16-byte piece of the query layout)
+      char* ol = o_lds[w];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *(bf16*)(ol + (8 * (r >> 2) + 4 * h + (r & 3)) * AB_OPITCH + 2 * l32) = (bf16)(acc[r] * p.c);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int id = l + 64 * i, r = id >> 2, c8 = id & 3;
+        const u32x4 v = *(const u32x4*)(ol + r * AB_OPITCH + 16 * c8);
+        if (bc0 + r < p.B)
+          *(u32x4*)(p.q + qop_index(bc0 + r, head, quarter * AB_COLS + 32 * w + 8 * c8, p.H)) = v;
+      }
     }
-    // lane holds column 32w + l32 of the slice, rows b = 8(r/4) + 4h + r%4:
-    // transpose through LDS so each lane stores 8 consecutive columns of one
-    // sequence (one 16-byte piece of the query layout)
-    char* ol = o_lds[w];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      *(bf16*)(ol + (8 * (r >> 2) + 4 * h + (r & 3)) * AB_OPITCH + 2 * l32) = (bf16)(acc[r] * p.c);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = l + 64 * i, r = id >> 2, c8 = id & 3;
-      const u32x4 v = *(const u32x4*)(ol + r * AB_OPITCH + 16 * c8);
-      if (b0 + r < p.B)
-        *(u32x4*)(p.q + qop_index(b0 + r, head, quarter * AB_COLS + 32 * w + 8 * c8, p.H)) = v;
-    }
-    __syncthreads();   // a_lds is rewritten by the next chunk
+    __syncthreads();   // a_lds is rewritten by the next pass
   }
 }
 
