@@ -86,10 +86,15 @@ class HipEvents:
         self.lib.hipEventDestroy(e)
 
 
+# the files whose text defines the split attention kernels (the launch code
+# in mla_api.hip only passes them their parameters)
+KERNEL_SOURCES = ("common.hpp", "decode_mfma.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "head_latent_attention_07_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -5,6 +5,8 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <hip/hip_ext.h>
+
 #include "mla.h"
 #include "append.hpp"
 #include "decode_mfma.hpp"
@@ -243,19 +245,26 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   dp.part_lse = part_lse;
   const int nq = B * pl.S;
   const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
-  if (opts && opts->attn_begin) (void)hipEventRecord(opts->attn_begin, stream);
+  // with timing events, the launch itself records the kernel's start and end
+  // (the dispatch's own timestamps, not those of separate event packets)
+  hipEvent_t ev0 = opts ? opts->attn_begin : nullptr, ev1 = opts ? opts->attn_end : nullptr;
+  auto launch = [&](auto kern, int threads) {
+    if (ev0 || ev1)
+      hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, ev0, ev1, 0, dp);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, dp);
+  };
   const bool fp8 = (cdt == MLA_FP8_E4M3);
   switch (pl.NW * 2 + (fp8 ? 1 : 0)) {
-    case 8: hipLaunchKernelGGL((mla_decode_bf16_kernel<4>), grid, dim3(256), 0, stream, dp); break;
-    case 9: hipLaunchKernelGGL((mla_decode_fp8_kernel<4>), grid, dim3(256), 0, stream, dp); break;
-    case 4: hipLaunchKernelGGL((mla_decode_bf16_kernel<2>), grid, dim3(128), 0, stream, dp); break;
-    case 5: hipLaunchKernelGGL((mla_decode_fp8_kernel<2>), grid, dim3(128), 0, stream, dp); break;
-    case 2: hipLaunchKernelGGL((mla_decode_bf16_kernel<1>), grid, dim3(64), 0, stream, dp); break;
-    case 3: hipLaunchKernelGGL((mla_decode_fp8_kernel<1>), grid, dim3(64), 0, stream, dp); break;
+    case 8: launch(mla_decode_bf16_kernel<4>, 256); break;
+    case 9: launch(mla_decode_fp8_kernel<4>, 256); break;
+    case 4: launch(mla_decode_bf16_kernel<2>, 128); break;
+    case 5: launch(mla_decode_fp8_kernel<2>, 128); break;
+    case 2: launch(mla_decode_bf16_kernel<1>, 64); break;
+    case 3: launch(mla_decode_fp8_kernel<1>, 64); break;
     default: return MLA_ERR_UNSUPPORTED;
   }
   MLA_TRY(launch_status());
-  if (opts && opts->attn_end) (void)hipEventRecord(opts->attn_end, stream);
 
   CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
   hipLaunchKernelGGL(mla_combine_kernel, dim3(ceil_div(H, 8) * 8 * nbc), dim3(256), 0, stream, cp);

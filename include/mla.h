@@ -76,8 +76,10 @@ typedef struct {
 /* Optional tuning and instrumentation for the decode calls (pass NULL for the
  * defaults). Zero fields mean "choose automatically".
  *   num_splits     number of token ranges each sequence is cut into (split-KV).
- *   attn_begin/end if non-NULL, HIP events recorded on `stream` immediately
- *                  before and after the split attention kernel, for timing it. */
+ *   attn_begin/end if non-NULL, HIP events that record the start and the end
+ *                  of the split attention kernel on `stream` (bf16 / fp8
+ *                  path: taken from the kernel's own dispatch; f32 path:
+ *                  recorded immediately before and after it), for timing it. */
 typedef struct {
   int32_t num_splits;
   int32_t reserved0;
