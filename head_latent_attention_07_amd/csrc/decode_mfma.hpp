@@ -555,17 +555,6 @@ __device__ __forceinline__ int tile_rows_lanes(const DecodeParams& p, int b, int
   return (int)((int64_t)b * p.seq_capacity + t);
 }
 
-// Physical row of the first token of a tile (tiles never cross a block:
-// block_size is a multiple of 32). `tab` is the split's block table in LDS.
-__device__ __forceinline__ int64_t tile_base_row(const DecodeParams& p, int b, int tile_t0,
-                                                 const int* tab, int first_blk) {
-  if (p.block_table) {
-    const int blk = __builtin_amdgcn_readfirstlane(tab[tile_t0 / p.block_size - first_blk]);
-    return (int64_t)blk * p.block_size + (tile_t0 % p.block_size);
-  }
-  return (int64_t)b * p.seq_capacity + tile_t0;
-}
-
 // Buffer resource over [base, base + bytes) for raw buffer loads: accesses at
 // or past `bytes` return zeros instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -662,15 +651,6 @@ struct TileLoad {
     (piece<I>(), ...);
   }
   __device__ __forceinline__ void all() const { all_(std::make_integer_sequence<int, PIECES>{}); }
-  // after MFMA t (0..67) of the tile being computed: piece i goes out at
-  // t = 2 + 64 i / PIECES, spread over both MFMA chains
-  template <int... I>
-  __device__ __forceinline__ void step_(int t, std::integer_sequence<int, I...>) const {
-    ((t == 2 + (64 * I) / PIECES ? piece<I>() : void()), ...);
-  }
-  __device__ __forceinline__ void step(int t) const {
-    step_(t, std::make_integer_sequence<int, PIECES>{});
-  }
   // after slot t of a pipelined step of n slots: piece i at
   // t = 1 + i * span / PIECES, span = min(n - 2, 2 PIECES) (every other slot
   // from the step's start while there is room), so the tile has most of two
