@@ -42,21 +42,11 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float v) {
 }
 
 // one wave per sequence: lane l owns latent values 8l..8l+7 and, for l < 32,
-// the RoPE pair (2l, 2l+1)
+// the RoPE pair (2l, 2l+1). The inputs are loaded and the rotation angle is
+// computed before the destination row is known (their latencies overlap
+// that of the position and block-table reads).
 __global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
   const int b = blockIdx.x, l = threadIdx.x;
-  const int pos = p.positions[b];
-  int64_t r;
-  if (p.block_table) {
-    if (pos < 0 || pos / p.block_size >= p.max_blocks) return;
-    r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
-        pos % p.block_size;
-  } else {
-    if (pos < 0 || pos >= p.seq_capacity) return;
-    r = (int64_t)b * p.seq_capacity + pos;
-  }
-  if (r < 0 || r >= p.rows) return;
-
   float x[8];
   if (p.in_bf16) {
     const bf16x8 v = *(const bf16x8*)((const bf16*)p.c_kv + (int64_t)b * D_C + 8 * l);
@@ -68,24 +58,34 @@ __global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { x[i] = v0[i]; x[4 + i] = v1[i]; }
   }
-  float r0 = 0.f, r1 = 0.f;
-  if (l < D_R / 2) {
-    double xe, xo;
-    if (p.in_bf16) {
-      const bf16* k = (const bf16*)p.k_pe + (int64_t)b * D_R;
-      xe = (float)k[2 * l];
-      xo = (float)k[2 * l + 1];
-    } else {
-      const float* k = (const float*)p.k_pe + (int64_t)b * D_R;
-      xe = k[2 * l];
-      xo = k[2 * l + 1];
-    }
-    const double freq = pow(p.theta, -2.0 * (double)l / (double)D_R);
-    double sn, cs;
-    sincos((double)pos * freq, &sn, &cs);
-    r0 = (float)(xe * cs - xo * sn);
-    r1 = (float)(xe * sn + xo * cs);
+  double xe = 0.0, xo = 0.0;
+  const int lp = l & (D_R / 2 - 1);   // lanes 32..63 repeat a pair (unused)
+  if (p.in_bf16) {
+    const bf16* k = (const bf16*)p.k_pe + (int64_t)b * D_R;
+    xe = (float)k[2 * lp];
+    xo = (float)k[2 * lp + 1];
+  } else {
+    const float* k = (const float*)p.k_pe + (int64_t)b * D_R;
+    xe = k[2 * lp];
+    xo = k[2 * lp + 1];
   }
+  const int pos = p.positions[b];
+  const double freq = pow(p.theta, -2.0 * (double)lp / (double)D_R);
+  double sn, cs;
+  sincos((double)pos * freq, &sn, &cs);
+  const float r0 = (float)(xe * cs - xo * sn);
+  const float r1 = (float)(xe * sn + xo * cs);
+
+  int64_t r;
+  if (p.block_table) {
+    if (pos < 0 || pos / p.block_size >= p.max_blocks) return;
+    r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
+        pos % p.block_size;
+  } else {
+    if (pos < 0 || pos >= p.seq_capacity) return;
+    r = (int64_t)b * p.seq_capacity + pos;
+  }
+  if (r < 0 || r >= p.rows) return;
 
   if (p.cache_kind == CACHE_F32) {
     float* dst = (float*)p.latent + r * p.latent_stride + 8 * l;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = fmaxf(amax, fmaxf(fabsf(r0), fabsf(r1)));
+    if (l < D_R / 2) amax = fmaxf(amax, fmaxf(fabsf(r0), fabsf(r1)));
     amax = wave_max(amax);
     float s;
     if (amax == 0.f) {
