@@ -1,9 +1,10 @@
 """Benchmark: one MLA decode step on one MI355X (gfx950).
 
-A step is one pass of the whole hot path over one batch: mla_cache_append
-(the new token of every sequence, RoPE on its key) then mla_decode_paged
-(absorb GEMM, split-KV flash decode over the latent+RoPE cache, merge of the
-splits and the W_UV projection). Workload: 64 sequences, 128 heads, 4096
+A step is one pass of the whole hot path over one batch: one
+mla_decode_paged call that first appends the new token of every sequence
+(RoPE on its key, in the same launch as the absorb GEMM), then runs the
+split-KV flash decode over the latent+RoPE cache, the merge of the splits and
+the W_UV projection. Workload: 64 sequences, 128 heads, 4096
 cached tokens each (the new one included), DeepSeek-V3 widths, bf16, paged
 cache of 64-token blocks placed by a seeded random permutation.
 
@@ -17,6 +18,8 @@ Prints ONE JSON line (see the fields below). Options:
   --gpus N                 only N = 1 is supported (one process, one GPU)
   --no-cpu                 skip the CPU-oracle baseline leg
   --config NAME            3u (default), 3, 4 or 5 (other workloads, for study)
+  --separate-append        append with its own mla_cache_append call before the
+                           decode call (same work, one more launch)
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
@@ -54,6 +57,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", default="3u")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate-append", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--write-traffic", nargs=4, default=None)
     return ap.parse_args()
@@ -249,10 +253,14 @@ def main():
 
     def step(L, events=None):
         inp = L["inp"]
-        mla.cache_append(L["c"], L["k"], L["pos"], L["lat"], L["rope"], heads=H,
-                         scales=inp.scales, seq_capacity=inp.seq_capacity,
-                         block_table=inp.block_table, block_size=inp.block_size)
-        mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events)
+        new_rows = (L["c"], L["k"], L["pos"])
+        if args.separate_append:
+            mla.cache_append(*new_rows, L["lat"], L["rope"], heads=H, scales=inp.scales,
+                             seq_capacity=inp.seq_capacity, block_table=inp.block_table,
+                             block_size=inp.block_size)
+            new_rows = None
+        mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events,
+                          append=new_rows)
 
     for i in range(args.warmup):
         step(layers[i % N_LAYERS_CYCLED])

@@ -36,9 +36,15 @@ class Dims(ctypes.Structure):
                 ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32)]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("c_kv", ctypes.c_void_p), ("k_pe", ctypes.c_void_p), ("in_dtype", ctypes.c_int),
+                ("positions", ctypes.c_void_p), ("rope_theta", ctypes.c_float)]
+
+
 class DecodeOptions(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-                ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p)]
+                ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p),
+                ("append", ctypes.POINTER(AppendArgs))]
 
 
 _lib = None
@@ -118,13 +124,21 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
-def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None):
-    if not num_splits and events is None:
+def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=None):
+    """mla_decode_options for the call (None when every field is a default).
+    `append` = (c_kv, k_pe, positions[, rope_theta]) appends those rows first."""
+    if not num_splits and events is None and append is None:
         return None
     o = DecodeOptions()
     o.num_splits = num_splits
     if events is not None:
         o.attn_begin, o.attn_end = events
+    if append is not None:
+        c_kv, k_pe, positions = append[:3]
+        theta = append[3] if len(append) > 3 else 10000.0
+        a = AppendArgs(_ptr(c_kv), _ptr(k_pe), dtype_code(c_kv.dtype), _ptr(positions), theta)
+        o._append_keep = a            # the struct must outlive the call
+        o.append = ctypes.pointer(a)
     return ctypes.byref(o)
 
 
@@ -159,8 +173,8 @@ def cache_append(c_kv: torch.Tensor, k_pe: torch.Tensor, positions: torch.Tensor
 
 def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
             scales=None, seq_capacity=0, block_table=None, block_size=64, softmax_scale=None,
-            out=None, lse=None, workspace=None, num_splits=0, events=None, stream=None,
-            want_lse=True):
+            out=None, lse=None, workspace=None, num_splits=0, events=None, append=None,
+            stream=None, want_lse=True):
     lib = load()
     B, H = q_nope.shape[0], q_nope.shape[1]
     d = dims(H)
@@ -176,7 +190,7 @@ def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
     if workspace is None:
         ws = workspace_size(H, B, max_len, act, cdt, num_splits)
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
-    opts = _opts(num_splits, events)
+    opts = _opts(num_splits, events, append)
     head = [ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), act,
             _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(scales), cdt,
             latent.shape[0]]

@@ -45,8 +45,7 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float v) {
 // the RoPE pair (2l, 2l+1). The inputs are loaded and the rotation angle is
 // computed before the destination row is known (their latencies overlap
 // that of the position and block-table reads).
-__global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
-  const int b = blockIdx.x, l = threadIdx.x;
+__device__ __forceinline__ void append_row(const AppendParams& p, int b, int l) {
   float x[8];
   if (p.in_bf16) {
     const bf16x8 v = *(const bf16x8*)((const bf16*)p.c_kv + (int64_t)b * D_C + 8 * l);
@@ -124,6 +123,10 @@ __global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
     }
     if (l == 0) p.scales[r] = (bf16)s;
   }
+}
+
+__global__ __launch_bounds__(64) void mla_append_kernel(AppendParams p) {
+  append_row(p, blockIdx.x, threadIdx.x);
 }
 
 }  // namespace mla

@@ -129,6 +129,51 @@ mla_status launch_status() {
     if (_s != MLA_OK) return _s;           \
   } while (0)
 
+// Validation of a cache append (mla_cache_append, or the append of a decode
+// call); fills the kernel parameters.
+mla_status check_append(const mla_dims* dims, const void* c_kv, const void* k_pe,
+                        mla_dtype in_dtype, const int32_t* positions, int32_t batch,
+                        void* latent, int64_t ls, void* rope, int64_t rs, void* scales,
+                        mla_dtype cdt, int64_t rows, int64_t seq_capacity,
+                        const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                        float rope_theta, AppendParams* out) {
+  if (!dims || batch < 0) return MLA_ERR_INVALID_ARG;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (in_dtype != MLA_F32 && in_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  const size_t ce = elem_size(cdt);
+  if (!ce) return MLA_ERR_UNSUPPORTED;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.f) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!c_kv || !k_pe || !positions || !latent || !rope) return MLA_ERR_INVALID_ARG;
+  if (cdt == MLA_FP8_E4M3 && !scales) return MLA_ERR_INVALID_ARG;
+  if (ls < D_C || rs < D_R || rows < 1) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(latent) || !aligned16(rope) || (ls * ce) % 16 != 0 || (rs * ce) % 16 != 0 ||
+      !aligned16(c_kv) || ((uintptr_t)k_pe & 3) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (block_size <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  } else {
+    if (seq_capacity < 1 || (int64_t)batch * seq_capacity > rows) return MLA_ERR_INVALID_ARG;
+  }
+  out->c_kv = c_kv;
+  out->k_pe = k_pe;
+  out->in_bf16 = (in_dtype == MLA_BF16);
+  out->positions = positions;
+  out->latent = latent;
+  out->latent_stride = ls;
+  out->rope = rope;
+  out->rope_stride = rs;
+  out->scales = (bf16*)scales;
+  out->cache_kind = (cdt == MLA_F32) ? CACHE_F32 : (cdt == MLA_BF16) ? CACHE_BF16 : CACHE_FP8;
+  out->rows = rows;
+  out->seq_capacity = seq_capacity;
+  out->block_table = block_table;
+  out->max_blocks = max_blocks;
+  out->block_size = block_size;
+  out->theta = (double)rope_theta;
+  return MLA_OK;
+}
+
 // Validation shared by both decode entry points.
 mla_status check_decode(const mla_dims* dims, const void* q_nope, const void* q_pe,
                         const void* w_uk, const void* w_uv, mla_dtype act, const void* latent,
@@ -170,6 +215,15 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
                       size_t workspace_bytes, const mla_decode_options* opts,
                       hipStream_t stream) {
   const int B = batch, H = dims->heads;
+  AppendParams app;
+  const bool do_append = opts && opts->append;
+  if (do_append) {
+    const mla_append_args* a = opts->append;
+    MLA_TRY(check_append(dims, a->c_kv, a->k_pe, a->in_dtype, a->positions, batch,
+                         const_cast<void*>(latent), ls, const_cast<void*>(rope), rs,
+                         const_cast<void*>(scales), cdt, rows, seq_capacity, block_table,
+                         max_blocks, block_size, a->rope_theta, &app));
+  }
   const Plan pl = make_plan(B, H, max_len, act, opts);
   const WsLayout wl = ws_layout(B, H, pl, act);
   if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
@@ -183,6 +237,10 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   (void)hipGetLastError();  // start from a clean launch-error state
 
   if (act == MLA_F32) {
+    if (do_append) {
+      hipLaunchKernelGGL(mla_append_kernel, dim3(B), dim3(64), 0, stream, app);
+      MLA_TRY(launch_status());
+    }
     float* q = (float*)(ws + wl.q_off);
     hipLaunchKernelGGL(mla_absorb_f32_kernel, dim3(B * H), dim3(256), 0, stream,
                        (const float*)q_nope, (const float*)q_pe, (const float*)w_uk, q, H, c);
@@ -218,7 +276,12 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   bf16* q = (bf16*)(ws + wl.q_off);
   const int nbc = ceil_div(B, 32);
   AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c};
-  hipLaunchKernelGGL(mla_absorb_kernel, dim3(ceil_div(H, 32) * 128), dim3(256), 0, stream, ap);
+  const int absorb_blocks = ceil_div(H, 32) * 128;
+  if (do_append)
+    hipLaunchKernelGGL(mla_absorb_append_kernel, dim3(absorb_blocks + ceil_div(B, 4)), dim3(256), 0,
+                       stream, ap, app, absorb_blocks);
+  else
+    hipLaunchKernelGGL(mla_absorb_kernel, dim3(absorb_blocks), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());
 
   DecodeParams dp;
@@ -346,41 +409,11 @@ mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* 
                             mla_dtype cdt, int64_t rows, int64_t seq_capacity,
                             const int32_t* block_table, int32_t max_blocks, int32_t block_size,
                             float rope_theta, hipStream_t stream) {
-  if (!dims || batch < 0) return MLA_ERR_INVALID_ARG;
-  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
-  if (in_dtype != MLA_F32 && in_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
-  const size_t ce = elem_size(cdt);
-  if (!ce) return MLA_ERR_UNSUPPORTED;
-  if (!std::isfinite(rope_theta) || rope_theta <= 0.f) return MLA_ERR_INVALID_ARG;
-  if (batch == 0) return MLA_OK;
-  if (!c_kv || !k_pe || !positions || !latent || !rope) return MLA_ERR_INVALID_ARG;
-  if (cdt == MLA_FP8_E4M3 && !scales) return MLA_ERR_INVALID_ARG;
-  if (ls < D_C || rs < D_R || rows < 1) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(latent) || !aligned16(rope) || (ls * ce) % 16 != 0 || (rs * ce) % 16 != 0 ||
-      !aligned16(c_kv) || ((uintptr_t)k_pe & 3) != 0)
-    return MLA_ERR_INVALID_ARG;
-  if (block_table) {
-    if (block_size <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
-  } else {
-    if (seq_capacity < 1 || (int64_t)batch * seq_capacity > rows) return MLA_ERR_INVALID_ARG;
-  }
   AppendParams p;
-  p.c_kv = c_kv;
-  p.k_pe = k_pe;
-  p.in_bf16 = (in_dtype == MLA_BF16);
-  p.positions = positions;
-  p.latent = latent;
-  p.latent_stride = ls;
-  p.rope = rope;
-  p.rope_stride = rs;
-  p.scales = (bf16*)scales;
-  p.cache_kind = (cdt == MLA_F32) ? CACHE_F32 : (cdt == MLA_BF16) ? CACHE_BF16 : CACHE_FP8;
-  p.rows = rows;
-  p.seq_capacity = seq_capacity;
-  p.block_table = block_table;
-  p.max_blocks = max_blocks;
-  p.block_size = block_size;
-  p.theta = (double)rope_theta;
+  MLA_TRY(check_append(dims, c_kv, k_pe, in_dtype, positions, batch, latent, ls, rope, rs,
+                       scales, cdt, rows, seq_capacity, block_table, max_blocks, block_size,
+                       rope_theta, &p));
+  if (batch == 0) return MLA_OK;
   (void)hipGetLastError();
   hipLaunchKernelGGL(mla_append_kernel, dim3(batch), dim3(64), 0, stream, p);
   return launch_status();

@@ -15,6 +15,7 @@
 // one column.
 #pragma once
 
+#include "append.hpp"
 #include "common.hpp"
 
 namespace mla {
@@ -59,7 +60,7 @@ constexpr int AB_COLS = 128;               // output columns per workgroup
 constexpr int AB_ROW = AB_COLS * 2;        // 256 B per W row slice in LDS
 constexpr int AB_OPITCH = 32 * 2 + 16;     // 80 B: output staging row (32 bf16 + pad)
 
-__global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
+__device__ __forceinline__ void absorb_workgroup(const AbsorbParams& p, int x) {
   __shared__ __attribute__((aligned(1024))) char w_lds[D_N * AB_ROW];   // 32 KB
   __shared__ __attribute__((aligned(16))) char a_lds[2][32 * AB_APITCH];  // two chunks of 32 seq
   __shared__ __attribute__((aligned(16))) char o_lds[4][32 * AB_OPITCH];  // per wave: 32 seq x 32 cols
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
   // one XCD, so its L2 merges them into whole lines
   int head, quarter;
   {
-    const int x = blockIdx.x, xcd = x & 7, i = x >> 3;
+    const int xcd = x & 7, i = x >> 3;
     const int cluster = (i >> 4) * 8 + xcd;
     head = cluster * 4 + ((i & 15) >> 2);
     quarter = i & 3;
@@ -157,6 +158,23 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
       }
     }
     __syncthreads();   // a_lds is rewritten by the next pass
+  }
+}
+
+__global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
+  absorb_workgroup(p, blockIdx.x);
+}
+
+// absorb and cache append in one launch: workgroups past the absorb grid
+// append the new rows, one sequence per wave (the absorb neither reads nor
+// writes the cache, so the two halves are independent)
+__global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, AppendParams a,
+                                                               int absorb_blocks) {
+  if ((int)blockIdx.x < absorb_blocks) {
+    absorb_workgroup(p, blockIdx.x);
+  } else {
+    const int b = ((int)blockIdx.x - absorb_blocks) * 4 + (int)(threadIdx.x >> 6);
+    if (b < p.B) append_row(a, b, threadIdx.x & 63);
   }
 }
 

@@ -73,6 +73,16 @@ typedef struct {
   int32_t heads, d_c, d_rope, d_nope, d_v;
 } mla_dims;
 
+/* The arguments of mla_cache_append that a decode call does not already
+ * carry (see mla_decode_options.append). */
+typedef struct mla_append_args {
+  const void* c_kv;           /* [batch, d_c] new latent rows, in_dtype */
+  const void* k_pe;           /* [batch, d_rope] new RoPE keys, not yet rotated */
+  mla_dtype in_dtype;         /* MLA_F32 or MLA_BF16 */
+  const int32_t* positions;   /* [batch] 0-based position of each new token */
+  float rope_theta;           /* RoPE base (10000 in the DeepSeek-V3 setting) */
+} mla_append_args;
+
 /* Optional tuning and instrumentation for the decode calls (pass NULL for the
  * defaults). Zero fields mean "choose automatically".
  *   num_splits     number of token ranges each sequence is cut into (split-KV).
@@ -85,6 +95,13 @@ typedef struct {
   int32_t reserved0;
   hipEvent_t attn_begin;
   hipEvent_t attn_end;
+  /* If non-NULL, the call first writes the new tokens' rows into the cache,
+   * with exactly the effect of mla_cache_append on the same cache arrays,
+   * strides, scales and block table (which must then be writable), before
+   * any of it is read. On the bf16 / fp8-cache path the append runs in the
+   * same launch as the query absorption, saving a kernel launch per step.
+   * Errors of the append arguments are those of mla_cache_append. */
+  const mla_append_args* append;
 } mla_decode_options;
 
 /* Text for a status code (static storage; never NULL). */

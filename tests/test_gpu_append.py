@@ -2,6 +2,8 @@
 quantisation, contiguous and paged slots) and of the decode loop built on it
 (append one token, decode, repeat), against the CPU oracle."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -171,3 +173,39 @@ def test_incremental_decode_equals_causal_prefill(gpu, cache_dtype):
             worst = max(worst, rel_err_rows(got, full))
     print(f"[result] incremental decode vs causal prefill: {worst:.3e}", flush=True)
     assert worst <= (3e-2 if fp8 else 1e-2)
+
+
+@pytest.mark.parametrize("cfg,cache_dtype", [(2, "bf16"), (3, "bf16"), (2, "fp8"), (1, "f32")])
+def test_decode_with_append_equals_separate_calls(gpu, cfg, cache_dtype):
+    """A decode call given the new rows (mla_decode_options.append) writes the
+    cache exactly as mla_cache_append does and returns exactly what the decode
+    after that append returns: same cache bytes, same output and lse bits."""
+    B = 4 if cfg == 3 else 3
+    N = 300
+    lengths = torch.tensor([N, N - 37, 1, N - 5][:B], dtype=torch.int32)
+    inp = synth.make_inputs(cfg, B=B, N=N, lengths=lengths, cache_dtype=cache_dtype,
+                            paged=(cfg == 3)).to("cuda")
+    c_new, k_new = synth.append_inputs(5, B, inp.act, device="cuda")
+    pos = (inp.lengths - 1).contiguous()
+    print(f"[case] decode+append cfg={cfg} cache={cache_dtype} B={B} paged={inp.paged}",
+          flush=True)
+
+    def fresh():
+        return dataclasses.replace(inp, cache=inp.cache.clone(),
+                                   scales=None if inp.scales is None else inp.scales.clone())
+
+    sep = fresh()
+    lat, rope = gpu.split_cache(sep.cache)
+    gpu.cache_append(c_new, k_new, pos, lat, rope, heads=inp.H, scales=sep.scales,
+                     seq_capacity=inp.seq_capacity, block_table=inp.block_table,
+                     block_size=inp.block_size)
+    out_a, lse_a = gpu.decode_inputs(sep)
+    one = fresh()
+    out_b, lse_b = gpu.decode_inputs(one, append=(c_new, k_new, pos))
+    torch.cuda.synchronize()
+    assert not torch.equal(sep.cache.view(torch.uint8), inp.cache.view(torch.uint8))
+    assert torch.equal(sep.cache.view(torch.uint8), one.cache.view(torch.uint8))
+    if sep.scales is not None:
+        assert torch.equal(sep.scales, one.scales)
+    assert torch.equal(out_a.view(torch.uint8), out_b.view(torch.uint8))
+    assert torch.equal(lse_a, lse_b)
