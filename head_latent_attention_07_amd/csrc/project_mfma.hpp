@@ -15,6 +15,8 @@
 // one column.
 #pragma once
 
+#include <type_traits>
+
 #include "append.hpp"
 #include "common.hpp"
 
@@ -179,9 +181,22 @@ __global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, 
 }
 
 // ----------------------------------------------------------------------------
-// merge + W_UV: one workgroup (4 waves) per head; W_UV[h] (512 rows x 256 B)
-// is brought into LDS whole by direct-to-LDS loads while the splits of the
-// first chunk of 32 sequences are merged.
+// merge + W_UV: one workgroup of 8 waves per (head, chunk of 32 sequences);
+// the chunks of one head run on one XCD, so W_UV[h] comes from HBM once and
+// from that XCD's L2 after.
+//
+// The kernel streams 256 KB per workgroup (128 KB of fp16 partials at S = 4,
+// 128 KB of W_UV) and does a little arithmetic on it. A wave stalls while
+// its loads queue up, so the work is spread over two waves per SIMD: while
+// one waits on memory the other merges. At entry each thread issues the lse
+// and scale of its share of the first 64 splits, the partials of the first
+// group of 4 splits, its part of the W_UV DMA and the partials of the second
+// group. The merge weights 2^(lse_s - L) * scale_s / sum_s' 2^(lse_s' - L)
+// go into an LDS table [32 sequences][64 splits]; the partials are merged
+// group by group, each group loaded two groups ahead. More than 64 splits
+// are merged in chunks of 64 (the table refilled per chunk). Each half of
+// the product is split over the two wave sets by its contraction index and
+// the two accumulators are summed through LDS at the end.
 // ----------------------------------------------------------------------------
 struct CombineParams {
   const _Float16* part_o;   // [B, S, H, 512] fp16, relative to part_scale
@@ -193,12 +208,57 @@ struct CombineParams {
   int B, H, S, nbc;
 };
 
-constexpr int CB_APITCH = D_C + 16;         // 528 B: half a merged row (256 dims) + pad
+constexpr int CB_THREADS = 512;       // 8 waves
+constexpr int CB_APITCH = D_C + 16;   // 528 B: half a merged row (256 dims) + pad
+constexpr int CB_CHUNK = 64;          // splits per weight table
+constexpr int CB_G = 4;               // splits per merge group
+constexpr int CB_R = 2;               // sequences per thread in the merge
+constexpr int CB_WJ = 4;              // table entries per thread (64 splits / 16)
 
-__global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
+// Position in the merge order (half of the 512 dims, chunk of 64 splits,
+// group of 4 splits, in that nesting); s0 is the group's first split.
+struct CbUnit {
+  int half, c0, s0;
+  __device__ bool valid() const { return half < 2; }
+  __device__ void next(int S) {
+    s0 += CB_G;
+    if (s0 < min(c0 + CB_CHUNK, S)) return;
+    c0 += CB_CHUNK;
+    s0 = c0;
+    if (c0 < S) return;
+    ++half;
+    c0 = s0 = 0;
+  }
+};
+
+// Workgroup barrier for LDS hand-offs only: this workgroup's LDS writes are
+// complete and visible, outstanding global loads stay in flight (the
+// __syncthreads fences would also wait for every global load).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The partials of one group for this thread: sequences rq + 16i, dims
+// half*256 + 8*d8 .. +7, splits s0 .. s0+3. A sequence or split past the end
+// reads the last one again (unused, or weighted 0): the loads stay
+// unconditional, so the compiler's wait counts stay exact.
+__device__ __forceinline__ void cb_load(const CombineParams& p, const _Float16* const (&po)[CB_R],
+                                        const CbUnit& u, int d8, f16x8 (&v)[CB_R][CB_G]) {
+#pragma unroll
+  for (int k = 0; k < CB_G; ++k) {
+    const int64_t so = (int64_t)min(u.s0 + k, p.S - 1) * p.H * D_C + u.half * 256 + 8 * d8;
+#pragma unroll
+    for (int i = 0; i < CB_R; ++i) v[i][k] = *(const f16x8*)(po[i] + so);
+  }
+}
+
+__global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p) {
   __shared__ __attribute__((aligned(1024))) char w_lds[D_C * D_V * 2];   // 128 KB
   __shared__ __attribute__((aligned(16))) char a_lds[32 * CB_APITCH];    // 32 seq x 256 dims
-  __shared__ float lmax[32], winv[32];   // per sequence of the chunk: max lse, 1/sum of weights
+  __shared__ __attribute__((aligned(16))) float wts[32 * CB_CHUNK];      // merge weights
+  __shared__ float red[2][16][32];                                       // max, sum partials
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
@@ -207,79 +267,191 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
   {
     const int x = blockIdx.x;
     const int q_lo = x & 7, rest = x >> 3;
-    bc = rest % p.nbc;
-    head = (rest / p.nbc) * 8 + q_lo;
+    bc = __builtin_amdgcn_readfirstlane(rest % p.nbc);
+    head = __builtin_amdgcn_readfirstlane((rest / p.nbc) * 8 + q_lo);
     if (head >= p.H) return;
   }
-  {
+  const int S = p.S, b0 = bc * 32, nrows = min(32, p.B - b0);
+  // 1. Loads. Weight-table role: sequence wr, splits wp + 16j of a chunk.
+  const int wr = tid & 31, wp = tid >> 5;
+  const int wb = b0 + wr;
+  const bool wrow = wb < p.B;
+  const int64_t wrow0 = (int64_t)min(wb, p.B - 1) * S * p.H + head;
+  float lv[CB_WJ], sv[CB_WJ];
+#pragma unroll
+  for (int j = 0; j < CB_WJ; ++j) {
+    const int64_t ix = wrow0 + (int64_t)min(wp + 16 * j, S - 1) * p.H;
+    lv[j] = p.part_lse[ix];   // masked below, after the issue
+    sv[j] = p.part_scale[ix];
+  }
+  // merge role: sequences rq + 16i, dims 8*d8 .. +7 of each half
+  const int rq = tid >> 5, d8 = tid & 31;
+  const _Float16* po[CB_R];
+#pragma unroll
+  for (int i = 0; i < CB_R; ++i)
+    po[i] = p.part_o + ((int64_t)min(b0 + rq + 16 * i, p.B - 1) * S * p.H + head) * D_C;
+  auto load_w = [&]() {
     const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {   // 128 lines of 1 KB (4 rows each), 32 per wave
-      const int line = w * 32 + k;
+    for (int k = 0; k < 16; ++k) {   // 128 lines of 1 KB (4 rows each), 16 per wave
+      const int line = w * 16 + k;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(w_lds + line * 1024), 16, 16 * l,
           line * 1024, 0, 0);
     }
+    asm volatile("" ::: "memory");   // later loads stay behind the DMA
+  };
+  // The first group, W_UV, the second group, in that order; every later
+  // group is loaded two groups ahead of its merge. With S <= 4 there are
+  // just two groups (one per half) and no loop, so that each step waits
+  // only for what it reads.
+  const bool one_group = S <= CB_G;
+  f16x8 va[CB_R][CB_G], vb[CB_R][CB_G];
+  CbUnit ua{0, 0, 0};
+  CbUnit ub = ua;
+  ub.next(S);
+  CbUnit un = ub;   // the next unit to load
+  un.next(S);
+  cb_load(p, po, ua, d8, va);
+  load_w();
+  cb_load(p, po, ub, d8, vb);
+#pragma unroll
+  for (int j = 0; j < CB_WJ; ++j) {   // (kept here: the issue above does not wait for these)
+    asm volatile("" : "+v"(lv[j]));
+    lv[j] = (wrow && wp + 16 * j < S) ? lv[j] : -INFINITY;
   }
-  const int colb = 32 * w + 16 * (g16 & 1) + 4 * (jj & 3);   // B-operand column base
-  {
-    const int b0 = bc * 32;
-    // merge weights: per sequence, 2^(lse_s - L) / sum over splits
-    if (tid < 32) {
-      const int b = b0 + tid;
-      float L = -INFINITY, wsum = 0.f;
-      if (b < p.B) {
-        const float* ls = p.part_lse + (int64_t)b * p.S * p.H + head;
-        for (int s = 0; s < p.S; ++s) L = fmaxf(L, ls[(int64_t)s * p.H]);
-        if (L > -INFINITY)
-          for (int s = 0; s < p.S; ++s) wsum += fast_exp2(ls[(int64_t)s * p.H] - L);
-        if (p.lse)
-          p.lse[(int64_t)b * p.H + head] =
-              (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
+  // 2. L = max over all splits, wsum = sum of 2^(lse - L), per sequence;
+  //    the weight table of the first chunk.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < CB_WJ; ++j) mx = fmaxf(mx, lv[j]);
+  if (wrow)
+    for (int s = CB_CHUNK + wp; s < S; s += 16) mx = fmaxf(mx, p.part_lse[wrow0 + (int64_t)s * p.H]);
+  red[0][wp][wr] = mx;
+  lds_barrier();
+  float L = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) L = fmaxf(L, red[0][k][wr]);
+  float sum = 0.f;
+  if (L > -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < CB_WJ; ++j) sum += fast_exp2(lv[j] - L);
+    if (wrow)
+      for (int s = CB_CHUNK + wp; s < S; s += 16)
+        sum += fast_exp2(p.part_lse[wrow0 + (int64_t)s * p.H] - L);
+  }
+  red[1][wp][wr] = sum;
+  lds_barrier();
+  float wsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) wsum += red[1][k][wr];
+  const float inv = (L > -INFINITY && wsum > 0.f) ? 1.0f / wsum : 0.f;
+  if (wp == 0 && wrow && p.lse)
+    p.lse[(int64_t)wb * p.H + head] = (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
+#pragma unroll
+  for (int j = 0; j < CB_WJ; ++j)
+    wts[wr * CB_CHUNK + wp + 16 * j] = (inv > 0.f) ? fast_exp2(lv[j] - L) * sv[j] * inv : 0.f;
+  lds_barrier();
+
+  // 3. Merge group by group; after the last group of a half, that half of
+  //    the merged rows times the matching 256 rows of W_UV[h] (waves w and
+  //    w + 4: output columns 32(w mod 4) .. +31, contraction steps
+  //    8(w div 4) .. +7 of the half's 16).
+  int table_c0 = 0;   // the chunk whose weights are in wts
+  int issued = 1;     // groups loaded after the W_UV DMA
+  f32x8 m[CB_R];
+#pragma unroll
+  for (int i = 0; i < CB_R; ++i) m[i] = f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int colb = 32 * (w & 3) + 16 * (g16 & 1) + 4 * (jj & 3);   // B-operand column base
+  const int ks0 = 8 * (w >> 2);
+  f32x16 acc = f32x16{};
+  auto merge = [&](const CbUnit& u, const f16x8 (&v)[CB_R][CB_G], auto looped) {
+    if (looped && u.c0 != table_c0) {   // weights of another chunk of splits (S > 64)
+      lds_barrier();                    // the table in use is no longer read
+#pragma unroll
+      for (int j = 0; j < CB_WJ; ++j) {
+        const int s = u.c0 + wp + 16 * j;
+        const int64_t ix = wrow0 + (int64_t)min(s, S - 1) * p.H;
+        const float x = (wrow && s < S) ? p.part_lse[ix] : -INFINITY;
+        wts[wr * CB_CHUNK + wp + 16 * j] = (inv > 0.f) ? fast_exp2(x - L) * p.part_scale[ix] * inv : 0.f;
       }
-      winv[tid] = (L > -INFINITY) ? 1.0f / wsum : 0.0f;
-      lmax[tid] = L;
+      lds_barrier();
+      table_c0 = u.c0;
     }
-    __syncthreads();
-    f32x16 acc = f32x16{};
-    for (int half = 0; half < 2; ++half) {
-      // thread: dims half*256 + 8*(tid%32) .. +7 of sequences b0 + tid/32 + 8i
-      const int d8 = tid & 31;
+    const int g = u.s0 - u.c0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 5) + 8 * i;
-        const int b = b0 + r;
-        f32x8 m = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (b < p.B && winv[r] > 0.f) {
-          const float L = lmax[r];
-          const int64_t row0 = (int64_t)b * p.S * p.H + head;
-          const _Float16* po = p.part_o + row0 * D_C + half * 256 + 8 * d8;
-#pragma unroll 4
-          for (int s = 0; s < p.S; ++s) {
-            const int64_t rs_ = row0 + (int64_t)s * p.H;
-            const float wgt = fast_exp2(p.part_lse[rs_] - L) * p.part_scale[rs_];
-            const f16x8 v = *(const f16x8*)(po + (int64_t)s * p.H * D_C);
+    for (int i = 0; i < CB_R; ++i) {
+      if (rq + 16 * i < nrows) {
+        const f32x4 w4 = *(const f32x4*)(wts + (rq + 16 * i) * CB_CHUNK + g);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) m[k] += wgt * (float)v[k];
-          }
-          m *= winv[r];
-        }
-        bf16x8 pk;
+        for (int k = 0; k < CB_G; ++k)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pk[k] = (bf16)m[k];
-        *(bf16x8*)(a_lds + r * CB_APITCH + 16 * d8) = pk;
+          for (int e = 0; e < 8; ++e) m[i][e] += w4[k] * (float)v[i][k][e];
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UV landed (first pass)
-      __syncthreads();
-#pragma unroll 4
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(a_lds + l32 * CB_APITCH + 2 * (16 * ks + 8 * h));
-        const int ra = half * 256 + 16 * ks + 8 * h + (jj >> 2);
-        const bf16x8 bop = tr_read_8(w_lds + ra * 256 + 2 * colb, w_lds + (ra + 4) * 256 + 2 * colb);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
-      }
-      __syncthreads();   // a_lds is rewritten next
     }
+    if (looped) {
+      CbUnit nx = u;
+      nx.next(S);
+      if (nx.half == u.half) return;
+    }
+#pragma unroll
+    for (int i = 0; i < CB_R; ++i) {
+      bf16x8 pk;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pk[k] = (bf16)m[i][k];
+      *(bf16x8*)(a_lds + (rq + 16 * i) * CB_APITCH + 16 * d8) = pk;
+      m[i] = f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    }
+    // W_UV has landed once at most the groups loaded after it are pending:
+    // they are the youngest loads, at most two groups of 8 (before the
+    // half-0 product without the loop: the 8 of the half-1 group)
+    if (issued >= 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (u.half == 0)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+#pragma unroll
+    for (int ks = ks0; ks < ks0 + 8; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(a_lds + l32 * CB_APITCH + 2 * (16 * ks + 8 * h));
+      const int ra = u.half * 256 + 16 * ks + 8 * h + (jj >> 2);
+      const bf16x8 bop = tr_read_8(w_lds + ra * 256 + 2 * colb, w_lds + (ra + 4) * 256 + 2 * colb);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+    }
+    lds_barrier();   // a_lds is rewritten next
+  };
+  if (one_group) {
+    merge(ua, va, std::false_type{});
+    merge(ub, vb, std::false_type{});
+  } else {
+    // units alternate between the buffers va and vb (named at compile
+    // time); after a unit is merged its buffer takes the unit two on
+    while (ua.valid()) {
+      merge(ua, va, std::true_type{});
+      ua = un;
+      if (un.valid()) {
+        cb_load(p, po, un, d8, va);
+        un.next(S);
+        ++issued;
+      }
+      if (!ub.valid()) break;
+      merge(ub, vb, std::true_type{});
+      ub = un;
+      if (un.valid()) {
+        cb_load(p, po, un, d8, vb);
+        un.next(S);
+        ++issued;
+      }
+    }
+  }
+  // 4. Sum the two contraction halves (waves w + 4 hand theirs to wave w
+  //    through the now unused a_lds) and store.
+  f32x16* const xch = (f32x16*)a_lds + ((w & 3) * 64 + l);
+  if (w >= 4) *xch = acc;
+  lds_barrier();
+  if (w < 4) {
+    acc += *xch;
     const int n = 32 * w + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

@@ -72,6 +72,15 @@ def test_split_invariance(gpu, splits):
     run_and_compare(gpu, inp, "bf16", num_splits=splits)
 
 
+@pytest.mark.parametrize("N,splits", [(2240, 70), (4096, 128)])
+def test_many_splits(gpu, N, splits):
+    """More than 64 splits: the merge takes its weights 64 splits at a time
+    (70 = one chunk of 64 and a chunk of 6 with a partial group of 4)."""
+    lengths = torch.tensor([N, N - 700, 33], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=3, N=N, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16", num_splits=splits)
+
+
 def test_paged_equals_contiguous_bitwise(gpu):
     """Block-table indexing is exact: the same rows, placed in a permuted
     pool of 64-token blocks, give bit-identical outputs under the same split
