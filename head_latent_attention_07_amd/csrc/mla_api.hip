@@ -330,8 +330,8 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   MLA_TRY(launch_status());
 
   CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(ceil_div(H, 8) * 8 * nbc), dim3(CB_THREADS), 0, stream,
-                     cp);
+  hipLaunchKernelGGL(pl.S <= CB_G ? mla_combine_s4_kernel : mla_combine_kernel,
+                     dim3(ceil_div(H, 8) * 8 * nbc), dim3(CB_THREADS), 0, stream, cp);
   return launch_status();
 }
 

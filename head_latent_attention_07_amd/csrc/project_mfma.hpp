@@ -461,4 +461,147 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
   }
 }
 
+// ----------------------------------------------------------------------------
+// merge + W_UV for S <= 4 splits (the many-sequence case), same grid and
+// work split as above but without the weight table and the A staging: wave
+// w owns dims 32w .. 32w+31 of each half of the latent, lane l the sequence
+// l mod 32. A lane computes its sequence's weights from the (at most 4)
+// split lse values itself, merges its 16 dims of each half straight into
+// the MFMA A operand, and multiplies them by the 64 rows of W_UV[h] it
+// loaded into LDS itself, for all 128 output columns. The 8 waves' partial
+// products are summed through LDS (the W_UV buffer, free by then).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParams p) {
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_C * D_V * 2];   // 128 KB
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
+  int head, bc;
+  {
+    const int x = blockIdx.x;
+    const int q_lo = x & 7, rest = x >> 3;
+    bc = __builtin_amdgcn_readfirstlane(rest % p.nbc);
+    head = __builtin_amdgcn_readfirstlane((rest / p.nbc) * 8 + q_lo);
+    if (head >= p.H) return;
+  }
+  const int S = p.S, b = bc * 32 + l32;
+  const bool brow = b < p.B;
+  const int64_t row0 = (int64_t)min(b, p.B - 1) * S * p.H + head;   // (b, split 0, head)
+  // loads: lse and scale, half-0 partials, this wave's W_UV rows, half-1
+  // partials (v[half][step][split]: dims 256 half + 32 w + 16 step + 8 h)
+  float lv[CB_G], sv[CB_G];
+#pragma unroll
+  for (int s = 0; s < CB_G; ++s) {
+    const int64_t ix = row0 + (int64_t)min(s, S - 1) * p.H;
+    lv[s] = p.part_lse[ix];
+    sv[s] = p.part_scale[ix];
+  }
+  f16x8 v[2][2][CB_G];
+  auto load_half = [&](int hf) {
+#pragma unroll
+    for (int s = 0; s < CB_G; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        v[hf][t][s] = *(const f16x8*)(p.part_o + (row0 + (int64_t)min(s, S - 1) * p.H) * D_C +
+                                      256 * hf + 32 * w + 16 * t + 8 * h);
+  };
+  load_half(0);
+  {
+    // rows 256 hf + 32 w .. +31 of W_UV[h] (8 KB per half) to the same
+    // rows of the LDS copy, 4 rows per 1 KB load
+    const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int line = (k >> 3) * 64 + 8 * w + (k & 7);   // line = 4 rows
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(w_lds + line * 1024), 16, 16 * l,
+          line * 1024, 0, 0);
+    }
+    asm volatile("" ::: "memory");   // later loads stay behind the DMA
+  }
+  load_half(1);
+  // weights of this lane's sequence
+  float L = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < CB_G; ++s) {
+    lv[s] = (brow && s < S) ? lv[s] : -INFINITY;
+    L = fmaxf(L, lv[s]);
+  }
+  float e[CB_G], wsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < CB_G; ++s) {
+    e[s] = (L > -INFINITY) ? fast_exp2(lv[s] - L) : 0.f;
+    wsum += e[s];
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  float wt[CB_G];
+#pragma unroll
+  for (int s = 0; s < CB_G; ++s) wt[s] = e[s] * sv[s] * inv;
+  if (w == 0 && h == 0 && brow && p.lse)
+    p.lse[(int64_t)b * p.H + head] = (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
+  const int colb0 = 16 * (g16 & 1) + 4 * (jj & 3);   // + 32 cb: B-operand column base
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    bf16x8 a[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < CB_G; ++s)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m[k] += wt[s] * (float)v[hf][t][s][k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[t][k] = (bf16)m[k];
+    }
+    // this wave's W_UV rows have landed once only the 8 half-1 loads, which
+    // follow them, may be pending
+    if (hf == 0) {
+      __builtin_amdgcn_sched_barrier(0);   // the half-0 merge stays ahead of the wait
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int ra = 256 * hf + 32 * w + 16 * t + 8 * h + (jj >> 2);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int colb = 32 * cb + colb0;
+        const bf16x8 bop = tr_read_8(w_lds + ra * 256 + 2 * colb, w_lds + (ra + 4) * 256 + 2 * colb);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], bop, acc[cb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // half 1 waits for its loads only after this
+  }
+  // sum over the 8 waves: wave w' stores acc[cb] registers 4 r4 .. 4 r4 + 3
+  // of lane l at f32x4 slot ((w' * 4 + cb) * 4 + r4) * 64 + l; wave w then
+  // adds up column block w / 2, registers 8 (w mod 2) .. +7
+  lds_barrier();   // every wave is done with W_UV
+  f32x4* const xch = (f32x4*)w_lds;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      xch[((w * 4 + cb) * 4 + r4) * 64 + l] =
+          f32x4{acc[cb][4 * r4], acc[cb][4 * r4 + 1], acc[cb][4 * r4 + 2], acc[cb][4 * r4 + 3]};
+  lds_barrier();
+  const int cb = w >> 1, rg = w & 1;
+  f32x4 sum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ww = 0; ww < 8; ++ww)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) sum[q] += xch[((ww * 4 + cb) * 4 + 2 * rg + q) * 64 + l];
+  const int n = 32 * cb + l32;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 4 * (2 * rg + q) + c;   // accumulator register
+      const int bb = bc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)sum[q][c];
+    }
+}
+
 }  // namespace mla
