@@ -863,6 +863,8 @@ __device__ __forceinline__ void write_empty(const WorkItem& wi, int h) {
 // 256-byte row segments. `scr` is PART_SCR_BYTES of LDS owned by this wave.
 constexpr int PART_ROW = 2 * 128 + 16;
 constexpr int PART_SCR_BYTES = 32 * PART_ROW;   // 8704
+constexpr int FLAG_OFF = 2 * PART_SCR_BYTES;     // overflow flags in a tile buffer
+static_assert(FLAG_OFF + 64 <= TILE_BYTES, "flags fit in a tile buffer");
 
 __device__ __forceinline__ void write_partial(const WorkItem& wi, const WaveState& st, int h,
                                               int l, char* scr) {
@@ -927,7 +929,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_bf16_kernel(DecodeParams p) {
   // four tile buffers and the RoPE k-steps of the queries (160 KB with four
   // waves); the split's block table and the waves' overflow flags borrow tile
-  // buffer space while it is idle (the prologue, the end of a pass)
+  // buffer space while it is idle (the prologue; the end of a pass, in the
+  // buffer after the last tile's, past the partial-output staging)
   __shared__ __attribute__((aligned(1024))) char bufs[4 * TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
   constexpr int NT = 64 * NW;
@@ -937,7 +940,6 @@ void mla_decode_bf16_kernel(DecodeParams p) {
   char* const buf2 = bufs + 2 * TILE_BYTES;
   char* const buf3 = bufs + 3 * TILE_BYTES;
   int* const blk_tab = (int*)buf3;   // prologue only (tile 3 is loaded after it is read)
-  int* const flags = (int*)buf0;     // end of a pass only (no load in flight, no reader)
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -1047,12 +1049,13 @@ void mla_decode_bf16_kernel(DecodeParams p) {
       pipe_step<false, true, false>(nullptr, bufs + (last & 3) * TILE_BYTES, 0, wi.t1, qreg, qpe,
                                     la, h, st, sl, sl, pb, pring, [](int, int) {});
     }
-    // every load has landed and every wave is past its last LDS read: the
-    // waves' overflow flags go through buffer 0
+    // The waves' overflow flags go through the buffer after the last tile's
+    // (no step reads it; the loads of the tiles past the end, which write
+    // zeros there, are drained first), past the bytes write_partial stages
+    // in. After the one barrier every wave is also done reading tiles.
     const bool ovf = split_overflowed(st);
+    int* const flags = (int*)(bufs + (ntiles & 3) * TILE_BYTES + FLAG_OFF);
     wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
     if (l == 0) flags[w] = ovf ? 1 : 0;
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
@@ -1061,10 +1064,10 @@ void mla_decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) any_ovf |= flags[i];
     any_ovf = __builtin_amdgcn_readfirstlane(any_ovf);
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
     if (any_ovf == 0) break;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();   // every wave has read the flags
+    compiler_fence();
 
     // Rare path: a weight reached 2^64 against the first tile's max (or the
     // sum is NaN). Drain the loads in flight, find each head's true maximum
@@ -1086,11 +1089,8 @@ void mla_decode_bf16_kernel(DecodeParams p) {
     }
     reset_state(st, mtrue);
   }
-  // loads of tiles past the end may still be landing in any buffer, and other
-  // waves may still read the last tile: drain both before reusing the LDS
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
+  // (every load has landed and every wave is past its last tile read: the
+  // flag exchange above ended with both)
   write_partial(wi, st, h, l, (w < 2 ? buf0 : buf1) + (w & 1) * PART_SCR_BYTES);
 }
 
