@@ -30,10 +30,11 @@
 //     2^64 is recomputed against its true max.
 //   * bf16 cache: a cross-tile software pipeline (pipe_step) interleaves the
 //     PV of tile j-1 with the S^T of tile j in one stream of MFMAs.
-//   * fp8 cache: raw e4m3 tiles are staged in LDS and widened (exactly) to
-//     the bf16 tile layout; the per-row scale multiplies the row's scores
-//     and, after the softmax sum, its weights, so both MFMAs see exact
-//     e4m3 values.
+//   * fp8 cache: the same pipeline over tiles widened (exactly) to the bf16
+//     tile layout: each lane widens the raw e4m3 pieces its own loads
+//     staged, in the step's early MFMA slots; the per-row scale multiplies
+//     the row's scores and, after the softmax sum, its weights, so both
+//     MFMAs see exact e4m3 values.
 //   * each split writes its normalised partial O (fp16 relative to the row
 //     max, with the fp32 factor) and its log2 sum-exp; a separate kernel
 //     merges the splits and applies W_UV.
@@ -235,79 +236,6 @@ __device__ __forceinline__ float tile_scores(const char* tile, const float* scal
   return pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
 }
 
-// One 32-token tile: scores, softmax weights against m_ref, O^T += C^T P^T.
-// With FIRST (the split's first tile) an unset reference (-inf) becomes the
-// tile's max. The weights of the first 16 tokens (B operand of the first 16
-// PV MFMAs) are computed before the PV chain, those of the last 16 between
-// its first MFMAs, where the vector ALU work overlaps the matrix pipe.
-// `issue(t)` runs after MFMA t of the tile's 68 (36 for S, 32 for PV).
-// Scores far above the reference are caught once per split, from the sum
-// of the weights (see split_overflowed).
-template <int CK, bool FIRST, typename Issue>
-__device__ __forceinline__ void tile_compute(const char* tile, const float* scale, int tile_t0,
-                                             int t1, const bf16x8 (&qreg)[QREG],
-                                             const bf16x8 (&qpe)[QLDS], const LaneAddr& la, int h,
-                                             WaveState& st,
-                                             const Issue& issue) {
-  float sv[16];
-  const float tmax = tile_scores<CK, FIRST>(tile, scale, tile_t0, t1, qreg, qpe, la, h, sv, issue);
-  // PV operands: 32 steps (2 k-steps x 16 dim tiles), two ahead
-  constexpr int NS = 32, AHEAD = 2;
-  auto v_op = [&](int s) {
-    const int ks = s >> 4, dt = s & 15;
-    const int off = 256 * (dt >> 2) + ks * 16 * LAT_ROW;
-    return lds_tr8(tile + la.tb[0][dt & 3] + off, tile + la.tb[1][dt & 3] + off);
-  };
-  bf16x8 ring[AHEAD + 1];
-#pragma unroll
-  for (int s = 0; s < AHEAD; ++s) ring[s] = v_op(s);
-  if (FIRST) st.m_ref = (st.m_ref == -INFINITY) ? tmax : st.m_ref;
-  const float mref = st.m_ref;
-  f32x4 sc4[4];
-  if (CK == CACHE_FP8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc4[i] = *(const f32x4*)(scale + 8 * i + 4 * h);
-  }
-  // weights in place of the scores; the sum of the tile's 16 weights of this
-  // lane as a pairwise tree per half, pinned where it is formed (the
-  // compiler would otherwise sink a serial chain of adds past the PV chain)
-  auto weights = [&](int r0) {
-#pragma unroll
-    for (int r = r0; r < r0 + 8; ++r) sv[r] = fast_exp2(sv[r] - mref);
-    float half = ((sv[r0] + sv[r0 + 1]) + (sv[r0 + 2] + sv[r0 + 3])) +
-                 ((sv[r0 + 4] + sv[r0 + 5]) + (sv[r0 + 6] + sv[r0 + 7]));
-    asm volatile("" : "+v"(half));
-    st.lsum += half;
-  };
-  auto pbf = [&](int r) {
-    return (CK == CACHE_FP8) ? (bf16)(sv[r] * sc4[r >> 2][r & 3]) : (bf16)sv[r];
-  };
-  bf16x8 pb[2];
-  weights(0);
-#pragma unroll
-  for (int r = 0; r < 8; ++r) pb[0][r] = pbf(r);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (s + AHEAD < NS) ring[(s + AHEAD) % (AHEAD + 1)] = v_op(s + AHEAD);
-    const int dt = s & 15;
-    st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % (AHEAD + 1)], pb[s >> 4], st.o[dt], 0, 0, 0);
-    // second half of the weights, a little per MFMA: exps, sum, packing
-    if (s < 8) sv[8 + s] = fast_exp2(sv[8 + s] - mref);
-    if (s == 8) {
-      float half = ((sv[8] + sv[9]) + (sv[10] + sv[11])) + ((sv[12] + sv[13]) + (sv[14] + sv[15]));
-      asm volatile("" : "+v"(half));
-      st.lsum += half;
-    }
-    if (s >= 9 && s < 13) {
-      pb[1][2 * (s - 9)] = pbf(8 + 2 * (s - 9));
-      pb[1][2 * (s - 9) + 1] = pbf(9 + 2 * (s - 9));
-    }
-    issue(36 + s);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // Every weight of a split is 2^(score - m_ref) <= its lane's share of the
 // softmax denominator, so a share below 2^64 bounds every weight (and the
 // accumulators) far from fp32 and bf16 overflow. A share at or above it
@@ -361,12 +289,17 @@ constexpr int slot_q_index(int t, int nq, int np) {
 // while its K operands are read, and the matrix pipe stays fed through the
 // softmax and across step boundaries. The first step only computes S^T,
 // the last only PV. `issue(t, n)` runs after slot t of the step's n.
-template <bool DO_QK, bool DO_PV, bool K_FIRST, typename Issue>
+// SCALED (fp8 cache, tiles holding the widened codes): `kscl` / `vscl` are
+// the row scales of the S^T tile and of the PV tile (LDS); a row's scale
+// multiplies its scores and, after the softmax sums, its weights.
+template <bool DO_QK, bool DO_PV, bool K_FIRST, bool SCALED = false, typename Issue>
 __device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_t0, int t1,
                                           const bf16x8 (&qreg)[QREG], const char* qpe,
                                           const LaneAddr& la, int h, WaveState& st,
                                           f32x16& sn, f32x16& sp, bf16x8 (&pb)[2],
-                                          bf16x8 (&pring)[3], const Issue& issue) {
+                                          bf16x8 (&pring)[3], const Issue& issue,
+                                          const float* kscl = nullptr,
+                                          const float* vscl = nullptr) {
   constexpr int NQ = DO_QK ? D_QK / 16 : 0, NP = DO_PV ? 32 : 0, NSLOT = NQ + NP;
   constexpr int QA = 2, PA = 2;   // LDS read lookahead, in MFMAs of each chain
   auto a_off = [&](int j) { return (j < 32) ? la.qb[j & 7] + 256 * (j >> 3) : la.rb[j - 32]; };
@@ -393,9 +326,24 @@ __device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_
     pb[r >> 3][r & 7] = (bf16)v[r];
     pb[r >> 3][(r & 7) + 1] = (bf16)v[r + 1];
   };
+  // register r of a score / weight fragment is token row 8(r/4) + 4h + r%4:
+  // rows 4h + 0..3 + 8i are the f32x4 at 8i + 4h of the tile's scales
+  f32x4 ksc[4], vsc[2];
+  auto load_ksc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ksc[i] = *(const f32x4*)(kscl + 8 * i + 4 * h);
+  };
+  auto pack_scaled = [&](const f32x16& v, int r, const f32x4& sc) {   // rows r, r+1 (r even)
+    pb[r >> 3][r & 7] = (bf16)(v[r] * sc[r & 3]);
+    pb[r >> 3][(r & 7) + 1] = (bf16)(v[r + 1] * sc[(r & 3) + 1]);
+  };
   // after the S^T chain (sn settled): mask, reference, first-half weights
   float mref_k = 0.f;
   auto softmax_head = [&]() {
+    if constexpr (SCALED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[r] *= ksc[r >> 2][r & 3];
+    }
     if (k_t0 + TILE > t1) {   // wave-uniform: the split's last tile only
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -438,12 +386,22 @@ __device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_
       // second half of tile j-1's weights
       if constexpr (pi < 8) sp[8 + pi] = fast_exp2(sp[8 + pi] - mref_pv);
       if constexpr (pi == 8) half_sum(sp, 8);
-      if constexpr (pi >= 9 && pi < 13) pack(sp, 8 + 2 * (pi - 9));
+      if constexpr (SCALED && pi == 4) {
+        vsc[0] = *(const f32x4*)(vscl + 16 + 4 * h);
+        vsc[1] = *(const f32x4*)(vscl + 24 + 4 * h);
+      }
+      if constexpr (pi >= 9 && pi < 13) {
+        if constexpr (SCALED)
+          pack_scaled(sp, 8 + 2 * (pi - 9), vsc[(pi - 9) >> 1]);
+        else
+          pack(sp, 8 + 2 * (pi - 9));
+      }
     }
     // tile j's softmax head over the tail slots, and its first PV operands
     // once the last two PV MFMAs have read the ring entries they replace
     if constexpr (DO_QK && DO_PV) {
       constexpr int u = t - (HEAD_AT - 1);   // 0 at the chain's last slot
+      if constexpr (SCALED && u == -4) load_ksc();
       if constexpr (u == 0) softmax_head();
       if constexpr (u >= 0 && u < 4) {
         sn[2 * u] = fast_exp2(sn[2 * u] - mref_k);
@@ -452,7 +410,12 @@ __device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_
       if constexpr (u == 3) {
         half_sum(sn, 0);
 #pragma unroll
-        for (int r = 0; r < 8; r += 2) pack(sn, r);
+        for (int r = 0; r < 8; r += 2) {
+          if constexpr (SCALED)
+            pack_scaled(sn, r, ksc[r >> 2]);
+          else
+            pack(sn, r);
+        }
       }
       if constexpr (t == NSLOT - 2) pring[0] = v_op(kt, 0);
       if constexpr (t == NSLOT - 1) pring[1] = v_op(kt, 1);
@@ -461,12 +424,18 @@ __device__ __forceinline__ void pipe_step(const char* kt, const char* vt, int k_
     __builtin_amdgcn_sched_barrier(0);
   });
   if constexpr (DO_QK && !DO_PV) {   // S^T-only step: the head after the chain
+    if constexpr (SCALED) load_ksc();
     softmax_head();
 #pragma unroll
     for (int r = 0; r < 8; ++r) sn[r] = fast_exp2(sn[r] - mref_k);
     half_sum(sn, 0);
 #pragma unroll
-    for (int r = 0; r < 8; r += 2) pack(sn, r);
+    for (int r = 0; r < 8; r += 2) {
+      if constexpr (SCALED)
+        pack_scaled(sn, r, ksc[r >> 2]);
+      else
+        pack(sn, r);
+    }
     pring[0] = v_op(kt, 0);
     pring[1] = v_op(kt, 1);
   }
@@ -769,48 +738,6 @@ __device__ __forceinline__ Fp8Load<NW> fp8_load(const DecodeParams& p, char* sta
   return t;
 }
 
-// Widen one staged tile into a bf16 tile (all NT threads of the workgroup):
-// e4m3 codes convert to bf16 exactly; the row scales are applied in the
-// attention math (to the scores and to the weights).
-template <int NT>
-__device__ __forceinline__ void fp8_tile_widen(const char* stage, char* tile, int tid) {
-  constexpr int CHUNKS = TILE * (D_QK / 16);  // 1152 chunks of 16 codes
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-  for (int i = 0; i < (CHUNKS + NT - 1) / NT; ++i) {
-    const int q = i * NT + tid;
-    if (CHUNKS % NT == 0 || q < CHUNKS) {
-      int row, c;
-      const char* src;
-      char* dst;
-      if (q < TILE * (D_C / 16)) {
-        row = q >> 5;
-        c = q & 31;
-        src = stage + q * 16;
-        dst = tile + row * LAT_ROW;
-      } else {
-        const int qq = q - TILE * (D_C / 16);
-        row = qq >> 2;
-        c = qq & 3;
-        src = stage + STG_ROPE + qq * 16;
-        dst = tile + ROPE_OFF + row * ROPE_ROW;
-      }
-      const u32x4 v = *(const u32x4*)src;
-      u32x4 lo, hi;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, false));
-        lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, true));
-        hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, false));
-        hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, true));
-      }
-      const int sw = (q < TILE * (D_C / 16)) ? lat_swz(row) : rope_swz(row);
-      *(u32x4*)(dst + 16 * ((2 * c) ^ sw)) = lo;
-      *(u32x4*)(dst + 16 * ((2 * c + 1) ^ sw)) = hi;
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // Common prologue: work item of this workgroup, the empty-split case, the
 // absorbed queries of this lane's head.
@@ -1095,21 +1022,105 @@ void mla_decode_bf16_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8 cache: the codes of tile k+1 are staged in LDS by DMA while tile k is
-// computed, then widened to bf16 into the other tile buffer
+// fp8 cache, pipelined: the bf16 kernel's cross-tile pipeline (pipe_step,
+// SCALED) over tiles widened to bf16 in LDS. Tile t lives in bf16 buffer
+// t mod 3: step j reads tile j (S^T) and tile j-1 (PV) and widens tile j+1
+// into the third buffer, which step j-1 finished reading. The raw codes of
+// one tile at a time wait in a staging tile, filled by the direct-to-LDS
+// loads of Fp8Load: every lane widens exactly the 16-byte pieces its own
+// loads wrote there, so as soon as its reads are done it loads the next
+// tile's codes into the same bytes, with no barrier. The widening runs in
+// the step's early MFMA slots, the next tile's loads right after it (they
+// then have the rest of the step and the next step's first slots to land).
+// The row scales of the split sit in LDS; pipe_step applies them to the
+// scores and the weights (SCALED).
 // ---------------------------------------------------------------------------
+
+// Widen piece I (a 16-byte chunk of 16 codes) of this lane's share of a
+// staged tile into a bf16 tile (e4m3 codes are exact in bf16; the row scales
+// are applied in the attention math). Latent pieces I < LAT (row
+// 2(w LAT + I) + l/32, codes 16 (l mod 32) ..), RoPE piece I = LAT (row
+// 16 pc + l/4, codes 16 (l mod 4) .., only on the waves whose RoPE loads are
+// real).
+template <int NW, int I>
+__device__ __forceinline__ void widen_own_piece(const char* stg, char* tile, int w, int l) {
+  constexpr int LAT = Fp8Load<NW>::LAT, ROPE = Fp8Load<NW>::ROPE;
+  // addresses are recomputed at each use (a few ALU operations): kept live
+  // across the loop they would not fit in the registers
+  asm volatile("" : "+v"(l));
+  const char* src;
+  char* row_base;
+  int c, sw;
+  if constexpr (I < LAT) {
+    const int row = 2 * (w * LAT + I) + (l >> 5);
+    c = l & 31;
+    sw = lat_swz(row);
+    src = stg + (w * LAT + I) * 1024 + 16 * l;
+    row_base = tile + row * LAT_ROW;
+  } else {
+    const int pc = w * ROPE + (I - LAT);
+    const int row = 16 * pc + (l >> 2);
+    c = l & 3;
+    sw = rope_swz(row);
+    src = stg + STG_ROPE + pc * 1024 + 16 * l;
+    row_base = tile + ROPE_OFF + row * ROPE_ROW;
+  }
+  const u32x4 v = *(const u32x4*)src;
+  u32x4 lo, hi;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, false));
+    lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], 1.0f, true));
+    hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, false));
+    hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j + 2], 1.0f, true));
+  }
+  // the read has returned before anything after this point (the next
+  // tile's loads into the same staging bytes) is issued
+  asm volatile("" ::"v"(lo[0]), "v"(hi[0]));
+  *(u32x4*)(row_base + 16 * ((2 * c) ^ sw)) = lo;
+  *(u32x4*)(row_base + 16 * ((2 * c + 1) ^ sw)) = hi;
+}
+
+// Every piece of this lane's share (the RoPE piece only where it is real).
+template <int NW, int... I>
+__device__ __forceinline__ void widen_own_all_(const char* stg, char* tile, int w, int l,
+                                               bool rope_real, std::integer_sequence<int, I...>) {
+  ((I < Fp8Load<NW>::LAT || rope_real ? widen_own_piece<NW, I>(stg, tile, w, l) : void()), ...);
+}
+template <int NW>
+__device__ __forceinline__ void widen_own_all(const char* stg, char* tile, int w, int l,
+                                              bool rope_real) {
+  widen_own_all_<NW>(stg, tile, w, l, rope_real,
+                     std::make_integer_sequence<int, Fp8Load<NW>::PIECES>{});
+}
+// The same, piece I after MFMA slot 2 + 3 I of a step.
+constexpr int WIDEN_SLOT0 = 2, WIDEN_EVERY = 3;
+constexpr int fp8_load_slot(int pieces) { return WIDEN_SLOT0 + WIDEN_EVERY * pieces; }
+template <int NW, int... I>
+__device__ __forceinline__ void widen_own_at_(int t, const char* stg, char* tile, int w, int l,
+                                              bool rope_real, std::integer_sequence<int, I...>) {
+  ((t == WIDEN_SLOT0 + WIDEN_EVERY * I && (I < Fp8Load<NW>::LAT || rope_real)
+        ? widen_own_piece<NW, I>(stg, tile, w, l)
+        : void()),
+   ...);
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * NW;
-  constexpr int P = Fp8Load<NW>::PIECES;   // wave-wide loads per tile per wave
-  // raw fp8 tiles k+1 .. k+3 in three stages, bf16 tiles k, k+1 in two buffers
-  __shared__ __attribute__((aligned(1024))) char stage[3][STG_BYTES];
-  __shared__ __attribute__((aligned(1024))) char tbuf[2][TILE_BYTES];
+  constexpr int P = Fp8Load<NW>::PIECES;
+  constexpr int LOAD_SLOT = fp8_load_slot(P);   // after the widening's last piece
+  __shared__ __attribute__((aligned(1024))) char bufs[3 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qpe_all[NW * QLDS * 1024];
+  __shared__ __attribute__((aligned(1024))) char stage[STG_BYTES];
   __shared__ __attribute__((aligned(1024))) char dummy[1024];
-  __shared__ float scl_all[64 * TILE];   // row scales of the split, tile i at 32 i
+  __shared__ __attribute__((aligned(16))) float scl_all[64 * TILE];   // tile i at 32 i
   __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
-  __shared__ int overflow;
+  __shared__ int flags[NW];
+  char* const buf0 = bufs;
+  char* const buf1 = bufs + TILE_BYTES;
+  char* const buf2 = bufs + 2 * TILE_BYTES;
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -1120,33 +1131,34 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     return;
   }
   const int ntiles = (wi.t1 - wi.t0 + TILE - 1) / TILE;
+  const bool rope_real = w * Fp8Load<NW>::ROPE < 2;   // wave-uniform
   int voff[P];
   fp8_piece_offsets<NW>(p, w, l, voff);
   auto nvalid = [&](int k) { return min(max(wi.t1 - (wi.t0 + k * TILE), 0), TILE); };
   int trow = 0;   // lane i: physical row of tile i's first token (set in the prologue)
-  auto load = [&](int k) {
-    return fp8_load<NW>(p, stage[k % 3], dummy,
-                        __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)), nvalid(k), w, voff);
+  auto load_raw = [&](char* stg, int k) {
+    return fp8_load<NW>(p, stg, dummy, __builtin_amdgcn_readlane(trow, min(k, ntiles - 1)),
+                        nvalid(k), w, voff);
   };
 
-  // Prologue (a tile's loads write all its staging bytes, zeros past the
-  // split's end, so nothing is cleared): raw tiles 0..2 (block entries on the
-  // scalar path), the queries, the split's block table; one wait; then the
-  // per-tile rows and the scales of the whole split; widen tile 0.
-#pragma unroll
-  for (int k = 0; k < 3; ++k)
-    fp8_load<NW>(p, stage[k], dummy,
-                 (int)tile_base_row_direct(p, wi.b, wi.t0 + min(k, ntiles - 1) * TILE), nvalid(k),
-                 w, voff)
-        .all();
-  bf16x8 qreg[QREG], qpe[QLDS];
-  load_q(p, wi, l, qreg, qpe);
+  // Prologue: raw tile 0 into the staging tile, raw tile 1 into buffer 2
+  // (idle until step 1 widens tile 2 into it), the queries, the block table;
+  // one wait; the RoPE query k-steps and the split's row scales into LDS;
+  // tile 0 widened into buffer 0.
+  fp8_load<NW>(p, stage, dummy, (int)tile_base_row_direct(p, wi.b, wi.t0), nvalid(0), w, voff).all();
+  fp8_load<NW>(p, buf2, dummy, (int)tile_base_row_direct(p, wi.b, wi.t0 + min(1, ntiles - 1) * TILE),
+               nvalid(1), w, voff)
+      .all();
+  bf16x8 qreg[QREG], qtmp[QLDS];
+  load_q(p, wi, l, qreg, qtmp);
   load_block_table<NT>(p, wi.b, wi.t0, wi.t1, blk_tab, tid);
+  char* const qpe = qpe_all + w * (QLDS * 1024) + 16 * l;   // this lane's RoPE query slot
   const LaneAddr la = lane_addr(l);
   WaveState st;
   reset_state(st, -INFINITY);
-  if (tid == 0) overflow = 0;
   wait_vm_lgkm0<0>();
+#pragma unroll
+  for (int j = 0; j < QLDS; ++j) *(bf16x8*)(qpe + 1024 * j) = qtmp[j];
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   trow = tile_rows_lanes(p, wi.b, wi.t0, wi.t1, blk_tab, first_blk_of(p, wi.t0), l);
@@ -1157,77 +1169,118 @@ void mla_decode_fp8_kernel(DecodeParams p) {
     row = (row >= 0 && row < p.rows) ? row : 0;
     scl_all[i] = (float)p.scales[row];
   }
-  fp8_tile_widen<NT>(stage[0], tbuf[0], tid);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();   // every row scale is in LDS before any is read
+  compiler_fence();
+  widen_own_all<NW>(stage, buf0, w, l, rope_real);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
 
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (attempt > 0) {
-#pragma unroll
-      for (int k = 0; k < 3; ++k) load(k).all();
-      wait_vm_lgkm0<0>();   // raw tiles 0..2 landed (rare path: no overlap needed)
-      __builtin_amdgcn_s_barrier();
-      compiler_fence();
-      fp8_tile_widen<NT>(stage[0], tbuf[0], tid);
+      load_raw(stage, 0).all();
+      load_raw(buf2, 1).all();
+      wait_vm_lgkm0<0>();
+      widen_own_all<NW>(stage, buf0, w, l, rope_real);
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
-    // phase k: widen raw tile k+1 into the other bf16 buffer (landed and
-    // published by the previous barrier), compute tile k while loading raw
-    // tile k+3 into the stage tile k came from, wait for raw tile k+2,
-    // barrier. Tile 0 (which sets the exponent reference) is peeled off.
-    {
-      fp8_tile_widen<NT>(stage[1], tbuf[1], tid);
-      const Fp8Load<NW> next = load(3);
-      tile_compute<CACHE_FP8, true>(tbuf[0], scl_all, wi.t0, wi.t1, qreg, qpe, la, h, st,
-                                    [&](int j) { next.step(j); });
-      wait_vm_lgkm0<P>();
+    f32x16 s0, s1;    // scores of even / odd tiles
+    bf16x8 pb[2];     // PV B operand (weights of the tile whose PV is next)
+    bf16x8 pring[3];  // PV A operands in flight
+    // a step's extra work: wait for its raw tile, widen it, load the one after
+    auto extra = [&](int t, const char* raw, char* dst, int j) {
+      if (j + 1 < ntiles) {
+        if (t == WIDEN_SLOT0 - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        widen_own_at_<NW>(t, raw, dst, w, l, rope_real, std::make_integer_sequence<int, P>{});
+      }
+      if (t == LOAD_SLOT && j + 2 < ntiles) {
+        int lv = l;   // lane offsets recomputed here, for the same reason
+        asm volatile("" : "+v"(lv));
+        int vo[P];
+        fp8_piece_offsets<NW>(p, w, lv, vo);
+        fp8_load<NW>(p, stage, dummy, __builtin_amdgcn_readlane(trow, min(j + 2, ntiles - 1)),
+                     nvalid(j + 2), w, vo)
+            .all();
+      }
+    };
+    auto step_end = [&]() {   // tile j+1 widened everywhere, tile j-1 read everywhere
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       compiler_fence();
+    };
+    pipe_step<true, false, true, true>(buf0, nullptr, wi.t0, wi.t1, qreg, qpe, la, h, st, s0, s1,
+                                       pb, pring, [&](int t, int) { extra(t, buf2, buf1, 0); },
+                                       scl_all);
+    // (with few waves a lane's pieces outnumber the S^T-only step's slots:
+    // the rest of its extra work follows the step)
+    static_for<(LOAD_SLOT + 1 > D_QK / 16) ? LOAD_SLOT + 1 - D_QK / 16 : 0>(
+        [&](auto tc) { extra(D_QK / 16 + decltype(tc)::value, buf2, buf1, 0); });
+    step_end();
+    auto step = [&](char* K, char* V, char* W, int j, f32x16& sn, f32x16& sp) {
+      if (j < ntiles) {
+        pipe_step<true, true, false, true>(K, V, wi.t0 + j * TILE, wi.t1, qreg, qpe, la, h, st, sn,
+                                           sp, pb, pring, [&](int t, int) { extra(t, stage, W, j); },
+                                           scl_all + TILE * j, scl_all + TILE * (j - 1));
+        step_end();
+      }
+    };
+    for (int j = 1; j < ntiles; j += 6) {
+      step(buf1, buf0, buf2, j, s1, s0);
+      step(buf2, buf1, buf0, j + 1, s0, s1);
+      step(buf0, buf2, buf1, j + 2, s1, s0);
+      step(buf1, buf0, buf2, j + 3, s0, s1);
+      step(buf2, buf1, buf0, j + 4, s1, s0);
+      step(buf0, buf2, buf1, j + 5, s0, s1);
     }
-    for (int k = 1; k < ntiles; ++k) {
-      fp8_tile_widen<NT>(stage[(k + 1) % 3], tbuf[(k + 1) & 1], tid);
-      const Fp8Load<NW> next = load(k + 3);
-      tile_compute<CACHE_FP8, false>(tbuf[k & 1], scl_all + TILE * k, wi.t0 + k * TILE, wi.t1,
-                                     qreg, qpe, la, h, st, [&](int j) { next.step(j); });
-      wait_vm_lgkm0<P>();   // raw tile k+2 landed, k+3 may be in flight
-      __builtin_amdgcn_s_barrier();
-      compiler_fence();
+    {   // softmax and PV of the last tile
+      const int last = ntiles - 1;
+      f32x16 sl = (last & 1) ? s1 : s0;
+      pipe_step<false, true, false, true>(nullptr, bufs + (last % 3) * TILE_BYTES, 0, wi.t1, qreg,
+                                          qpe, la, h, st, sl, sl, pb, pring, [](int, int) {},
+                                          nullptr, scl_all + TILE * last);
     }
-    if (split_overflowed(st) && l == 0) overflow = 1;
+    // overflow flags (own LDS words); after the barrier every wave is also
+    // past its last tile read, and no load is in flight
+    const bool ovf = split_overflowed(st);
+    wait_vm_lgkm0<0>();
+    if (l == 0) flags[w] = ovf ? 1 : 0;
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    if (overflow == 0) break;
-    // rare path (see the bf16 kernel): true maximum, then recompute
+    int any_ovf = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any_ovf |= flags[i];
+    any_ovf = __builtin_amdgcn_readfirstlane(any_ovf);
+    if (any_ovf == 0) break;
+    // Rare path (see the bf16 kernel): each head's true maximum over the
+    // split (scores only), then the split again against it.
     float mtrue = -INFINITY;
     for (int k = 0; k < ntiles; ++k) {
-      load(k).all();
-      wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();   // buffer 0 and the flags are no longer read
       compiler_fence();
-      fp8_tile_widen<NT>(stage[k % 3], tbuf[0], tid);
+      load_raw(stage, k).all();
+      wait_vm_lgkm0<0>();
+      widen_own_all<NW>(stage, buf0, w, l, rope_real);
       wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
       float sv[16];
-      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8, true>(tbuf[0], scl_all + TILE * k,
-                                                        wi.t0 + k * TILE, wi.t1, qreg,
-                                                        qpe, la, h, sv, [](int) {}));
-      __builtin_amdgcn_s_barrier();
-      compiler_fence();
+      bf16x8 qp[QLDS];
+#pragma unroll
+      for (int j = 0; j < QLDS; ++j) qp[j] = *(const bf16x8*)(qpe + 1024 * j);
+      mtrue = fmaxf(mtrue, tile_scores<CACHE_FP8, true>(buf0, scl_all + TILE * k, wi.t0 + k * TILE,
+                                                        wi.t1, qreg, qp, la, h, sv, [](int) {}));
     }
     reset_state(st, mtrue);
-    if (tid == 0) overflow = 0;
+    wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
   }
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-  write_partial(wi, st, h, l, tbuf[w >> 1] + (w & 1) * PART_SCR_BYTES);
+  write_partial(wi, st, h, l, (w < 2 ? buf0 : buf1) + (w & 1) * PART_SCR_BYTES);
 }
+
 
 }  // namespace mla
