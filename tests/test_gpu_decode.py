@@ -164,6 +164,28 @@ def test_fp8_cache_small(gpu):
     run_and_compare(gpu, inp, "fp8", num_splits=4)
 
 
+@pytest.mark.parametrize("H", [32, 64])
+def test_fp8_cache_fewer_waves(gpu, H):
+    """fp8 cache with H/32 = 1 or 2 waves per workgroup (with one wave a
+    lane's staged pieces outnumber the first step's MFMA slots): lengths 1,
+    33, 300 and 777 (several tiles, a ragged tail)."""
+    lengths = torch.tensor([1, 33, 300, 777], dtype=torch.int32)
+    inp = synth.make_inputs(5, B=4, N=777, H=H, lengths=lengths)
+    run_and_compare(gpu, inp, "fp8")
+    run_and_compare(gpu, inp, "fp8", num_splits=3)
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_size", [32, 128])
+def test_paged_block_sizes(gpu, cache_dtype, block_size):
+    """Paged caches with 32- and 128-token blocks (any multiple of the
+    32-token tile): 32 puts every tile in its own block, 128 four per block."""
+    lengths = torch.tensor([1000, 129, 32, 500], dtype=torch.int32)
+    inp = synth.make_inputs(3, B=4, N=1000, lengths=lengths, paged=True, block_size=block_size,
+                            cache_dtype=cache_dtype)
+    run_and_compare(gpu, inp, cache_dtype)
+
+
 def test_config2_full(gpu):
     """bf16, B=1, H=128, N=4096 (DeepSeek-V3 shape): every output."""
     run_and_compare(gpu, synth.make_inputs(2), "bf16")
