@@ -14,7 +14,9 @@ a step never finds its cache in the 256 MB last-level cache left by the
 previous step, as in a real model where the other layers run in between.
 
 Prints ONE JSON line (see the fields below). Options:
-  --steps K --warmup W     timed and untimed steps (defaults 50 / 10)
+  --steps K --warmup W     timed and untimed steps (defaults 1000 / 300: the
+                           GPU reaches its steady-state speed only after a few
+                           hundred steps; before, steps run ~15 % slower)
   --gpus N                 only N = 1 is supported (one process, one GPU)
   --no-cpu                 skip the CPU-oracle baseline leg
   --config NAME            3u (default), 3, 4 or 5 (other workloads, for study)
@@ -52,8 +54,8 @@ N_LAYERS_CYCLED = 3
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", default="3u")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
