@@ -278,8 +278,8 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c};
   const int absorb_blocks = ceil_div(H, 32) * 128;
   if (do_append)
-    hipLaunchKernelGGL(mla_absorb_append_kernel, dim3(absorb_blocks + ceil_div(B, 4)), dim3(256), 0,
-                       stream, ap, app, absorb_blocks);
+    hipLaunchKernelGGL(mla_absorb_append_kernel, dim3(append_blocks(B) + absorb_blocks), dim3(256),
+                       0, stream, ap, app);
   else
     hipLaunchKernelGGL(mla_absorb_kernel, dim3(absorb_blocks), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());

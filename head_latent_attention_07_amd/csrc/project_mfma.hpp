@@ -167,17 +167,22 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
   absorb_workgroup(p, blockIdx.x);
 }
 
-// absorb and cache append in one launch: workgroups past the absorb grid
-// append the new rows, one sequence per wave (the absorb neither reads nor
-// writes the cache, so the two halves are independent)
-__global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, AppendParams a,
-                                                               int absorb_blocks) {
-  if ((int)blockIdx.x < absorb_blocks) {
-    absorb_workgroup(p, blockIdx.x);
-  } else {
-    const int b = ((int)blockIdx.x - absorb_blocks) * 4 + (int)(threadIdx.x >> 6);
+// absorb and cache append in one launch (the absorb neither reads nor
+// writes the cache, so the two are independent). The append workgroups come
+// first (one sequence per wave, their count rounded up to a multiple of 8 so
+// the absorb workgroups keep their XCD placement): dispatched first, they
+// run beside the absorb from the start; placed after it, they would wait for
+// absorb workgroups to retire (two fit per CU) and end the launch late.
+__host__ __device__ constexpr int append_blocks(int B) { return ((B + 3) / 4 + 7) / 8 * 8; }
+
+__global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, AppendParams a) {
+  const int na = append_blocks(p.B);
+  if ((int)blockIdx.x < na) {
+    const int b = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
     if (b < p.B) append_row(a, b, threadIdx.x & 63);
+    return;
   }
+  absorb_workgroup(p, blockIdx.x - na);
 }
 
 // ----------------------------------------------------------------------------
