@@ -350,6 +350,32 @@ def append_row(c_kv: np.ndarray, k_pe: np.ndarray, pos: int, cache_dtype: str):
 
 
 # ---------------------------------------------------------------------------
+# Down-projection of the new token ([TN] "Architectural Innovations:
+# Multi-Head Latent Attention (MLA)", equation for c_KV; [WL] "MLA: compress
+# the pair, not the heads", diagram: the input h_t gives both the 512-wide
+# latent and the 64-wide RoPE key that go to the cache)
+# ---------------------------------------------------------------------------
+
+
+def kv_down_project(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray):
+    """Latent c_KV = W_DKV h and un-rotated RoPE key W_KR h of one token.
+
+    Column convention of the [TN] equation: W_DKV is [d_c, d_model] and W_KR
+    [d_rope, d_model] (reading: the pages name the RoPE key's projection only
+    through the diagram, so it takes the same convention), h is [d_model].
+    float64 products, no bias and no normalisation (the pages give neither).
+    """
+    return w_dkv @ h, w_kr @ h
+
+
+def project_append_row(h, w_dkv, w_kr, pos: int, cache_dtype: str):
+    """Row written for a token given its hidden state: the down-projection,
+    then the append of the latent and the RoPE-rotated key (append_row)."""
+    c, k = kv_down_project(h, w_dkv, w_kr)
+    return append_row(c, k, pos, cache_dtype)
+
+
+# ---------------------------------------------------------------------------
 # Cache-size closed forms ([WL] "Classic attention and the cost of the KV
 # cache" and "MLA: compress the pair, not the heads"; [IA] "A conta feita
 # fora da DeepSeek")

@@ -204,6 +204,21 @@ def append_inputs(seed: int, B: int, in_dtype: str, device="cpu"):
     return c, k
 
 
+D_MODEL = 7168    # hidden width of the DeepSeek-V3 setting
+
+
+def projection_inputs(seed: int, B: int, act: str, d_model: int = D_MODEL, device="cpu"):
+    """Hidden states h [B, d_model] ~ N(0,1) and the down-projection weights
+    W_DKV [512, d_model], W_KR [64, d_model] ~ N(0, 1/d_model) (standard
+    deviation 1/sqrt(fan_in), fan_in = d_model), in the activation type.
+    Seeds: seed (h), seed+1 (W_DKV), seed+2 (W_KR)."""
+    sd = 1.0 / math.sqrt(d_model)
+    h = to_storage(normal((B, d_model), seed, device), act)
+    w_dkv = to_storage(normal((D_C, d_model), seed + 1, device, std=sd), act)
+    w_kr = to_storage(normal((D_ROPE, d_model), seed + 2, device, std=sd), act)
+    return h, w_dkv, w_kr
+
+
 def raw_bits(t: torch.Tensor):
     """Storage bits of a CPU tensor as a numpy integer array (uint16 for bf16,
     uint32 for f32, uint8 for fp8 codes)."""

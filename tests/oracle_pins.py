@@ -234,6 +234,71 @@ def pin_rope(orc):
     assert abs(d1 - d2) < 1e-11
 
 
+def pin_projection_hand_example(orc):
+    """Hand-worked down-projection with square 2x2 weights (so a transposed
+    operand still runs and must give other numbers): W_DKV = [[1,2],[3,4]],
+    W_KR = [[0,1],[2,0]], h = (1,-1): c = (1-2, 3-4) = (-1,-1) (W^T h would
+    be (-2,-2)); k = (-1, 2) (W^T h would be (-2,1)). At position 1 the key
+    pair turns by 1 radian: (-cos 1 - 2 sin 1, -sin 1 + 2 cos 1)."""
+    w_dkv = np.array([[1.0, 2.0], [3.0, 4.0]])
+    w_kr = np.array([[0.0, 1.0], [2.0, 0.0]])
+    h = np.array([1.0, -1.0])
+    c, k = orc.kv_down_project(h, w_dkv, w_kr)
+    assert np.array_equal(c, [-1.0, -1.0]) and np.array_equal(k, [-1.0, 2.0])
+    lat, rope, _, _ = orc.project_append_row(h, w_dkv, w_kr, 0, "f32")
+    assert np.array_equal(lat, [-1.0, -1.0]) and np.array_equal(rope, [-1.0, 2.0])
+    _, rope, _, _ = orc.project_append_row(h, w_dkv, w_kr, 1, "f32")
+    want = [-math.cos(1.0) - 2 * math.sin(1.0), -math.sin(1.0) + 2 * math.cos(1.0)]
+    assert np.allclose(rope, want, rtol=1e-7, atol=1e-7)
+
+
+def pin_projection_basis(orc):
+    """A basis vector h = e_i selects column i of both weights (first, middle
+    and last coordinate, non-square shapes); the projection is linear in h;
+    and a latent key decompressed from the projected latent equals the key of
+    the pre-multiplied weights (W_UK W_DKV) h ([TN] equations for c_KV and
+    K_t, multiplied in the other order)."""
+    r = _rng(21)
+    d_model, d_c, d_r = 12, 8, 4
+    w_dkv = r.standard_normal((d_c, d_model))
+    w_kr = r.standard_normal((d_r, d_model))
+    for i in (0, 5, d_model - 1):
+        e = np.zeros(d_model)
+        e[i] = 1.0
+        c, k = orc.kv_down_project(e, w_dkv, w_kr)
+        assert np.array_equal(c, w_dkv[:, i]) and np.array_equal(k, w_kr[:, i])
+    h1, h2 = r.standard_normal(d_model), r.standard_normal(d_model)
+    c1, k1 = orc.kv_down_project(h1, w_dkv, w_kr)
+    c2, k2 = orc.kv_down_project(h2, w_dkv, w_kr)
+    c3, k3 = orc.kv_down_project(2.0 * h1 - 3.0 * h2, w_dkv, w_kr)
+    assert np.allclose(c3, 2.0 * c1 - 3.0 * c2, atol=1e-12)
+    assert np.allclose(k3, 2.0 * k1 - 3.0 * k2, atol=1e-12)
+    w_uk = r.standard_normal((5, d_c))
+    assert np.allclose(w_uk @ c1, (w_uk @ w_dkv) @ h1, atol=1e-12)
+
+
+def pin_projection_append(orc):
+    """The appended row of a projected token: at position 0 the bf16 row is
+    the nearest bf16 of every projected value (RoPE is the identity there);
+    at another position the latent is unchanged and each key pair keeps the
+    norm of the projected pair."""
+    r = _rng(22)
+    d_model = 96
+    w_dkv = r.standard_normal((512, d_model)) / math.sqrt(d_model)
+    w_kr = r.standard_normal((64, d_model)) / math.sqrt(d_model)
+    h = r.standard_normal(d_model)
+    c, k = orc.kv_down_project(h, w_dkv, w_kr)
+    lat, rope, _, _ = orc.project_append_row(h, w_dkv, w_kr, 0, "bf16")
+    assert np.array_equal(lat, orc.round_to_bf16(c)) and np.array_equal(rope, orc.round_to_bf16(k))
+    lat, rope, _, _ = orc.project_append_row(h, w_dkv, w_kr, 4321, "f32")
+    assert np.array_equal(lat, orc.round_to_f32(c))
+    assert np.allclose(np.hypot(rope[0::2], rope[1::2]), np.hypot(k[0::2], k[1::2]), rtol=1e-6)
+    assert not np.allclose(rope, k, rtol=1e-3)
+
+
+PROJECTION_PINS = [pin_projection_hand_example, pin_projection_basis, pin_projection_append]
+
+
 ALL_DECODE_PINS = [pin_bruteforce, pin_single_row, pin_zero_query, pin_rope_shift,
                    pin_permutation, pin_absorption, pin_hand_example, pin_causal_prefill,
                    pin_lse_combine, pin_empty]

@@ -121,11 +121,33 @@ def m_absorbed_missing_uv(o):
     o.decode_head_absorbed = f
 
 
+def m_proj_transposed(o):
+    o.kv_down_project = lambda h, w_dkv, w_kr: (w_dkv.T @ h, w_kr.T @ h)
+
+
+def m_proj_last_term_dropped(o):
+    o.kv_down_project = lambda h, w_dkv, w_kr: (w_dkv[:, :-1] @ h[:-1], w_kr[:, :-1] @ h[:-1])
+
+
+def m_proj_key_from_latent_weights(o):
+    o.kv_down_project = lambda h, w_dkv, w_kr: (w_dkv @ h, w_dkv[-w_kr.shape[0]:] @ h)
+
+
+def m_proj_key_not_rotated(o):
+    def f(h, w_dkv, w_kr, pos, cache_dtype):
+        c, k = o.kv_down_project(h, w_dkv, w_kr)
+        lat, _, s, codes = o.append_row(c, k, 0, cache_dtype)
+        return lat, o.append_row(c, k, 0, cache_dtype)[1], s, codes
+    o.project_append_row = f
+
+
 MUTATIONS = [m_drop_rope_term, m_wrong_scale, m_head_index, m_uv_for_uk_layout,
              m_unnormalised, m_lse_without_max, m_rope_sign, m_rope_half_split, m_rope_freq,
-             m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv]
+             m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv,
+             m_proj_transposed, m_proj_last_term_dropped, m_proj_key_from_latent_weights,
+             m_proj_key_not_rotated]
 
-PINS = P.ALL_DECODE_PINS + [P.pin_paged_rows, P.pin_rope]
+PINS = P.ALL_DECODE_PINS + [P.pin_paged_rows, P.pin_rope] + P.PROJECTION_PINS
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
