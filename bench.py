@@ -25,6 +25,9 @@ Prints ONE JSON line (see the fields below). Options:
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
+  --project                only measure mla_project_append (the down-projection
+                           of 64 new tokens' hidden states, d_model 7168, bf16,
+                           and the append of their rows) and print its own line
   --write-traffic F W CF CW  only turn four rocprofv3 counter CSVs (decode
                            kernel FETCH_SIZE, WRITE_SIZE; copy FETCH_SIZE,
                            WRITE_SIZE, taken with --copy-calibration 1024)
@@ -62,6 +65,7 @@ def parse():
     ap.add_argument("--separate-append", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--write-traffic", nargs=4, default=None)
+    ap.add_argument("--project", action="store_true")
     return ap.parse_args()
 
 
@@ -202,8 +206,86 @@ def write_traffic(paths, config: str, kernel: str, copy_mib: int = 1024):
     print(json.dumps(rec))
 
 
+PROJECT_SETS = 48     # weight sets cycled: ~400 MB, more than the last-level cache
+
+
+def bench_project(args):
+    """Time mla_project_append alone: 64 tokens, d_model 7168, bf16 operands,
+    bf16 cache. Each call uses the next of PROJECT_SETS weight/hidden sets so
+    that its 8.3 MB of weights come from HBM as in a model whose other layers
+    run in between. Algorithmic bytes per call: the weights, the hidden
+    states and the written rows."""
+    import torch
+    import head_latent_attention_07_amd as mla
+    import synth
+
+    mla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, D, cap = 64, synth.D_MODEL, 16
+    sets = [synth.projection_inputs(9000 + 10 * i, B, "bf16", D, device=dev)
+            for i in range(PROJECT_SETS)]
+    cache = torch.zeros((B * cap, 576), dtype=torch.bfloat16, device=dev)
+    lat, rope = mla.split_cache(cache)
+    pos = torch.full((B,), cap - 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(mla.project_workspace_size(B, D), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        h, wd, wk = sets[i % PROJECT_SETS]
+        mla.project_append(h, wd, wk, pos, lat, rope, heads=128, seq_capacity=cap, workspace=ws)
+
+    # A call costs the host more than the GPU, so calls issued one by one
+    # leave the GPU idle between them: the calls over all weight sets are
+    # captured once in a HIP graph and the graph is replayed (kernels back to
+    # back, as in a model's decode step).
+    call(PROJECT_SETS - 1)
+    torch.cuda.synchronize()
+    eager = cache.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(PROJECT_SETS):
+            call(i)
+    reps = max(1, args.steps // PROJECT_SETS)
+    for _ in range(max(1, args.warmup // PROJECT_SETS)):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(cache.view(torch.int16), eager.view(torch.int16)):
+        raise RuntimeError("graph replay of mla_project_append differs from the eager call")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    avg_ms = a.elapsed_time(b) / (reps * PROJECT_SETS)
+    nbytes = (D_QK_ROWS * D + B * D) * 2 + B * 576 * 2
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "MLA down-projection + append rows/s (c_KV = W_DKV h, RoPE(W_KR h))",
+        "value": B / (avg_ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
+        "steps": reps * PROJECT_SETS, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / (reps * PROJECT_SETS),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normals, weights N(0, 1/d_model))",
+        "config": {"workload": "mla_project_append_b64_d7168_bf16", "B": B, "d_model": D,
+                   "weight_sets_cycled": PROJECT_SETS},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "mla_kv_project_kernel + mla_project_append_kernel",
+                     "bytes_per_launch": nbytes, "avg_launch_us": avg_ms * 1e3},
+    }), flush=True)
+
+
+D_QK_ROWS = 576    # rows of W_DKV (512) and W_KR (64)
+
+
 def main():
     args = parse()
+    if args.project:
+        bench_project(args)
+        return
     if args.write_traffic:
         write_traffic(args.write_traffic, args.config, "mla_decode_bf16_kernel")
         return

@@ -22,7 +22,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 
 SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
-           "mla_decode_workspace_size", "mla_decode", "mla_decode_paged")
+           "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
+           "mla_project_append", "mla_project_workspace_size")
 
 
 class MLAError(RuntimeError):
@@ -84,6 +85,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode.argtypes = common + [_I64] + tail
     lib.mla_decode_paged.restype = ctypes.c_int
     lib.mla_decode_paged.argtypes = common + [_P, _I32, _I32] + tail
+    lib.mla_project_workspace_size.restype = _SZ
+    lib.mla_project_workspace_size.argtypes = [_I32, _I32]
+    lib.mla_project_append.restype = ctypes.c_int
+    lib.mla_project_append.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int, _I32, _P,
+                                       _I32, _P, _I64, _P, _I64, _P, ctypes.c_int, _I64, _I64, _P,
+                                       _I32, _I32, _F, _P, _SZ, _P]
     _lib = lib
     return lib
 
@@ -169,6 +176,32 @@ def cache_append(c_kv: torch.Tensor, k_pe: torch.Tensor, positions: torch.Tensor
         _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(scales),
         dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table), max_blocks,
         block_size, rope_theta, _stream(stream)))
+
+
+def project_workspace_size(batch: int, d_model: int) -> int:
+    return int(load().mla_project_workspace_size(batch, d_model))
+
+
+def project_append(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+                   positions: torch.Tensor, latent: torch.Tensor, rope: torch.Tensor, *,
+                   heads: int, scales: Optional[torch.Tensor] = None, seq_capacity: int = 0,
+                   block_table: Optional[torch.Tensor] = None, block_size: int = 64,
+                   rope_theta: float = 10000.0, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Project the new tokens' hidden states to their latent rows and RoPE keys
+    and append them (mla_project_append)."""
+    lib = load()
+    d = dims(heads)
+    B, D = hidden.shape
+    if workspace is None:
+        workspace = torch.empty(project_workspace_size(B, D), dtype=torch.uint8,
+                                device=hidden.device)
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    _check(lib.mla_project_append(
+        ctypes.byref(d), _ptr(hidden), _ptr(w_dkv), _ptr(w_kr), dtype_code(hidden.dtype), D,
+        _ptr(positions), B, _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+        _ptr(scales), dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table),
+        max_blocks, block_size, rope_theta, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,

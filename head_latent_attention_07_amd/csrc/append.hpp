@@ -41,10 +41,37 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float v) {
   return sign | (uint32_t)(((E + 7) << 3) | (int)q);
 }
 
+// Rotate and store one row, given its values in fp32: lane l of the wave
+// holds latent values x = c[8l .. 8l+7] and (xe, xo) = the un-rotated RoPE
+// pair (2l', 2l'+1), l' = l mod 32 (lanes 32..63 repeat a pair and do not
+// store it). The rotation angle is computed before the destination row is
+// known (its latency overlaps that of the position and block-table reads).
+__device__ __forceinline__ void append_store(const AppendParams& p, int b, int l,
+                                             const float (&x)[8], double xe, double xo);
+
+// The token's position and the rotation of lane l's pair, (cos, sin) of
+// pos * theta^(-2 l' / 64) in double precision: needs only the position, so
+// a caller can start it before the row's values are known.
+struct RopeAngle {
+  int pos;
+  double cs, sn;
+};
+
+__device__ __forceinline__ RopeAngle append_angle(const AppendParams& p, int b, int l) {
+  const int lp = l & (D_R / 2 - 1);
+  RopeAngle a;
+  a.pos = p.positions[b];
+  const double freq = pow(p.theta, -2.0 * (double)lp / (double)D_R);
+  sincos((double)a.pos * freq, &a.sn, &a.cs);
+  return a;
+}
+
+__device__ __forceinline__ void append_write(const AppendParams& p, int b, int l,
+                                             const float (&x)[8], double xe, double xo,
+                                             const RopeAngle& ang);
+
 // one wave per sequence: lane l owns latent values 8l..8l+7 and, for l < 32,
-// the RoPE pair (2l, 2l+1). The inputs are loaded and the rotation angle is
-// computed before the destination row is known (their latencies overlap
-// that of the position and block-table reads).
+// the RoPE pair (2l, 2l+1), read from the c_kv / k_pe inputs.
 __device__ __forceinline__ void append_row(const AppendParams& p, int b, int l) {
   float x[8];
   if (p.in_bf16) {
@@ -68,10 +95,19 @@ __device__ __forceinline__ void append_row(const AppendParams& p, int b, int l) 
     xe = k[2 * lp];
     xo = k[2 * lp + 1];
   }
-  const int pos = p.positions[b];
-  const double freq = pow(p.theta, -2.0 * (double)lp / (double)D_R);
-  double sn, cs;
-  sincos((double)pos * freq, &sn, &cs);
+  append_store(p, b, l, x, xe, xo);
+}
+
+__device__ __forceinline__ void append_store(const AppendParams& p, int b, int l,
+                                             const float (&x)[8], double xe, double xo) {
+  append_write(p, b, l, x, xe, xo, append_angle(p, b, l));
+}
+
+__device__ __forceinline__ void append_write(const AppendParams& p, int b, int l,
+                                             const float (&x)[8], double xe, double xo,
+                                             const RopeAngle& ang) {
+  const int pos = ang.pos;
+  const double cs = ang.cs, sn = ang.sn;
   const float r0 = (float)(xe * cs - xo * sn);
   const float r1 = (float)(xe * sn + xo * cs);
 

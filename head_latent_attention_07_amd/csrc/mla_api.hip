@@ -11,6 +11,7 @@
 #include "append.hpp"
 #include "decode_mfma.hpp"
 #include "fp32_path.hpp"
+#include "kv_project.hpp"
 #include "project_mfma.hpp"
 
 using namespace mla;
@@ -172,6 +173,42 @@ mla_status check_append(const mla_dims* dims, const void* c_kv, const void* k_pe
   out->block_size = block_size;
   out->theta = (double)rope_theta;
   return MLA_OK;
+}
+
+// Split of the down-projection's K (d_model) into slices: about 256
+// workgroups (9 column tiles x slices x batch groups) so that one wave of
+// workgroups covers the chip and reads the weights once; every slice is
+// non-empty. MLA_PROJECT_SPLITS overrides the slice count (for tuning).
+struct ProjPlan {
+  int S, cps, mgroups, msub;
+};
+
+ProjPlan project_plan(int B, int D) {
+  ProjPlan pl;
+  const int nchunks = D / PJ_CHUNK;
+  pl.mgroups = ceil_div(B, PJ_MG);
+  pl.msub = pl.mgroups > 1 ? 4 : ceil_div(B, 32);
+  int target = env_int("MLA_PROJECT_SPLITS");
+  if (target <= 0) target = 256 / (PJ_NTILES * pl.mgroups);
+  target = std::max(1, std::min(target, nchunks));
+  pl.cps = ceil_div(nchunks, target);
+  pl.S = ceil_div(nchunks, pl.cps);
+  return pl;
+}
+
+size_t project_ws_bytes(int B, int D) {
+  const ProjPlan pl = project_plan(B, D);
+  return align_up((size_t)pl.S * B * D_QK * sizeof(float), 256);
+}
+
+template <typename T>
+void launch_project(const ProjectParams& pp, int msub, int grid, hipStream_t stream) {
+  switch (msub) {
+    case 1: hipLaunchKernelGGL((mla_kv_project_kernel<T, 1>), dim3(grid), dim3(256), 0, stream, pp); break;
+    case 2: hipLaunchKernelGGL((mla_kv_project_kernel<T, 2>), dim3(grid), dim3(256), 0, stream, pp); break;
+    case 3: hipLaunchKernelGGL((mla_kv_project_kernel<T, 3>), dim3(grid), dim3(256), 0, stream, pp); break;
+    default: hipLaunchKernelGGL((mla_kv_project_kernel<T, 4>), dim3(grid), dim3(256), 0, stream, pp); break;
+  }
 }
 
 // Validation shared by both decode entry points.
@@ -417,6 +454,53 @@ mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* 
   if (batch == 0) return MLA_OK;
   (void)hipGetLastError();
   hipLaunchKernelGGL(mla_append_kernel, dim3(batch), dim3(64), 0, stream, p);
+  return launch_status();
+}
+
+size_t mla_project_workspace_size(int32_t batch, int32_t d_model) {
+  if (batch < 0 || d_model <= 0 || d_model % PJ_CHUNK != 0) return 0;
+  if (batch == 0) return 256;
+  return project_ws_bytes(batch, d_model);
+}
+
+mla_status mla_project_append(const mla_dims* dims, const void* hidden, const void* w_dkv,
+                              const void* w_kr, mla_dtype act, int32_t d_model,
+                              const int32_t* positions, int32_t batch, void* latent, int64_t ls,
+                              void* rope, int64_t rs, void* scales, mla_dtype cdt, int64_t rows,
+                              int64_t seq_capacity, const int32_t* block_table,
+                              int32_t max_blocks, int32_t block_size, float rope_theta,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AppendParams a;
+  // the append's own checks (the hidden state stands in for its inputs)
+  MLA_TRY(check_append(dims, hidden, hidden, act, positions, batch, latent, ls, rope, rs, scales,
+                       cdt, rows, seq_capacity, block_table, max_blocks, block_size, rope_theta,
+                       &a));
+  if (d_model <= 0 || d_model % PJ_CHUNK != 0) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!w_dkv || !w_kr || !aligned16(hidden) || !aligned16(w_dkv) || !aligned16(w_kr))
+    return MLA_ERR_INVALID_ARG;
+  const ProjPlan pl = project_plan(batch, d_model);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < project_ws_bytes(batch, d_model))
+    return MLA_ERR_WORKSPACE;
+  a.c_kv = nullptr;
+  a.k_pe = nullptr;
+  ProjectParams pp;
+  pp.h = hidden;
+  pp.w_dkv = w_dkv;
+  pp.w_kr = w_kr;
+  pp.part = (float*)workspace;
+  pp.B = batch;
+  pp.D = d_model;
+  pp.S = pl.S;
+  pp.cps = pl.cps;
+  const int grid = PJ_NTILES * pl.S * pl.mgroups;
+  (void)hipGetLastError();
+  if (act == MLA_BF16)
+    launch_project<bf16>(pp, pl.msub, grid, stream);
+  else
+    launch_project<float>(pp, pl.msub, grid, stream);
+  hipLaunchKernelGGL(mla_project_append_kernel, dim3(batch), dim3(256), 0, stream,
+                     (const float*)workspace, pl.S, batch, a);
   return launch_status();
 }
 

@@ -156,6 +156,51 @@ mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* 
                             const int32_t* block_table, int32_t max_blocks_per_seq,
                             int32_t block_size, float rope_theta, hipStream_t stream);
 
+/*
+ * mla_project_append: compute the new tokens' cache rows from their hidden
+ * states and append them (the step before mla_cache_append, fused with it).
+ *
+ * For each b in [0, batch): c = W_DKV h[b] (the latent, 512 values) and
+ * k = W_KR h[b] (the un-rotated RoPE key, 64 values), then the row is
+ * stored exactly as mla_cache_append stores (c, k) at position positions[b]
+ * (RoPE, rounding or fp8 quantisation, addressing). (Sources: the equation
+ * c_KV = W_DKV h_t of "DeepSeek AI efficiency, architecture, benchmarks",
+ * section "Architectural Innovations: Multi-Head Latent Attention (MLA)";
+ * the diagram of "How DeepSeek Rewrote the Transformer [MLA]", section
+ * "MLA: compress the pair, not the heads", where the input h_t yields both
+ * the latent and the RoPE key. The pages name no bias and no normalisation
+ * of c, so there is none.) The products are accumulated in fp32 (bf16 or
+ * fp32 operands); the fp32 sums are the values handed to the append.
+ *
+ * Arguments
+ *   hidden     [batch, d_model] in act_dtype (MLA_BF16 or MLA_F32), row stride
+ *              d_model, 16-byte aligned
+ *   w_dkv      [512, d_model] in act_dtype, row-major (row n gives latent n)
+ *   w_kr       [64, d_model]  in act_dtype, row-major (row n gives key n)
+ *   d_model    hidden width: a positive multiple of 64 (7168 in the
+ *              DeepSeek-V3 setting)
+ *   positions .. rope_theta: as for mla_cache_append
+ *   workspace  device scratch of at least mla_project_workspace_size(batch,
+ *              d_model) bytes, 16-byte aligned (fp32 partial sums); its
+ *              contents on entry do not matter
+ * Errors: those of mla_cache_append; INVALID_ARG for a d_model that is not a
+ * positive multiple of 64 or null/misaligned weights; WORKSPACE for a
+ * missing, misaligned or small workspace. batch == 0 is a valid no-op.
+ * Two launches on `stream`; the result does not depend on timing (fixed
+ * summation order).
+ */
+mla_status mla_project_append(const mla_dims* dims, const void* hidden, const void* w_dkv,
+                              const void* w_kr, mla_dtype act_dtype, int32_t d_model,
+                              const int32_t* positions, int32_t batch, void* latent,
+                              int64_t latent_stride, void* rope, int64_t rope_stride,
+                              void* scales, mla_dtype cache_dtype, int64_t cache_rows,
+                              int64_t seq_capacity, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, int32_t block_size, float rope_theta,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by mla_project_append (0 on invalid sizes). */
+size_t mla_project_workspace_size(int32_t batch, int32_t d_model);
+
 /* Workspace bytes needed by mla_decode / mla_decode_paged for these sizes
  * (absorbed queries, split partials). 0 on invalid arguments. The split plan
  * depends on the current device's compute-unit count, so query it on the

@@ -103,3 +103,25 @@ def test_paged_and_append_argument_errors():
     zero = list(args)
     zero[5] = 0
     assert lib.mla_cache_append(*zero, 10000.0, None) == 0
+
+
+def test_project_argument_errors():
+    lib = mla.load()
+    d = mla.dims(128)
+    p = ctypes.c_void_p(16)
+    assert lib.mla_project_workspace_size(64, 7168) >= 64 * 576 * 4
+    assert lib.mla_project_workspace_size(64, 100) == 0        # d_model not a multiple of 64
+    assert lib.mla_project_workspace_size(-1, 7168) == 0
+
+    def call(d_model=7168, batch=4, act=1, w_kr=p, ws=p, ws_bytes=1 << 30, theta=10000.0):
+        return lib.mla_project_append(ctypes.byref(d), p, p, w_kr, act, d_model, p, batch, p, 576,
+                                      p, 576, None, 1, 4096, 1024, None, 0, 64, theta, ws,
+                                      ws_bytes, None)
+    assert call(d_model=100) == 1
+    assert call(d_model=0) == 1
+    assert call(w_kr=None) == 1
+    assert call(act=2) == 2                                       # fp8 activations
+    assert call(theta=-1.0) == 1
+    assert call(ws=None) == 3
+    assert call(ws_bytes=1024) == 3
+    assert call(batch=0) == 0
