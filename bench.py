@@ -163,6 +163,36 @@ def cpu_baseline(cfg, seconds: float):
                       f"float64 non-absorbed oracle, {dt:.1f} s"}
 
 
+def cpu_baseline_project(seconds: float):
+    """The oracle's down-projection and append (float64) on the host cores:
+    rows of the --project workload (same shapes, seeds of its first weight
+    set) one at a time until `seconds` elapse; the weights are decoded once."""
+    import synth
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    h, wd, wk = synth.projection_inputs(9000, 64, "bf16", synth.D_MODEL)
+
+    def f64(t):
+        return orc.decode_storage(synth.raw_bits(t), "bf16")
+
+    hh, wdd, wkk = f64(h), f64(wd), f64(wk)
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.project_append_row(hh[rows % 64], wdd, wkk, 15, "bf16")
+        rows += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} rows of the same workload (d_model 7168, bf16 cache), float64 "
+                      f"oracle, weights decoded once beforehand, {dt:.1f} s"}
+
+
 def copy_calibration(mib: int):
     """A plain copy of known size: each launch reads and writes exactly
     mib MiB, so a profiler's HBM read/write counters for it give the factor
@@ -262,7 +292,7 @@ def bench_project(args):
     avg_ms = a.elapsed_time(b) / (reps * PROJECT_SETS)
     nbytes = (D_QK_ROWS * D + B * D) * 2 + B * 576 * 2
     gbs = nbytes / (avg_ms * 1e-3) / 1e9
-    print(json.dumps({
+    line = {
         "metric": "MLA down-projection + append rows/s (c_KV = W_DKV h, RoPE(W_KR h))",
         "value": B / (avg_ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
         "steps": reps * PROJECT_SETS, "warmup": args.warmup,
@@ -275,7 +305,10 @@ def bench_project(args):
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "mla_kv_project_kernel + mla_project_append_kernel",
                      "bytes_per_launch": nbytes, "avg_launch_us": avg_ms * 1e3},
-    }), flush=True)
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_project(min(args.cpu_seconds, 10.0))
+    print(json.dumps(line), flush=True)
 
 
 D_QK_ROWS = 576    # rows of W_DKV (512) and W_KR (64)

@@ -12,9 +12,10 @@
 // at d_model 7168; 2 * batch flops per weight element, under the MFMA ridge
 // for any batch up to ~300). So the kernel is laid out for the weight
 // stream:
-//   * grid = 9 column tiles of 64 outputs x S slices of K (x batch groups of
-//     128): every weight element is read by exactly one workgroup, and each
-//     workgroup covers the whole batch group, so no weight is read twice;
+//   * grid = 18 column tiles of 32 outputs x S slices of K (x batch groups
+//     of 128): every weight element is read by exactly one workgroup, and
+//     each workgroup covers the whole batch group, so no weight is read
+//     twice;
 //   * both operands are contiguous along K, so each lane loads its MFMA
 //     operands straight from global memory (no LDS staging): lane l of a
 //     wave reads 32 consecutive k of row l % 32 (half l / 32 of a 64-wide
@@ -23,7 +24,10 @@
 //     is a permutation of k, which a sum does not see);
 //   * the four waves of a workgroup take interleaved chunks of its K slice
 //     and are reduced through LDS in a fixed order (the result does not
-//     depend on timing); each slice writes an fp32 partial [S, B, 576];
+//     depend on timing); each slice writes an fp32 partial [S, B, 576]. The
+//     LDS reduction and the partials grow with the accumulator volume, so
+//     a workgroup holds one 32-wide column tile (64-wide tiles measured no
+//     faster and double both);
 //   * a second kernel (one workgroup per sequence) sums the S partials in a
 //     fixed order and hands the fp32 row to the append's rotate-and-store.
 #pragma once
@@ -33,8 +37,10 @@
 namespace mla {
 
 constexpr int PJ_CHUNK = 64;               // k per chunk (two lane halves of 32)
-constexpr int PJ_NT = 64;                  // outputs per workgroup: two 32-wide MFMA tiles
-constexpr int PJ_NTILES = D_QK / PJ_NT;    // 9; tile 8 is exactly the 64 rows of W_KR
+constexpr int PJ_NSUB = 1;                 // 32-wide MFMA column tiles per workgroup
+constexpr int PJ_NT = 32 * PJ_NSUB;        // outputs per workgroup
+constexpr int PJ_NTILES = D_QK / PJ_NT;    // the W_KR rows (512..575) fill whole tiles
+constexpr int PJ_CH = 1;                   // chunks whose loads a wave has in flight at once
 constexpr int PJ_MG = 128;                 // batch rows per batch group: four 32-row tiles
 constexpr int PJ_WAVES = 4;
 
@@ -81,7 +87,7 @@ struct PjOps<float> {
 };
 
 // Workgroups whose ids share the dispatcher's round-robin XCD (id mod 8) get
-// consecutive tile indices, so the nine column tiles of a K slice, which
+// consecutive tile indices, so the column tiles of a K slice, which
 // read the same hidden-state columns, meet in one XCD's L2. A bijection of
 // [0, G).
 __device__ __forceinline__ int pj_tile_index(int bid, int G) {
@@ -93,7 +99,7 @@ template <typename T, int MSUB>
 __global__ __launch_bounds__(256) void mla_kv_project_kernel(ProjectParams p) {
   using Ops = PjOps<T>;
   constexpr int L = Ops::LOADS;
-  constexpr int E = MSUB * 2 * 16;         // accumulator values per lane
+  constexpr int E = MSUB * PJ_NSUB * 16;   // accumulator values per lane
   __shared__ float red[PJ_WAVES][E][64];
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
@@ -107,9 +113,9 @@ __global__ __launch_bounds__(256) void mla_kv_project_kernel(ProjectParams p) {
   const int c0 = s * p.cps;
   const int c1 = min(c0 + p.cps, nchunks);
 
-  const T* wrow[2];
+  const T* wrow[PJ_NSUB];
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
+  for (int ns = 0; ns < PJ_NSUB; ++ns) {
     const int n = nt * PJ_NT + 32 * ns + r;
     wrow[ns] = (n < D_C) ? (const T*)p.w_dkv + (int64_t)n * p.D
                          : (const T*)p.w_kr + (int64_t)(n - D_C) * p.D;
@@ -121,45 +127,56 @@ __global__ __launch_bounds__(256) void mla_kv_project_kernel(ProjectParams p) {
     hrow[ms] = (const T*)p.h + (int64_t)m * p.D;
   }
 
-  f32x16 acc[MSUB][2];
+  f32x16 acc[MSUB][PJ_NSUB];
 #pragma unroll
   for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
+    for (int ns = 0; ns < PJ_NSUB; ++ns)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[ms][ns][j] = 0.f;
 
-  for (int c = c0 + w; c < c1; c += PJ_WAVES) {
-    const int k = c * PJ_CHUNK + 32 * g;
-    u32x4 bw[2][L], ah[MSUB][L];
+  // wave w takes chunks w, w+4, ... of the slice, PJ_CH of them per pass
+  // (a pass's chunks past the slice load its last chunk again and skip it)
+  for (int c = c0 + w; c < c1; c += PJ_WAVES * PJ_CH) {
+    u32x4 bw[PJ_CH][PJ_NSUB][L], ah[PJ_CH][MSUB][L];
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
+    for (int ch = 0; ch < PJ_CH; ++ch) {
+      const int k = min(c + PJ_WAVES * ch, c1 - 1) * PJ_CHUNK + 32 * g;
 #pragma unroll
-      for (int i = 0; i < L; ++i) bw[ns][i] = *(const u32x4*)((const char*)(wrow[ns] + k) + 16 * i);
+      for (int ns = 0; ns < PJ_NSUB; ++ns)
 #pragma unroll
-    for (int ms = 0; ms < MSUB; ++ms)
+        for (int i = 0; i < L; ++i)
+          bw[ch][ns][i] = *(const u32x4*)((const char*)(wrow[ns] + k) + 16 * i);
 #pragma unroll
-      for (int i = 0; i < L; ++i) ah[ms][i] = *(const u32x4*)((const char*)(hrow[ms] + k) + 16 * i);
-    // every load of the chunk is issued before the first MFMA waits on one
+      for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+          ah[ch][ms][i] = *(const u32x4*)((const char*)(hrow[ms] + k) + 16 * i);
+    }
+    // every load of the pass is issued before the first MFMA waits on one
     // (left to itself the scheduler interleaves them and pays the memory
     // latency several times per chunk)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ms = 0; ms < MSUB; ++ms)
+    for (int ch = 0; ch < PJ_CH; ++ch) {
+      if (ch > 0 && c + PJ_WAVES * ch >= c1) break;
 #pragma unroll
-      for (int ns = 0; ns < 2; ++ns) Ops::mfma_chunk(acc[ms][ns], ah[ms], bw[ns]);
+      for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < PJ_NSUB; ++ns) Ops::mfma_chunk(acc[ms][ns], ah[ch][ms], bw[ch][ns]);
+    }
   }
 
   // reduce the four waves' sums: wave w adds entries [w E/4, (w+1) E/4) of
   // all four in wave order and stores them
 #pragma unroll
-  for (int i = 0; i < E; ++i) red[w][i][l] = acc[i >> 5][(i >> 4) & 1][i & 15];
+  for (int i = 0; i < E; ++i) red[w][i][l] = acc[i / (16 * PJ_NSUB)][(i >> 4) % PJ_NSUB][i & 15];
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < E / PJ_WAVES; ++q) {
     const int i = w * (E / PJ_WAVES) + q;
     const float v = ((red[0][i][l] + red[1][i][l]) + red[2][i][l]) + red[3][i][l];
-    const int ms = i >> 5, ns = (i >> 4) & 1, j = i & 15;
+    const int ms = i / (16 * PJ_NSUB), ns = (i >> 4) % PJ_NSUB, j = i & 15;
     // 32x32 accumulator layout: lane l holds column l % 32, rows
     // 8 (j / 4) + 4 (l / 32) + j % 4
     const int m = mg * PJ_MG + 32 * ms + 8 * (j >> 2) + 4 * g + (j & 3);

@@ -176,7 +176,7 @@ mla_status check_append(const mla_dims* dims, const void* c_kv, const void* k_pe
 }
 
 // Split of the down-projection's K (d_model) into slices: about 256
-// workgroups (9 column tiles x slices x batch groups) so that one wave of
+// workgroups (18 column tiles x slices x batch groups) so that one wave of
 // workgroups covers the chip and reads the weights once; every slice is
 // non-empty. MLA_PROJECT_SPLITS overrides the slice count (for tuning).
 struct ProjPlan {
