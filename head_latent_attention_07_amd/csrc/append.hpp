@@ -70,6 +70,23 @@ __device__ __forceinline__ void append_write(const AppendParams& p, int b, int l
                                              const float (&x)[8], double xe, double xo,
                                              const RopeAngle& ang);
 
+// Cache row of the new token of sequence b at position pos (contiguous or
+// paged); false if it falls outside the cache (then nothing is written).
+__device__ __forceinline__ bool append_dest(const AppendParams& p, int b, int pos, int64_t* row) {
+  int64_t r;
+  if (p.block_table) {
+    if (pos < 0 || pos / p.block_size >= p.max_blocks) return false;
+    r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
+        pos % p.block_size;
+  } else {
+    if (pos < 0 || pos >= p.seq_capacity) return false;
+    r = (int64_t)b * p.seq_capacity + pos;
+  }
+  if (r < 0 || r >= p.rows) return false;
+  *row = r;
+  return true;
+}
+
 // one wave per sequence: lane l owns latent values 8l..8l+7 and, for l < 32,
 // the RoPE pair (2l, 2l+1), read from the c_kv / k_pe inputs.
 __device__ __forceinline__ void append_row(const AppendParams& p, int b, int l) {
@@ -112,15 +129,7 @@ __device__ __forceinline__ void append_write(const AppendParams& p, int b, int l
   const float r1 = (float)(xe * sn + xo * cs);
 
   int64_t r;
-  if (p.block_table) {
-    if (pos < 0 || pos / p.block_size >= p.max_blocks) return;
-    r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
-        pos % p.block_size;
-  } else {
-    if (pos < 0 || pos >= p.seq_capacity) return;
-    r = (int64_t)b * p.seq_capacity + pos;
-  }
-  if (r < 0 || r >= p.rows) return;
+  if (!append_dest(p, b, pos, &r)) return;
 
   if (p.cache_kind == CACHE_F32) {
     float* dst = (float*)p.latent + r * p.latent_stride + 8 * l;

@@ -140,3 +140,28 @@ def test_projected_token_then_decode(gpu):
     err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
     print(f"[result] decode after projected append: {err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+def test_workspace_reused_across_calls(gpu):
+    """One workspace serves calls of different batch sizes and cache types in
+    a row (its contents on entry do not matter): every call's rows match the
+    oracle."""
+    D = 2048
+    cases = [(64, "bf16"), (200, "bf16"), (3, "f32"), (130, "fp8"), (64, "bf16")]
+    ws = torch.full((max(gpu.project_workspace_size(B, D) for B, _ in cases),), 0x5A,
+                    dtype=torch.uint8, device="cuda")
+    for i, (B, cache_dtype) in enumerate(cases):
+        print(f"[case] reused workspace call {i}: B={B} cache={cache_dtype}", flush=True)
+        h, w_dkv, w_kr = synth.projection_inputs(300 + i, B, "bf16", D)
+        pos = torch.full((B,), 2, dtype=torch.int32)
+        fp8 = cache_dtype == "fp8"
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[cache_dtype]
+        cache = torch.zeros((B * 4, 576), dtype=dt, device="cuda")
+        scales = torch.ones(B * 4, dtype=torch.bfloat16, device="cuda") if fp8 else None
+        lat, rope = gpu.split_cache(cache)
+        gpu.project_append(h.cuda(), w_dkv.cuda(), w_kr.cuda(), pos.cuda(), lat, rope,
+                           heads=128, scales=scales, seq_capacity=4, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle_rows(h, w_dkv, w_kr, pos, cache_dtype)
+        rows = [b * 4 + 2 for b in range(B)]
+        check_rows(cache_values(cache, scales, rows, cache_dtype), ref, cache_dtype)
