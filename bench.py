@@ -31,7 +31,9 @@ Prints ONE JSON line (see the fields below). Options:
   --write-traffic F W CF CW  only turn four rocprofv3 counter CSVs (decode
                            kernel FETCH_SIZE, WRITE_SIZE; copy FETCH_SIZE,
                            WRITE_SIZE, taken with --copy-calibration 1024)
-                           into profiles/<kernel>_<config>_traffic.json
+                           into profiles/<kernel>_<config>_traffic.json (with
+                           --project: the two kernels of mla_project_append,
+                           summed per call)
 """
 
 from __future__ import annotations
@@ -97,28 +99,32 @@ class HipEvents:
 
 
 # the files whose text defines the split attention kernels (the launch code
-# in mla_api.hip only passes them their parameters)
+# in mla_api.hip only passes them their parameters), and the down-projection's
 KERNEL_SOURCES = ("common.hpp", "decode_mfma.hpp")
+PROJECT_SOURCES = ("common.hpp", "append.hpp", "kv_project.hpp")
+PROJECT_KERNELS = ("mla_kv_project_kernel", "mla_project_append_kernel")
+PROJECT_WORKLOAD = "b64_d7168_bf16"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "head_latent_attention_07_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, per_launch_bytes: float):
-    """HBM bytes per launch of the attention kernel from the committed
+def measured_traffic(workload: str, per_launch_bytes: float, kernel="mla_decode_bf16_kernel",
+                     sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the measured kernel(s) from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"mla_decode_bf16_kernel_{workload}_traffic.json")
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -217,17 +223,20 @@ def _counter_mean(csv_path: str, kernel_substr: str, counter: str) -> float:
     return sum(vals) / len(vals)
 
 
-def write_traffic(paths, config: str, kernel: str, copy_mib: int = 1024):
-    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by the factor between the true bytes of a
-    plain copy of copy_mib MiB and what the same counter reads for it."""
+def write_traffic(paths, config: str, kernels, copy_mib: int = 1024, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of `kernels` (summed: the launches of one call)
+    from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    the factor between the true bytes of a plain copy of copy_mib MiB and
+    what the same counter reads for it."""
     f, w, cf, cw = paths
     true_kib = copy_mib * 1024.0
     rf = true_kib / _counter_mean(cf, "copyBuffer", "FETCH_SIZE")
     wf = true_kib / _counter_mean(cw, "copyBuffer", "WRITE_SIZE")
-    fetch = _counter_mean(f, kernel, "FETCH_SIZE") * 1024.0 * rf
-    write = _counter_mean(w, kernel, "WRITE_SIZE") * 1024.0 * wf
-    rec = {"kernel": kernel, "workload": config, "kernel_source_hash": kernel_source_hash(),
+    fetch = sum(_counter_mean(f, k, "FETCH_SIZE") for k in kernels) * 1024.0 * rf
+    write = sum(_counter_mean(w, k, "WRITE_SIZE") for k in kernels) * 1024.0 * wf
+    kernel = kernels[0]
+    rec = {"kernel": " + ".join(kernels), "workload": config,
+           "kernel_source_hash": kernel_source_hash(sources),
            "read_factor": rf, "write_factor": wf, "hbm_read_bytes_per_launch": fetch,
            "hbm_write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write}
     out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
@@ -299,10 +308,12 @@ def bench_project(args):
         "ms_per_step": (t1 - t0) * 1e3 / (reps * PROJECT_SETS),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded normals, weights N(0, 1/d_model))",
-        "config": {"workload": "mla_project_append_b64_d7168_bf16", "B": B, "d_model": D,
+        "config": {"workload": "mla_project_append_" + PROJECT_WORKLOAD, "B": B, "d_model": D,
                    "weight_sets_cycled": PROJECT_SETS},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(PROJECT_WORKLOAD, nbytes, PROJECT_KERNELS[0],
+                                                 PROJECT_SOURCES),
                      "kernel": "mla_kv_project_kernel + mla_project_append_kernel",
                      "bytes_per_launch": nbytes, "avg_launch_us": avg_ms * 1e3},
     }
@@ -316,11 +327,15 @@ D_QK_ROWS = 576    # rows of W_DKV (512) and W_KR (64)
 
 def main():
     args = parse()
-    if args.project:
+    if args.project and not args.write_traffic:
         bench_project(args)
         return
     if args.write_traffic:
-        write_traffic(args.write_traffic, args.config, "mla_decode_bf16_kernel")
+        if args.project:
+            write_traffic(args.write_traffic, PROJECT_WORKLOAD, PROJECT_KERNELS,
+                          sources=PROJECT_SOURCES)
+        else:
+            write_traffic(args.write_traffic, args.config, ("mla_decode_bf16_kernel",))
         return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)

@@ -165,3 +165,26 @@ def test_workspace_reused_across_calls(gpu):
         ref, _ = oracle_rows(h, w_dkv, w_kr, pos, cache_dtype)
         rows = [b * 4 + 2 for b in range(B)]
         check_rows(cache_values(cache, scales, rows, cache_dtype), ref, cache_dtype)
+
+
+def test_project_append_paged_fp8(gpu):
+    """fp8 cache through a block table (the two-launch form: whole-row
+    scale), rows in three different blocks, against the oracle's rows."""
+    B, bs = 3, 32
+    h, w_dkv, w_kr = synth.projection_inputs(55, B, "bf16")
+    table = torch.tensor([[4, 1], [0, 5], [2, 3]], dtype=torch.int32)
+    pos = torch.tensor([33, 0, 63], dtype=torch.int32)
+    rows = [orc.paged_row(table.numpy(), b, int(pos[b]), bs) for b in range(B)]
+    assert rows == [32 + 1, 0, 3 * 32 + 31]
+    cache = torch.zeros((6 * bs, 576), dtype=torch.uint8, device="cuda")
+    scales = torch.ones(6 * bs, dtype=torch.bfloat16, device="cuda")
+    lat, rope = gpu.split_cache(cache)
+    gpu.project_append(h.cuda(), w_dkv.cuda(), w_kr.cuda(), pos.cuda(), lat, rope, heads=128,
+                       scales=scales, block_table=table.cuda(), block_size=bs)
+    torch.cuda.synchronize()
+    ref, ref_scales = oracle_rows(h, w_dkv, w_kr, pos, "fp8")
+    check_rows(cache_values(cache, scales, rows, "fp8"), ref, "fp8")
+    got_s = to_f64(scales.cpu()[rows], "bf16")
+    assert np.max(np.abs(got_s / np.array(ref_scales) - 1)) <= 2 ** -7
+    others = sorted(set(range(6 * bs)) - set(rows))
+    assert not cache.cpu()[others].any()
