@@ -51,6 +51,8 @@ def check_rows(got, ref, cache_dtype):
     ("bf16", "bf16", 1, 64),        # a single 64-wide chunk
     ("f32", "f32", 3, 512),         # fp32 operands and cache
     ("f32", "bf16", 33, 2048),      # fp32 operands, bf16 cache, 33 rows
+    ("f32", "fp8", 5, 512),         # fp32 operands, fp8 cache (two launches)
+    ("bf16", "bf16", 1000, 1024),   # eight batch groups of 128, the last ragged
 ])
 def test_project_append_contiguous(gpu, act, cache_dtype, B, d_model):
     cap = 8
