@@ -23,7 +23,7 @@ D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 
 SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
-           "mla_project_append", "mla_project_workspace_size")
+           "mla_project_append", "mla_project_workspace_size", "mla_project")
 
 
 class MLAError(RuntimeError):
@@ -39,7 +39,8 @@ class Dims(ctypes.Structure):
 
 class AppendArgs(ctypes.Structure):
     _fields_ = [("c_kv", ctypes.c_void_p), ("k_pe", ctypes.c_void_p), ("in_dtype", ctypes.c_int),
-                ("positions", ctypes.c_void_p), ("rope_theta", ctypes.c_float)]
+                ("positions", ctypes.c_void_p), ("rope_theta", ctypes.c_float),
+                ("projected", ctypes.c_void_p), ("d_model", ctypes.c_int32)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -87,6 +88,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = common + [_P, _I32, _I32] + tail
     lib.mla_project_workspace_size.restype = _SZ
     lib.mla_project_workspace_size.argtypes = [_I32, _I32]
+    lib.mla_project.restype = ctypes.c_int
+    lib.mla_project.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int, _I32, _I32, _P, _SZ,
+                                _P]
     lib.mla_project_append.restype = ctypes.c_int
     lib.mla_project_append.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int, _I32, _P,
                                        _I32, _P, _I64, _P, _I64, _P, ctypes.c_int, _I64, _I64, _P,
@@ -133,7 +137,9 @@ def _stream(stream=None) -> int:
 
 def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=None):
     """mla_decode_options for the call (None when every field is a default).
-    `append` = (c_kv, k_pe, positions[, rope_theta]) appends those rows first."""
+    `append` = (c_kv, k_pe, positions[, rope_theta]) appends those rows first;
+    (None, None, positions, rope_theta, workspace, d_model) appends the rows of
+    a preceding project() call whose workspace that is."""
     if not num_splits and events is None and append is None:
         return None
     o = DecodeOptions()
@@ -143,7 +149,12 @@ def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=
     if append is not None:
         c_kv, k_pe, positions = append[:3]
         theta = append[3] if len(append) > 3 else 10000.0
-        a = AppendArgs(_ptr(c_kv), _ptr(k_pe), dtype_code(c_kv.dtype), _ptr(positions), theta)
+        if len(append) > 4:          # rows from a projection workspace
+            a = AppendArgs(None, None, MLA_F32, _ptr(positions), theta, _ptr(append[4]),
+                           int(append[5]))
+        else:
+            a = AppendArgs(_ptr(c_kv), _ptr(k_pe), dtype_code(c_kv.dtype), _ptr(positions), theta,
+                           None, 0)
         o._append_keep = a            # the struct must outlive the call
         o.append = ctypes.pointer(a)
     return ctypes.byref(o)
@@ -202,6 +213,16 @@ def project_append(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor
         _ptr(positions), B, _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
         _ptr(scales), dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table),
         max_blocks, block_size, rope_theta, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def project(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+            workspace: torch.Tensor, *, heads: int = 128, stream=None) -> None:
+    """The down-projection alone (mla_project): partial sums of the new rows
+    left in `workspace` for a following decode call's append."""
+    B, D = hidden.shape
+    _check(load().mla_project(ctypes.byref(dims(heads)), _ptr(hidden), _ptr(w_dkv), _ptr(w_kr),
+                              dtype_code(hidden.dtype), D, B, _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
 
 
 def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,

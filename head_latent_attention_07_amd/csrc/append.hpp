@@ -23,6 +23,11 @@ struct AppendParams {
   const int32_t* block_table;
   int max_blocks, block_size;
   double theta;
+  // instead of c_kv / k_pe: the fp32 partial sums [S, B, 576] that a
+  // down-projection left in its workspace (nullptr: use c_kv / k_pe)
+  const float* part;
+  int part_slices;
+  int rows_in_batch;   // B of the partials' [S, B, 576] layout
 };
 
 // OCP e4m3fn code of v, round to nearest even, saturating to +-448.
@@ -87,9 +92,55 @@ __device__ __forceinline__ bool append_dest(const AppendParams& p, int b, int po
   return true;
 }
 
+// The row of sequence b as the sum of a down-projection's S partials, added
+// in the order of the down-projection's own append kernel (slices of each
+// residue mod 4 in increasing order, then the four residues in order), so
+// both give the same bits. Lane layout as in append_row.
+__device__ __forceinline__ void append_row_projected(const AppendParams& p, int b, int l) {
+  const int lp = l & (D_R / 2 - 1), S = p.part_slices;
+  float acc[4][10];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 10; ++i) acc[r][i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    f32x4 v0[4], v1[4];
+    f32x2 pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {   // clamped loads, the extra ones discarded
+      const float* row = p.part + ((int64_t)min(s0 + r, S - 1) * p.rows_in_batch + b) * D_QK;
+      v0[r] = *(const f32x4*)(row + 8 * l);
+      v1[r] = *(const f32x4*)(row + 8 * l + 4);
+      pr[r] = *(const f32x2*)(row + D_C + 2 * lp);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (s0 + r < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[r][i] += v0[r][i];
+          acc[r][4 + i] += v1[r][i];
+        }
+        acc[r][8] += pr[r][0];
+        acc[r][9] += pr[r][1];
+      }
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = ((acc[0][i] + acc[1][i]) + acc[2][i]) + acc[3][i];
+  const float xe = ((acc[0][8] + acc[1][8]) + acc[2][8]) + acc[3][8];
+  const float xo = ((acc[0][9] + acc[1][9]) + acc[2][9]) + acc[3][9];
+  append_store(p, b, l, x, (double)xe, (double)xo);
+}
+
 // one wave per sequence: lane l owns latent values 8l..8l+7 and, for l < 32,
 // the RoPE pair (2l, 2l+1), read from the c_kv / k_pe inputs.
 __device__ __forceinline__ void append_row(const AppendParams& p, int b, int l) {
+  if (p.part) {
+    append_row_projected(p, b, l);
+    return;
+  }
   float x[8];
   if (p.in_bf16) {
     const bf16x8 v = *(const bf16x8*)((const bf16*)p.c_kv + (int64_t)b * D_C + 8 * l);

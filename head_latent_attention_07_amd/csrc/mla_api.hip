@@ -172,6 +172,9 @@ mla_status check_append(const mla_dims* dims, const void* c_kv, const void* k_pe
   out->max_blocks = max_blocks;
   out->block_size = block_size;
   out->theta = (double)rope_theta;
+  out->part = nullptr;
+  out->part_slices = 0;
+  out->rows_in_batch = batch;
   return MLA_OK;
 }
 
@@ -256,10 +259,19 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   const bool do_append = opts && opts->append;
   if (do_append) {
     const mla_append_args* a = opts->append;
-    MLA_TRY(check_append(dims, a->c_kv, a->k_pe, a->in_dtype, a->positions, batch,
-                         const_cast<void*>(latent), ls, const_cast<void*>(rope), rs,
-                         const_cast<void*>(scales), cdt, rows, seq_capacity, block_table,
-                         max_blocks, block_size, a->rope_theta, &app));
+    // rows from a down-projection's workspace: its partials stand in for the
+    // inputs in the checks, and the row values are their sums
+    const void* ci = a->projected ? a->projected : a->c_kv;
+    const void* ki = a->projected ? a->projected : a->k_pe;
+    const mla_dtype in_dt = a->projected ? MLA_F32 : a->in_dtype;
+    MLA_TRY(check_append(dims, ci, ki, in_dt, a->positions, batch, const_cast<void*>(latent), ls,
+                         const_cast<void*>(rope), rs, const_cast<void*>(scales), cdt, rows,
+                         seq_capacity, block_table, max_blocks, block_size, a->rope_theta, &app));
+    if (a->projected) {
+      if (a->d_model <= 0 || a->d_model % PJ_CHUNK != 0) return MLA_ERR_INVALID_ARG;
+      app.part = (const float*)a->projected;
+      app.part_slices = project_plan(batch, a->d_model).S;
+    }
   }
   const Plan pl = make_plan(B, H, max_len, act, opts);
   const WsLayout wl = ws_layout(B, H, pl, act);
@@ -461,6 +473,37 @@ size_t mla_project_workspace_size(int32_t batch, int32_t d_model) {
   if (batch < 0 || d_model <= 0 || d_model % PJ_CHUNK != 0) return 0;
   if (batch == 0) return 256;
   return project_ws_bytes(batch, d_model);
+}
+
+mla_status mla_project(const mla_dims* dims, const void* hidden, const void* w_dkv,
+                       const void* w_kr, mla_dtype act, int32_t d_model, int32_t batch,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dims || batch < 0) return MLA_ERR_INVALID_ARG;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (act != MLA_F32 && act != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d_model <= 0 || d_model % PJ_CHUNK != 0) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!hidden || !w_dkv || !w_kr || !aligned16(hidden) || !aligned16(w_dkv) || !aligned16(w_kr))
+    return MLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < project_ws_bytes(batch, d_model))
+    return MLA_ERR_WORKSPACE;
+  const ProjPlan pl = project_plan(batch, d_model);
+  ProjectParams pp;
+  pp.h = hidden;
+  pp.w_dkv = w_dkv;
+  pp.w_kr = w_kr;
+  pp.part = (float*)workspace;
+  pp.B = batch;
+  pp.D = d_model;
+  pp.S = pl.S;
+  pp.cps = pl.cps;
+  (void)hipGetLastError();
+  const int grid = PJ_NTILES * pl.S * pl.mgroups;
+  if (act == MLA_BF16)
+    launch_project<bf16>(pp, pl.msub, grid, stream);
+  else
+    launch_project<float>(pp, pl.msub, grid, stream);
+  return launch_status();
 }
 
 mla_status mla_project_append(const mla_dims* dims, const void* hidden, const void* w_dkv,

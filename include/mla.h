@@ -81,6 +81,12 @@ typedef struct mla_append_args {
   mla_dtype in_dtype;         /* MLA_F32 or MLA_BF16 */
   const int32_t* positions;   /* [batch] 0-based position of each new token */
   float rope_theta;           /* RoPE base (10000 in the DeepSeek-V3 setting) */
+  /* If non-NULL, c_kv, k_pe and in_dtype are ignored: the rows are those of
+   * a preceding mla_project call on the same stream with the same batch and
+   * d_model, whose workspace this is (the sums of its partial products).
+   * The cache then receives exactly what mla_project_append would write. */
+  const void* projected;
+  int32_t d_model;            /* with projected: its hidden width */
 } mla_append_args;
 
 /* Optional tuning and instrumentation for the decode calls (pass NULL for the
@@ -198,7 +204,20 @@ mla_status mla_project_append(const mla_dims* dims, const void* hidden, const vo
                               int32_t max_blocks_per_seq, int32_t block_size, float rope_theta,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by mla_project_append (0 on invalid sizes). */
+/*
+ * mla_project: the first half of mla_project_append alone. It leaves the
+ * new rows' products, as partial sums, in `workspace` for the append of a
+ * following decode call (mla_append_args.projected), so a decode step runs
+ * the down-projection, the append, the absorption and the attention in
+ * four launches without a launch of its own for the append. Arguments,
+ * sizes and errors as for mla_project_append (the same workspace size).
+ */
+mla_status mla_project(const mla_dims* dims, const void* hidden, const void* w_dkv,
+                       const void* w_kr, mla_dtype act_dtype, int32_t d_model, int32_t batch,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by mla_project_append and mla_project (0 on invalid
+ * sizes). */
 size_t mla_project_workspace_size(int32_t batch, int32_t d_model);
 
 /* Workspace bytes needed by mla_decode / mla_decode_paged for these sizes

@@ -190,3 +190,41 @@ def test_project_append_paged_fp8(gpu):
     assert np.max(np.abs(got_s / np.array(ref_scales) - 1)) <= 2 ** -7
     others = sorted(set(range(6 * bs)) - set(rows))
     assert not cache.cpu()[others].any()
+
+
+@pytest.mark.parametrize("cfg,cache_dtype", [(3, "bf16"), (2, "fp8")])
+def test_decode_append_from_projection_equals_two_calls(gpu, cfg, cache_dtype):
+    """mla_project, then a decode call whose append takes the projection's
+    workspace (mla_append_args.projected), writes the same cache bytes and
+    returns the same output and lse bits as mla_project_append followed by
+    a decode without append (the partial sums are added in the same order)."""
+    import dataclasses
+    B, N, D = 4, 300, 2048
+    lengths = torch.tensor([N, 200, 1, 64][:B], dtype=torch.int32)
+    inp = synth.make_inputs(cfg, B=B, N=N, lengths=lengths, cache_dtype=cache_dtype,
+                            paged=(cfg == 3)).to("cuda")
+    h, w_dkv, w_kr = [t.cuda() for t in synth.projection_inputs(66, B, "bf16", D)]
+    pos = (inp.lengths - 1).contiguous()
+    print(f"[case] projected append in decode cfg={cfg} cache={cache_dtype}", flush=True)
+
+    def fresh():
+        return dataclasses.replace(inp, cache=inp.cache.clone(),
+                                   scales=None if inp.scales is None else inp.scales.clone())
+
+    two = fresh()
+    lat, rope = gpu.split_cache(two.cache)
+    gpu.project_append(h, w_dkv, w_kr, pos, lat, rope, heads=inp.H, scales=two.scales,
+                       seq_capacity=inp.seq_capacity, block_table=inp.block_table,
+                       block_size=inp.block_size)
+    out_a, lse_a = gpu.decode_inputs(two)
+    one = fresh()
+    ws = torch.empty(gpu.project_workspace_size(B, D), dtype=torch.uint8, device="cuda")
+    gpu.project(h, w_dkv, w_kr, ws, heads=inp.H)
+    out_b, lse_b = gpu.decode_inputs(one, append=(None, None, pos, 10000.0, ws, D))
+    torch.cuda.synchronize()
+    assert not torch.equal(two.cache.view(torch.uint8), inp.cache.view(torch.uint8))
+    assert torch.equal(two.cache.view(torch.uint8), one.cache.view(torch.uint8))
+    if two.scales is not None:
+        assert torch.equal(two.scales, one.scales)
+    assert torch.equal(out_a.view(torch.uint8), out_b.view(torch.uint8))
+    assert torch.equal(lse_a, lse_b)
