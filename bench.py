@@ -25,6 +25,11 @@ Prints ONE JSON line (see the fields below). Options:
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
+  --with-projection        the step also computes the new rows from the tokens'
+                           hidden states (d_model 7168): mla_project, then the
+                           decode call appends from its workspace (with
+                           --separate-append: mla_project_append, then a decode
+                           call without append)
   --project                only measure mla_project_append (the down-projection
                            of 64 new tokens' hidden states, d_model 7168, bf16,
                            and the append of their rows) and print its own line
@@ -68,6 +73,7 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--write-traffic", nargs=4, default=None)
     ap.add_argument("--project", action="store_true")
+    ap.add_argument("--with-projection", action="store_true")
     return ap.parse_args()
 
 
@@ -371,8 +377,13 @@ def main():
                          dtype=torch.uint8, device=dev)
         out = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-        layers.append(dict(inp=inp, lat=lat, rope=rope, c=c_new, k=k_new, pos=pos, ws=ws,
-                           out=out, lse=lse))
+        L = dict(inp=inp, lat=lat, rope=rope, c=c_new, k=k_new, pos=pos, ws=ws, out=out, lse=lse)
+        if args.with_projection:
+            L["proj"] = synth.projection_inputs(9100 + 10 * layer, B, "bf16", synth.D_MODEL,
+                                                device=dev)
+            L["pws"] = torch.empty(mla.project_workspace_size(B, synth.D_MODEL),
+                                   dtype=torch.uint8, device=dev)
+        layers.append(L)
     torch.cuda.synchronize()
     inp0 = layers[0]["inp"]
     B, H = inp0.B, inp0.H
@@ -386,6 +397,20 @@ def main():
     def step(L, events=None):
         inp = L["inp"]
         new_rows = (L["c"], L["k"], L["pos"])
+        if args.with_projection:
+            h, wd, wk = L["proj"]
+            if args.separate_append:
+                mla.project_append(h, wd, wk, L["pos"], L["lat"], L["rope"], heads=H,
+                                   scales=inp.scales, seq_capacity=inp.seq_capacity,
+                                   block_table=inp.block_table, block_size=inp.block_size,
+                                   workspace=L["pws"])
+                new_rows = None
+            else:
+                mla.project(h, wd, wk, L["pws"], heads=H)
+                new_rows = (None, None, L["pos"], 10000.0, L["pws"], synth.D_MODEL)
+            mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events,
+                              append=new_rows)
+            return
         if args.separate_append:
             mla.cache_append(*new_rows, L["lat"], L["rope"], heads=H, scales=inp.scales,
                              seq_capacity=inp.seq_capacity, block_table=inp.block_table,
@@ -418,6 +443,8 @@ def main():
                 3: "mla_decode_b64_h128_ragged1024to4096_paged_bf16",
                 4: "mla_decode_b4_h128_n131072_bf16",
                 5: "mla_decode_b32_h128_n32768_fp8cache_per_layer"}[cfg]
+    if args.with_projection:
+        workload += "_with_down_projection_d7168"
     traffic = measured_traffic(str(cfg), cache_bytes)
     result = {
         "metric": METRIC,
