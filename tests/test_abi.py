@@ -125,3 +125,24 @@ def test_project_argument_errors():
     assert call(ws=None) == 3
     assert call(ws_bytes=1024) == 3
     assert call(batch=0) == 0
+
+
+def test_projected_append_argument_errors():
+    """A decode call whose append takes a projection workspace checks its
+    d_model (a positive multiple of 64) before launching anything; mla_project
+    checks its sizes and workspace like mla_project_append."""
+    lib = mla.load()
+    d = mla.dims(128)
+    p = ctypes.c_void_p(16)
+    for d_model in (0, 100):
+        a = mla.AppendArgs(None, None, mla.MLA_F32, 16, 10000.0, 16, d_model)
+        o = mla.DecodeOptions()
+        o.append = ctypes.pointer(a)
+        st = lib.mla_decode(ctypes.byref(d), p, p, p, p, 1, p, 576, p, 576, None, 1, 4096, 1024,
+                            p, 4, 1024, 0.07, p, None, p, 1 << 30, ctypes.byref(o), None)
+        assert st == 1, (d_model, st)
+    assert lib.mla_project(ctypes.byref(d), p, p, p, 1, 100, 4, p, 1 << 30, None) == 1
+    assert lib.mla_project(ctypes.byref(d), p, p, None, 1, 7168, 4, p, 1 << 30, None) == 1
+    assert lib.mla_project(ctypes.byref(d), p, p, p, 2, 7168, 4, p, 1 << 30, None) == 2
+    assert lib.mla_project(ctypes.byref(d), p, p, p, 1, 7168, 4, p, 1024, None) == 3
+    assert lib.mla_project(ctypes.byref(d), p, p, p, 1, 7168, 0, p, 0, None) == 0
