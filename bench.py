@@ -64,14 +64,16 @@ N_LAYERS_CYCLED = 3
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--config", default="3u")
+    ap.add_argument("--config", default="3u", choices=["1", "2", "3", "3u", "4", "5"])
+    ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--write-traffic", nargs=4, default=None)
+    ap.add_argument("--write-mfma", nargs=2, default=None, metavar=("COUNTERS_CSV", "TRACE_CSV"))
     ap.add_argument("--project", action="store_true")
     ap.add_argument("--with-projection", action="store_true")
     return ap.parse_args()
@@ -135,44 +137,87 @@ def measured_traffic(workload: str, per_launch_bytes: float, kernel="mla_decode_
     return t.get("hbm_bytes_per_launch")
 
 
+def _host_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(cfg, seconds: float):
     """The oracle as it stands (float64, non-absorbed), on a bounded sample of
     the same workload: whole sequences (all heads) until `seconds` elapse."""
     import numpy as np
+    import torch
     import synth
     from oracle import mla_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = _host_threads()
     inp = synth.make_inputs(cfg)
+    act = "f32" if inp.q_nope.dtype == torch.float32 else "bf16"
 
     def f64(t, kind):
         return orc.decode_storage(synth.raw_bits(t), kind)
 
-    wuk, wuv = f64(inp.w_uk, "bf16"), f64(inp.w_uv, "bf16")
+    wuk, wuv = f64(inp.w_uk, act), f64(inp.w_uv, act)
     table = None if inp.block_table is None else inp.block_table.numpy()
     done = 0
-    tokens = 0
     t0 = time.perf_counter()
     while True:
         b = done % inp.B
         n = int(inp.lengths[b])
-        rows = orc.gather_rows(b, n, seq_capacity=inp.seq_capacity, block_table=table,
-                               block_size=inp.block_size)
-        import torch
-        vals = f64(inp.cache[torch.from_numpy(rows)], inp.cache_dtype)
-        orc.decode(f64(inp.q_nope[b:b + 1], "bf16"), f64(inp.q_pe[b:b + 1], "bf16"), wuk, wuv,
+        rows = torch.from_numpy(orc.gather_rows(b, n, seq_capacity=inp.seq_capacity,
+                                                block_table=table, block_size=inp.block_size))
+        vals = f64(inp.cache[rows], inp.cache_dtype)
+        if inp.scales is not None:
+            vals = vals * f64(inp.scales[rows], "bf16")[:, None]
+        orc.decode(f64(inp.q_nope[b:b + 1], act), f64(inp.q_pe[b:b + 1], act), wuk, wuv,
                    [vals[:, :512]], [vals[:, 512:]], inp.scale)
         done += 1
-        tokens += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} sequence(s) x 128 heads of the same workload (N={inp.max_len}), "
-                      f"float64 non-absorbed oracle, {dt:.1f} s"}
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} sequence(s) x {inp.H} heads of the same workload "
+                      f"(N={inp.max_len}), float64 non-absorbed oracle, {dt:.1f} s"}
+
+
+def cpu_absorbed_f32(cfg, seconds: float):
+    """A same-algorithm CPU baseline (not the oracle): the absorbed form in
+    float32 on the host cores (torch CPU matrix products, all heads of a
+    sequence at once), whole sequences until `seconds` elapse."""
+    import torch
+    import synth
+    inp = synth.make_inputs(cfg)
+    threads = torch.get_num_threads()
+    wuk, wuv = inp.w_uk.float(), inp.w_uv.float()
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % inp.B
+        n = int(inp.lengths[b])
+        if inp.block_table is None:
+            rows = b * inp.seq_capacity + torch.arange(n)
+        else:
+            t = torch.arange(n)
+            rows = inp.block_table[b].long()[t // inp.block_size] * inp.block_size + t % inp.block_size
+        sel = inp.cache[rows]
+        if inp.cache_dtype == "fp8":
+            x = sel.view(torch.float8_e4m3fn).float() * inp.scales[rows].float()[:, None]
+        else:
+            x = sel.float()
+        C, R = x[:, :512], x[:, 512:]
+        q_lat = torch.einsum("hk,hkc->hc", inp.q_nope[b].float(), wuk)
+        S = inp.scale * (C @ q_lat.T + R @ inp.q_pe[b].float().T)
+        P = torch.softmax(S, dim=0)
+        torch.einsum("hc,hcv->hv", P.T @ C, wuv)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "absorbed float32 (same algorithm as the GPU path, torch CPU)",
+            "sample": f"{done} sequence(s) x {inp.H} heads (N={inp.max_len}), {dt:.1f} s"}
 
 
 def cpu_baseline_project(seconds: float):
@@ -331,9 +376,87 @@ def bench_project(args):
 D_QK_ROWS = 576    # rows of W_DKV (512) and W_KR (64)
 
 
+SIMD_COUNT = 1024            # MI355X: 256 CUs x 4 SIMDs
+
+WORKLOADS = {"1": "mla_decode_b1_h16_n512_f32", "2": "mla_decode_b1_h128_n4096_bf16",
+             "3u": "mla_decode_b64_h128_n4096_paged_bf16",
+             "3": "mla_decode_b64_h128_ragged1024to4096_paged_bf16",
+             "4": "mla_decode_b4_h128_n131072_bf16",
+             "5": "mla_decode_b32_h128_n32768_fp8cache_per_layer"}
+FULL_STEP_WORKLOAD = "mla_decode_61layer_step_b32_h128_n32768_fp8cache"
+
+
+def decode_kernel_name(cache_dtype: str) -> str:
+    return {"f32": "mla_decode_f32_kernel", "bf16": "mla_decode_bf16_kernel",
+            "fp8": "mla_decode_fp8_kernel"}[cache_dtype]
+
+
+def write_mfma(counters_csv: str, trace_csv: str, config: str, kernel: str):
+    """MFMA evidence for one kernel from a rocprofv3 run with --kernel-trace
+    and --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+    GRBM_GUI_ACTIVE: per-dispatch means, the FLOP the matrix cores executed
+    (MOPS x 512, rocprofv3's MfmaFlopsBF16), the busy fraction of the
+    matrix pipes (MfmaUtil = busy cycles summed over the SIMDs / (the GPU's
+    active cycles x SIMDs)), and the GPU clock while the kernel ran (active
+    cycles of the busiest counter instance / the traced duration)."""
+    import csv
+    rows = [r for r in csv.DictReader(open(counters_csv)) if kernel in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"no {kernel} rows in {counters_csv}")
+    by = {}
+    for r in rows:
+        by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: sum(v) / len(v) for k, v in by.items()}
+    tr = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr)
+    dur_ns = durs[len(durs) // 2]
+    util = mean["MfmaUtil"]
+    busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"]
+    grbm_max = busy / (util / 100.0 * SIMD_COUNT) if util > 0 else None
+    flops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    rec = {"kernel": kernel, "workload": config, "kernel_source_hash": kernel_source_hash(),
+           "dispatches": len(rows) // max(1, len(by)), "counters_mean": mean,
+           "median_duration_us": dur_ns / 1e3,
+           "mfma_util_pct": util,
+           "mfma_bf16_flop_per_dispatch": flops,
+           "mfma_bf16_tflops": flops / dur_ns / 1e3,
+           "mfma_bf16_frac_of_peak": flops / dur_ns / 1e3 / MFMA_BF16_PEAK_TFLOPS,
+           "gpu_active_cycles_max_instance": grbm_max,
+           "clock_ghz": grbm_max / dur_ns if grbm_max else None,
+           "peak_used": {"bf16_dense_tflops": MFMA_BF16_PEAK_TFLOPS, "simds": SIMD_COUNT}}
+    out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_mfma.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def measured_mfma(workload: str, kernel: str):
+    """The committed MFMA counter record of the kernel on this workload, if it
+    was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_mfma.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {k: t[k] for k in ("mfma_util_pct", "mfma_bf16_tflops", "mfma_bf16_frac_of_peak",
+                              "clock_ghz", "median_duration_us")}
+
+
+def percentile(vals, q):
+    v = sorted(vals)
+    k = (len(v) - 1) * q / 100.0
+    i = int(math.floor(k))
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (k - i)
+
+
 def main():
     args = parse()
     if args.project and not args.write_traffic:
+        args.steps = 1000 if args.steps is None else args.steps
+        args.warmup = 300 if args.warmup is None else args.warmup
         bench_project(args)
         return
     if args.write_traffic:
@@ -341,7 +464,12 @@ def main():
             write_traffic(args.write_traffic, PROJECT_WORKLOAD, PROJECT_KERNELS,
                           sources=PROJECT_SOURCES)
         else:
-            write_traffic(args.write_traffic, args.config, ("mla_decode_bf16_kernel",))
+            kern = "mla_decode_fp8_kernel" if args.config == "5" else "mla_decode_bf16_kernel"
+            write_traffic(args.write_traffic, args.config, (kern,))
+        return
+    if args.write_mfma:
+        kern = "mla_decode_fp8_kernel" if args.config == "5" else "mla_decode_bf16_kernel"
+        write_mfma(*args.write_mfma, args.config, kern)
         return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
@@ -357,33 +485,46 @@ def main():
     import synth
 
     mla.load()
-    cfg = args.config if args.config in ("3u", "3", "4", "5") else "3u"
-    cfg = cfg if cfg == "3u" else int(cfg)
+    cfg_key = args.config
+    cfg = cfg_key if cfg_key == "3u" else int(cfg_key)
+    # config 5 with --layers 61: a step is the whole 61-layer decode step
+    # (every layer resident, one decode call per layer); otherwise a step is
+    # one layer's decode call, cycling over a few resident layers so that no
+    # step finds its cache in the last-level cache left by the previous one
+    full_step = cfg == 5 and args.layers > 1
+    n_layers = args.layers if full_step else (args.layers or N_LAYERS_CYCLED)
+    per_step = n_layers if full_step else 1
+    steps = args.steps if args.steps is not None else (50 if full_step else 1000)
+    warmup = args.warmup if args.warmup is not None else (10 if full_step else 300)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    # ---- inputs (resident in HBM), one set per cycled layer ----
+    # ---- inputs (resident in HBM), one set per layer ----
     layers = []
-    for layer in range(N_LAYERS_CYCLED):
+    for layer in range(n_layers):
         gen = "cuda" if cfg == 5 else "cpu"
         inp = synth.make_inputs(cfg, layer=layer, gen_device=gen).to(dev)
         lat, rope = mla.split_cache(inp.cache)
         B, H = inp.B, inp.H
+        act = mla.dtype_code(inp.q_nope.dtype)
         # the new token of each sequence sits at position N_b - 1
-        c_new, k_new = synth.append_inputs(7000 + layer, B, "bf16", device=dev)
+        c_new, k_new = synth.append_inputs(7000 + layer, B, inp.act, device=dev)
         pos = (inp.lengths - 1).to(dev)
         cdt = mla.dtype_code(inp.cache.dtype)
-        ws = torch.empty(mla.workspace_size(H, B, inp.max_len, mla.MLA_BF16, cdt),
+        ws = torch.empty(mla.workspace_size(H, B, inp.max_len, act, cdt),
                          dtype=torch.uint8, device=dev)
-        out = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, H, 128), dtype=inp.q_nope.dtype, device=dev)
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         L = dict(inp=inp, lat=lat, rope=rope, c=c_new, k=k_new, pos=pos, ws=ws, out=out, lse=lse)
         if args.with_projection:
-            L["proj"] = synth.projection_inputs(9100 + 10 * layer, B, "bf16", synth.D_MODEL,
+            L["proj"] = synth.projection_inputs(9100 + 10 * layer, B, inp.act, synth.D_MODEL,
                                                 device=dev)
             L["pws"] = torch.empty(mla.project_workspace_size(B, synth.D_MODEL),
                                    dtype=torch.uint8, device=dev)
         layers.append(L)
+        if full_step and (layer + 1) % 10 == 0:
+            print(f"bench.py: {layer + 1} of {n_layers} layers resident", file=sys.stderr,
+                  flush=True)
     torch.cuda.synchronize()
     inp0 = layers[0]["inp"]
     B, H = inp0.B, inp0.H
@@ -394,7 +535,7 @@ def main():
 
     ev = HipEvents()
 
-    def step(L, events=None):
+    def layer_call(L, events=None):
         inp = L["inp"]
         new_rows = (L["c"], L["k"], L["pos"])
         if args.with_projection:
@@ -419,64 +560,91 @@ def main():
         mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events,
                           append=new_rows)
 
-    for i in range(args.warmup):
-        step(layers[i % N_LAYERS_CYCLED])
+    def step(i, events=None):
+        if full_step:
+            for k, L in enumerate(layers):
+                layer_call(L, events[k] if events else None)
+        else:
+            layer_call(layers[i % n_layers], events[0] if events else None)
+
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = [[(ev.create(), ev.create()) for _ in range(per_step)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(layers[i % N_LAYERS_CYCLED], events=pairs[i])
+    for i in range(steps):
+        step(i, events=pairs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    attn_ms = [ev.elapsed_ms(a, b) for ps in pairs for a, b in ps]
+    for ps in pairs:
+        for a, b in ps:
+            ev.destroy(a)
+            ev.destroy(b)
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = B * args.steps / (t1 - t0)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    tokens_per_s = B * steps / (t1 - t0)
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     achieved_gbs = cache_bytes / (attn_avg_ms * 1e-3) / 1e9
-    workload = {"3u": "mla_decode_b64_h128_n4096_paged_bf16",
-                3: "mla_decode_b64_h128_ragged1024to4096_paged_bf16",
-                4: "mla_decode_b4_h128_n131072_bf16",
-                5: "mla_decode_b32_h128_n32768_fp8cache_per_layer"}[cfg]
+    workload = FULL_STEP_WORKLOAD if full_step else WORKLOADS[cfg_key]
     if args.with_projection:
         workload += "_with_down_projection_d7168"
-    traffic = measured_traffic(str(cfg), cache_bytes)
+    kernel = decode_kernel_name(inp0.cache_dtype)
+    traffic = measured_traffic(cfg_key, cache_bytes, kernel)
+    dtype = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp8cache"}[inp0.cache_dtype]
+    config = {"workload": workload, "B": B, "H": H, "N_max": inp0.max_len,
+              "cache_token_rows": tok_rows, "paged": inp0.paged,
+              "block_size": inp0.block_size if inp0.paged else None,
+              "d_c": 512, "d_rope": 64, "d_nope": 128, "d_v": 128}
+    if full_step:
+        config["layers_per_step"] = n_layers
+    else:
+        config["layers_cycled"] = n_layers
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if inp0.cache_dtype == "bf16" else "bf16+fp8cache",
+        "dtype": dtype,
         "data": "synthetic (seeded normals; random-init weights of the DeepSeek-V3 MLA widths)",
-        "config": {"workload": workload, "B": B, "H": H, "N_max": inp0.max_len,
-                   "cache_token_rows": tok_rows, "paged": inp0.paged,
-                   "block_size": inp0.block_size if inp0.paged else None,
-                   "d_c": 512, "d_rope": 64, "d_nope": 128, "d_v": 128,
-                   "layers_cycled": N_LAYERS_CYCLED},
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "mla_decode_bf16_kernel" if inp0.cache_dtype == "bf16"
-                     else "mla_decode_fp8_kernel",
-                     "bytes_per_launch": cache_bytes, "avg_launch_us": attn_avg_ms * 1e3},
+                     "kernel": kernel, "bytes_per_launch": cache_bytes,
+                     "avg_launch_us": attn_avg_ms * 1e3,
+                     "launch_us_p10_p50_p90": [percentile(attn_ms, q) * 1e3 for q in (10, 50, 90)]},
         "latent_cache_gbs": achieved_gbs,
         "latent_cache_pct_of_hbm_peak": 100.0 * achieved_gbs / HBM_PEAK_GBS,
-        "attention_mfma_tflops": flop_attn / (attn_avg_ms * 1e-3) / 1e12,
-        "attention_mfma_frac_of_bf16_peak": flop_attn / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "step_cache_gbs": cache_bytes / (ms_per_step * 1e-3) / 1e9,
+        # algorithmic: the attention FLOP of the launch / its event time
+        "attention_mfma_algorithmic_tflops": flop_attn / (attn_avg_ms * 1e-3) / 1e12,
+        "attention_mfma_algorithmic_frac_of_bf16_peak":
+            flop_attn / (attn_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        # counters: the committed rocprofv3 record of this kernel and workload
+        "mfma_counters": measured_mfma(cfg_key, kernel),
+        "step_cache_gbs": cache_bytes * per_step / (ms_per_step * 1e-3) / 1e9,
     }
+    if full_step:
+        step_bytes = cache_bytes * per_step
+        step_flop = flop_attn * per_step
+        hbm_floor_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        mfma_floor_ms = step_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+        result["full_step"] = {
+            "cache_bytes_per_step": step_bytes, "attention_flop_per_step": step_flop,
+            "hbm_floor_ms": hbm_floor_ms, "bf16_mfma_floor_ms": mfma_floor_ms,
+            "fp8_mfma_floor_ms": mfma_floor_ms / 2,
+            "frac_of_hbm_floor": hbm_floor_ms / ms_per_step,
+            "frac_of_bf16_mfma_floor": mfma_floor_ms / ms_per_step}
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg if cfg != 5 else 5, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        result["cpu_absorbed_f32"] = cpu_absorbed_f32(cfg, min(args.cpu_seconds, 8.0))
     print(json.dumps(result), flush=True)
 
 

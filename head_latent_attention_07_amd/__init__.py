@@ -9,7 +9,6 @@ library is missing, every entry point raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -40,7 +39,8 @@ class Dims(ctypes.Structure):
 class AppendArgs(ctypes.Structure):
     _fields_ = [("c_kv", ctypes.c_void_p), ("k_pe", ctypes.c_void_p), ("in_dtype", ctypes.c_int),
                 ("positions", ctypes.c_void_p), ("rope_theta", ctypes.c_float),
-                ("projected", ctypes.c_void_p), ("d_model", ctypes.c_int32)]
+                ("projected", ctypes.c_void_p), ("d_model", ctypes.c_int32),
+                ("projected_bytes", ctypes.c_size_t)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -150,11 +150,12 @@ def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=
         c_kv, k_pe, positions = append[:3]
         theta = append[3] if len(append) > 3 else 10000.0
         if len(append) > 4:          # rows from a projection workspace
-            a = AppendArgs(None, None, MLA_F32, _ptr(positions), theta, _ptr(append[4]),
-                           int(append[5]))
+            pws = append[4]
+            a = AppendArgs(None, None, MLA_F32, _ptr(positions), theta, _ptr(pws),
+                           int(append[5]), pws.numel() * pws.element_size())
         else:
             a = AppendArgs(_ptr(c_kv), _ptr(k_pe), dtype_code(c_kv.dtype), _ptr(positions), theta,
-                           None, 0)
+                           None, 0, 0)
         o._append_keep = a            # the struct must outlive the call
         o.append = ctypes.pointer(a)
     return ctypes.byref(o)
@@ -235,7 +236,7 @@ def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
     act = dtype_code(q_nope.dtype)
     cdt = dtype_code(latent.dtype)
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(D_NOPE + D_ROPE)
+        softmax_scale = 0.0          # the library's default, 1/sqrt(d_nope + d_rope)
     dev = q_nope.device
     if out is None:
         out = torch.empty((B, H, D_V), dtype=q_nope.dtype, device=dev)

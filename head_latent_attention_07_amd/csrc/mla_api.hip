@@ -120,6 +120,11 @@ WsLayout ws_layout(int B, int H, const Plan& pl, mla_dtype act) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Largest row stride (bytes) of a cache array that a decode call accepts:
+// the attention kernels form a tile's buffer records and lane offsets as
+// 32-bit products of up to 32 rows times the stride.
+constexpr int64_t kMaxRowStrideBytes = (int64_t)1 << 24;
+
 mla_status launch_status() {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -237,6 +242,9 @@ mla_status check_decode(const mla_dims* dims, const void* q_nope, const void* q_
   if (rows > INT32_MAX) return MLA_ERR_UNSUPPORTED;   // row indices are 32-bit in the kernels
   if (!aligned16(latent) || !aligned16(rope) || (ls * ce) % 16 != 0 || (rs * ce) % 16 != 0)
     return MLA_ERR_INVALID_ARG;
+  // the attention kernels address a tile's rows with 32-bit byte offsets
+  if (ls * (int64_t)ce >= kMaxRowStrideBytes || rs * (int64_t)ce >= kMaxRowStrideBytes)
+    return MLA_ERR_UNSUPPORTED;
   const size_t ae = elem_size(act);
   if (((uintptr_t)q_nope | (uintptr_t)q_pe | (uintptr_t)w_uk | (uintptr_t)w_uv | (uintptr_t)out) %
           16 != 0 &&
@@ -277,11 +285,23 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   const WsLayout wl = ws_layout(B, H, pl, act);
   if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
     return MLA_ERR_WORKSPACE;
+  if (do_append && opts->append->projected) {
+    // the partial sums must all be there (their slice count follows from
+    // batch and d_model), and must not share bytes with the workspace, whose
+    // absorbed queries are written in the launch that reads the sums
+    const mla_append_args* a = opts->append;
+    if (a->projected_bytes < project_ws_bytes(batch, a->d_model)) return MLA_ERR_WORKSPACE;
+    const uintptr_t p0 = (uintptr_t)a->projected, p1 = p0 + a->projected_bytes;
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + wl.total;
+    if (p0 < w1 && w0 < p1) return MLA_ERR_WORKSPACE;
+  }
   char* ws = (char*)workspace;
   float* part_o = (float*)(ws + wl.po_off);           // fp32 path
   _Float16* part_h = (_Float16*)(ws + wl.po_off);     // bf16 path
   float* part_scale = (float*)(ws + wl.ps_off);
   float* part_lse = (float*)(ws + wl.pl_off);
+  // 0 selects 1/sqrt(key width), the key being [k_nope | k_pe]
+  if (softmax_scale == 0.f) softmax_scale = 1.0f / std::sqrt((float)(D_N + D_R));
   const float c = softmax_scale * LOG2E;
   (void)hipGetLastError();  // start from a clean launch-error state
 

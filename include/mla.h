@@ -35,7 +35,9 @@
  *   - Strides are in ELEMENTS. Rows of the latent and RoPE arrays must start
  *     16-byte aligned (stride * element size a multiple of 16, pointers
  *     16-byte aligned). A packed 576-wide row (latent | RoPE key) is passed as
- *     latent = base, rope = base + 512, both with stride 576.
+ *     latent = base, rope = base + 512, both with stride 576. The decode calls
+ *     also need stride * element size below 2^24 bytes (MLA_ERR_UNSUPPORTED
+ *     otherwise).
  *   - The library is stateless apart from a per-device cache of the compute
  *     unit count; all entry points are thread-safe. Calls that share a
  *     workspace must be ordered by the caller (same stream).
@@ -84,9 +86,15 @@ typedef struct mla_append_args {
   /* If non-NULL, c_kv, k_pe and in_dtype are ignored: the rows are those of
    * a preceding mla_project call on the same stream with the same batch and
    * d_model, whose workspace this is (the sums of its partial products).
-   * The cache then receives exactly what mla_project_append would write. */
+   * The cache then receives exactly what mla_project_append would write.
+   * projected_bytes must be at least mla_project_workspace_size(batch,
+   * d_model), and [projected, projected + projected_bytes) must not overlap
+   * the decode call's own workspace (the absorbed queries are written while
+   * the append still reads the sums); either violation returns
+   * MLA_ERR_WORKSPACE and launches nothing. */
   const void* projected;
   int32_t d_model;            /* with projected: its hidden width */
+  size_t projected_bytes;     /* with projected: size of that buffer in bytes */
 } mla_append_args;
 
 /* Optional tuning and instrumentation for the decode calls (pass NULL for the
@@ -253,7 +261,10 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t ma
  *               (MLA_ERR_UNSUPPORTED otherwise)
  *   lengths     [batch] int32 (device)
  *   max_len     host upper bound of lengths (sizes the split plan)
- *   softmax_scale  usually 1/sqrt(d_nope + d_rope)
+ *   softmax_scale  the factor on every score; 0 selects the scale of the
+ *               "Classic attention and the cost of the KV cache" section,
+ *               1/sqrt(d_k) with d_k = d_nope + d_rope (the key width);
+ *               non-finite values are INVALID_ARG
  *   out    [batch, H, 128] act_dtype;  lse [batch, H] fp32 or NULL
  *   workspace   device buffer of at least mla_decode_workspace_size(...)
  *               bytes (256-byte aligned)

@@ -143,6 +143,11 @@ def bf16_value_to_bits(v: np.ndarray) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+# the value of every e4m3fn code, from the definition above (one entry per
+# code), so that large caches decode by table lookup
+_E4M3FN_TABLE = e4m3fn_bits_to_f64(np.arange(256))
+
+
 def decode_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Raw storage (uint16 for bf16, uint32 for f32, uint8 for e4m3) -> float64."""
     if dtype == "bf16":
@@ -150,7 +155,7 @@ def decode_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return f32_bits_to_f64(bits)
     if dtype == "fp8":
-        return e4m3fn_bits_to_f64(bits)
+        return _E4M3FN_TABLE[np.asarray(bits).astype(np.uint8)]
     raise ValueError(dtype)
 
 
@@ -201,14 +206,13 @@ def paged_row(block_table: np.ndarray, b: int, t: int, block_size: int) -> int:
 
 def gather_rows(b: int, n: int, *, seq_capacity=None, block_table=None,
                 block_size=None) -> np.ndarray:
-    """Physical row index of tokens 0..n-1 of sequence b, one token at a time."""
-    rows = np.empty(n, dtype=np.int64)
-    for t in range(n):
-        if block_table is None:
-            rows[t] = contiguous_row(b, t, seq_capacity)
-        else:
-            rows[t] = paged_row(block_table, b, t, block_size)
-    return rows
+    """Physical row index of tokens 0..n-1 of sequence b: the two formulas
+    above, evaluated for all t at once."""
+    t = np.arange(n, dtype=np.int64)
+    if block_table is None:
+        return b * int(seq_capacity) + t
+    blocks = np.asarray(block_table)[b].astype(np.int64)
+    return blocks[t // block_size] * block_size + t % block_size
 
 
 # ---------------------------------------------------------------------------
@@ -281,6 +285,29 @@ def decode(q_nope, q_pe, w_uk, w_uv, latent_rows, rope_rows, scale, *,
             out[b, h], lse[b, h] = fn(q_nope[b, h], q_pe[b, h], w_uk[h], w_uv[h],
                                       C, R, scale)
     return out, lse
+
+
+def decode_seq_absorbed(q_nope, q_pe, w_uk, w_uv, C, R, scale):
+    """Every head of one sequence in the absorbed form, the same sums as
+    decode_head_absorbed written as matrix products over the head axis:
+    q_lat[h] = q_nope[h] W_UK[h]; S[t, h] = scale (c_t . q_lat[h] + k^R_t .
+    q_pe[h]); softmax over t for each h; o[h] = (sum_t P[t, h] c_t) W_UV[h].
+
+    q_nope [H, d_nope], q_pe [H, d_rope], w_uk [H, d_nope, d_c],
+    w_uv [H, d_c, d_v], C [n, d_c], R [n, d_rope].
+    Returns out [H, d_v] and lse [H] (zeros and -inf when n == 0)."""
+    H = q_nope.shape[0]
+    n = C.shape[0]
+    if n == 0:
+        return np.zeros((H, w_uv.shape[2])), np.full(H, -math.inf)
+    q_lat = np.einsum("hk,hkc->hc", q_nope, w_uk)       # [H, d_c]
+    S = scale * (C @ q_lat.T + R @ q_pe.T)              # [n, H]
+    m = S.max(axis=0)
+    E = np.exp(S - m)
+    l = E.sum(axis=0)
+    P = E / l
+    o_lat = P.T @ C                                     # [H, d_c]
+    return np.einsum("hc,hcv->hv", o_lat, w_uv), m + np.log(l)
 
 
 def causal_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):

@@ -53,6 +53,26 @@ def oracle_decode(inp, batch_ids=None, heads=None, absorbed=False):
     return orc.decode(qn, qp, wuk, wuv, lat, rope, inp.scale, heads=heads, absorbed=absorbed)
 
 
+def oracle_decode_seq(inp, batch_ids=None):
+    """Oracle outputs for every head of the chosen sequences (all by default)
+    through the oracle's all-heads absorbed form, one sequence at a time (the
+    affordable form at the full workload sizes). Returns (out [nb, H, 128],
+    lse [nb, H])."""
+    cpu = inp.to("cpu")
+    bs = list(range(inp.B)) if batch_ids is None else list(batch_ids)
+    kind = act_kind(cpu.q_nope)
+    qn = to_f64(cpu.q_nope[bs], kind)
+    qp = to_f64(cpu.q_pe[bs], kind)
+    wuk = to_f64(cpu.w_uk, kind)
+    wuv = to_f64(cpu.w_uv, kind)
+    out = np.empty((len(bs), inp.H, synth.D_V))
+    lse = np.empty((len(bs), inp.H))
+    for i, b in enumerate(bs):
+        c, r = gathered_rows(cpu, b)
+        out[i], lse[i] = orc.decode_seq_absorbed(qn[i], qp[i], wuk, wuv, c, r, inp.scale)
+    return out, lse
+
+
 def rel_err_rows(gpu: np.ndarray, ref: np.ndarray) -> float:
     """max over (b, h) of ||gpu - ref||_inf / ||ref||_inf (NaN rows of ref skipped)."""
     g = gpu.reshape(-1, gpu.shape[-1])

@@ -137,6 +137,25 @@ def pin_absorption(orc):
         assert np.max(np.abs(l1 - l2)) <= 1e-12 * np.max(np.abs(l1))
 
 
+def pin_seq_absorbed(orc):
+    """The all-heads absorbed form equals the per-head non-absorbed
+    definition (itself pinned by brute force) to float64 rounding, on cases
+    with distinct head weights and non-square widths, including one row and
+    an empty sequence."""
+    for seed, n in ((60, 7), (61, 1), (62, 33)):
+        case = tiny_case(seed, n, H=3, d_c=16, d_n=5, d_r=4, d_v=6)
+        ref, ref_lse = _decode1(orc, case)
+        out, lse = orc.decode_seq_absorbed(case["q_nope"][0], case["q_pe"][0], case["w_uk"],
+                                           case["w_uv"], case["C"], case["R"], case["scale"])
+        assert out.shape == ref[0].shape
+        assert np.max(np.abs(out - ref[0])) <= 1e-12 * np.max(np.abs(ref[0]))
+        assert np.max(np.abs(lse - ref_lse[0])) <= 1e-12 * max(1.0, np.max(np.abs(ref_lse[0])))
+    case = tiny_case(63, 0, H=3, d_c=16, d_n=5, d_r=4, d_v=6)
+    out, lse = orc.decode_seq_absorbed(case["q_nope"][0], case["q_pe"][0], case["w_uk"],
+                                       case["w_uv"], case["C"], case["R"], case["scale"])
+    assert np.all(out == 0) and np.all(lse == -math.inf)
+
+
 def pin_hand_example(orc):
     """Hand-worked case: one head, d_c=2, d_nope=1, d_rope=1, d_v=1,
     W_UK=[[1,0]] (key = first latent coordinate), W_UV=[[0],[1]] (value =
@@ -300,5 +319,5 @@ PROJECTION_PINS = [pin_projection_hand_example, pin_projection_basis, pin_projec
 
 
 ALL_DECODE_PINS = [pin_bruteforce, pin_single_row, pin_zero_query, pin_rope_shift,
-                   pin_permutation, pin_absorption, pin_hand_example, pin_causal_prefill,
-                   pin_lse_combine, pin_empty]
+                   pin_permutation, pin_absorption, pin_seq_absorbed, pin_hand_example,
+                   pin_causal_prefill, pin_lse_combine, pin_empty]

@@ -80,6 +80,12 @@ def test_decode_argument_errors():
     assert _decode_status(d, act=mla.MLA_F32, cdt=mla.MLA_BF16) == 2  # dtype combination
     assert _decode_status(d, cdt=mla.MLA_FP8_E4M3, scales=False) == 1  # fp8 without scales
     assert _decode_status(d, ws=16) == 3                              # workspace too small
+    # row strides of 2^24 bytes or more do not fit the kernels' 32-bit tile offsets
+    big = 1 << 23                                                     # bf16 elements = 2^24 B
+    assert _decode_status(d, ls=big, rows=1 << 20, cap=16) == 2
+    assert _decode_status(d, rs=big, rows=1 << 20, cap=16) == 2
+    # just below the limit the call gets as far as the workspace (misaligned here)
+    assert _decode_status(d, ls=big - 8, rows=1 << 20, cap=16) == 3
 
 
 def test_paged_and_append_argument_errors():
@@ -135,7 +141,7 @@ def test_projected_append_argument_errors():
     d = mla.dims(128)
     p = ctypes.c_void_p(16)
     for d_model in (0, 100):
-        a = mla.AppendArgs(None, None, mla.MLA_F32, 16, 10000.0, 16, d_model)
+        a = mla.AppendArgs(None, None, mla.MLA_F32, 16, 10000.0, 16, d_model, 1 << 30)
         o = mla.DecodeOptions()
         o.append = ctypes.pointer(a)
         st = lib.mla_decode(ctypes.byref(d), p, p, p, p, 1, p, 576, p, 576, None, 1, 4096, 1024,
@@ -146,3 +152,30 @@ def test_projected_append_argument_errors():
     assert lib.mla_project(ctypes.byref(d), p, p, p, 2, 7168, 4, p, 1 << 30, None) == 2
     assert lib.mla_project(ctypes.byref(d), p, p, p, 1, 7168, 4, p, 1024, None) == 3
     assert lib.mla_project(ctypes.byref(d), p, p, p, 1, 7168, 0, p, 0, None) == 0
+
+
+def test_projected_append_buffer_checks():
+    """A decode call that appends from a projection workspace rejects, before
+    any launch, a projection buffer smaller than mla_project_workspace_size
+    and one that overlaps the decode workspace (the absorb workgroups write
+    the queries there while the append workgroups still read the sums)."""
+    lib = mla.load()
+    d = mla.dims(128)
+    p = ctypes.c_void_p(16)
+    B, D, max_len = 4, 7168, 1024
+    need = lib.mla_project_workspace_size(B, D)
+    ws_addr, ws_bytes = 1 << 30, 1 << 28                       # 256-byte aligned, large enough
+    assert mla.workspace_size(128, B, max_len, mla.MLA_BF16, mla.MLA_BF16) <= ws_bytes
+
+    def call(proj_addr, proj_bytes):
+        a = mla.AppendArgs(None, None, mla.MLA_F32, 16, 10000.0, proj_addr, D, proj_bytes)
+        o = mla.DecodeOptions()
+        o.append = ctypes.pointer(a)
+        return lib.mla_decode(ctypes.byref(d), p, p, p, p, 1, p, 576, p, 576, None, 1, 4096,
+                              1024, p, B, max_len, 0.07, p, None, ctypes.c_void_p(ws_addr),
+                              ws_bytes, ctypes.byref(o), None)
+    far = 1 << 34
+    assert call(far, need - 1) == 3                                 # too small
+    assert call(far, 0) == 3
+    assert call(ws_addr + 256, need) == 3                           # inside the workspace
+    assert call(ws_addr - need + 16, need) == 3                     # overlaps its start

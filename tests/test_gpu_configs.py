@@ -1,32 +1,51 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times: sampled sequences and heads are compared with the oracle
-one by one (the oracle cannot afford every output at these sizes)."""
+benchmark times.
+
+Every (sequence, head) output row and lse is compared with the oracle's
+all-heads absorbed form (decode_seq_absorbed, pinned against the per-head
+non-absorbed definition at 1e-12). Sampled sequences and heads are also
+compared with the non-absorbed definition itself (K = C W_UK^T and
+V = C W_UV per head, then softmax attention). The 61-layer fp8 workload is
+checked layer by layer, in groups of layers, every layer and sequence."""
 
 import numpy as np
 import pytest
 import torch
 
 import synth
-from helpers import LSE_TOL, TOL, gpu_f64, oracle_decode, rel_err_rows
+from helpers import (LSE_TOL, TOL, gpu_f64, oracle_decode, oracle_decode_seq, rel_err_rows,
+                     to_f64)
 
 pytestmark = pytest.mark.gpu
 
 
-def check_sampled(gpu, inp, batch_ids, heads, tol_key, **kw):
+def compare(tag, got, got_lse, ref, ref_lse, tol_key):
+    err = rel_err_rows(got, ref)
+    lerr = float(np.max(np.abs(got_lse - ref_lse)))
+    print(f"[result] {tag}: normwise rel err {err:.3e} (tol {TOL[tol_key]}), "
+          f"lse {lerr:.3e} (tol {LSE_TOL[tol_key]})", flush=True)
+    assert err <= TOL[tol_key], tag
+    assert lerr <= LSE_TOL[tol_key], tag
+
+
+def check_full(gpu, inp, sample_b, sample_heads, tol_key, ref_inp=None, **kw):
+    """Decode the whole workload on the GPU; compare every row with the
+    all-heads absorbed oracle and the sample with the non-absorbed one.
+    `ref_inp` is the cache the oracle sees (default: `inp`)."""
     print(f"[case] cfg={inp.cfg} B={inp.B} max_len={inp.max_len} paged={inp.paged} "
-          f"sample b={batch_ids} heads={len(heads)}", flush=True)
+          f"cache={inp.cache_dtype}", flush=True)
     out, lse = gpu.decode_inputs(inp.to("cuda"), **kw)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    ref, ref_lse = oracle_decode(inp, batch_ids=batch_ids, heads=heads)
-    g = gpu_f64(out)[batch_ids][:, heads]
-    err = rel_err_rows(g, ref[:, heads])
-    lerr = float(np.max(np.abs(lse.cpu().double().numpy()[batch_ids][:, heads] - ref_lse[:, heads])))
-    print(f"[result] sampled normwise rel err {err:.3e} (tol {TOL[tol_key]}), lse {lerr:.3e}",
-          flush=True)
-    assert err <= TOL[tol_key]
-    assert lerr <= LSE_TOL[tol_key]
-    return out, lse
+    got, got_lse = gpu_f64(out), lse.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    ref_inp = inp if ref_inp is None else ref_inp
+    ref, ref_lse = oracle_decode_seq(ref_inp)
+    compare(f"cfg {inp.cfg} all {inp.B}x{inp.H} rows", got, got_lse, ref, ref_lse, tol_key)
+    nref, nref_lse = oracle_decode(ref_inp, batch_ids=sample_b, heads=sample_heads)
+    g = got[sample_b][:, sample_heads]
+    compare(f"cfg {inp.cfg} non-absorbed sample b={sample_b} {len(sample_heads)} heads", g,
+            got_lse[sample_b][:, sample_heads], nref[:, sample_heads],
+            nref_lse[:, sample_heads], tol_key)
 
 
 HEADS = list(range(0, 128, 5))
@@ -36,56 +55,75 @@ def test_config3_ragged_paged(gpu):
     """B=64, lengths U[1024, 4096], paged 64-token blocks."""
     inp = synth.make_inputs(3)
     b = [0, 17, int(torch.argmax(inp.lengths)), int(torch.argmin(inp.lengths))]
-    check_sampled(gpu, inp, b, HEADS, "bf16")
+    check_full(gpu, inp, b, HEADS, "bf16")
 
 
 def test_config3_uniform_paged(gpu):
     """B=64, every N=4096, paged: the benchmark workload."""
     inp = synth.make_inputs("3u")
-    check_sampled(gpu, inp, [0, 63], HEADS, "bf16")
+    check_full(gpu, inp, [0, 63], HEADS, "bf16")
 
 
 def test_config3_uniform_paged_step_with_append(gpu):
     """The benchmark step itself: B=64, N=4096, paged, one decode call that
     first appends each sequence's new token (position N-1, RoPE on its key)
-    in the absorb launch. The oracle makes the appended rows with its own
+    in the absorb launch. The oracle makes every appended row with its own
     append and decodes the resulting cache."""
     from oracle import mla_oracle as orc
-    from helpers import to_f64
     inp = synth.make_inputs("3u")
     c_new, k_new = synth.append_inputs(7000, inp.B, "bf16")
     pos = inp.lengths - 1
-    dev = inp.to("cuda")
-    print("[case] 3u step with append", flush=True)
-    out, lse = gpu.decode_inputs(dev, append=(c_new.cuda(), k_new.cuda(), pos.cuda()))
-    torch.cuda.synchronize()
-    batch_ids = [0, 31, 63]
+    ref_inp = synth.make_inputs("3u")
     table = inp.block_table.numpy()
-    for b in batch_ids:
+    for b in range(inp.B):
         p = int(pos[b])
-        lat, rope, _, _ = orc.append_row(to_f64(c_new[b], "bf16"), to_f64(k_new[b], "bf16"), p, "bf16")
+        lat, rope, _, _ = orc.append_row(to_f64(c_new[b], "bf16"), to_f64(k_new[b], "bf16"), p,
+                                         "bf16")
         row = orc.paged_row(table, b, p, inp.block_size)
-        inp.cache[row] = torch.from_numpy(np.concatenate([lat, rope]).astype(np.float32)).to(torch.bfloat16)
-    ref, ref_lse = oracle_decode(inp, batch_ids=batch_ids, heads=HEADS)
-    g = gpu_f64(out)[batch_ids][:, HEADS]
-    err = rel_err_rows(g, ref[:, HEADS])
-    lerr = float(np.max(np.abs(lse.cpu().double().numpy()[batch_ids][:, HEADS] - ref_lse[:, HEADS])))
-    print(f"[result] sampled normwise rel err {err:.3e}, lse {lerr:.3e}", flush=True)
-    assert err <= TOL["bf16"]
-    assert lerr <= LSE_TOL["bf16"]
+        ref_inp.cache[row] = torch.from_numpy(
+            np.concatenate([lat, rope]).astype(np.float32)).to(torch.bfloat16)
+    check_full(gpu, inp, [0, 31, 63], HEADS, "bf16", ref_inp=ref_inp,
+               append=(c_new.cuda(), k_new.cuda(), pos.cuda()))
 
 
 def test_config4_long_context(gpu):
     """B=4, N=131072 (128K context), contiguous: many splits per sequence."""
     inp = synth.make_inputs(4)
-    check_sampled(gpu, inp, [1], list(range(0, 128, 16)), "bf16")
+    check_full(gpu, inp, [1], list(range(0, 128, 4)), "bf16")
 
 
-def test_config5_fp8_layer_sample(gpu):
-    """fp8 cache, B=32, N=32768: two of the 61 layers (each layer has its own
-    seeded weights, queries and cache), sampled sequences and heads."""
-    for layer in (0, 60):
-        inp = synth.make_inputs(5, layer=layer, gen_device="cuda")
-        check_sampled(gpu, inp.to("cpu"), [3], list(range(0, 128, 32)), "fp8")
+# Config 5: 61 independent layers (own weights, queries and cache each), in
+# groups of 8 layers per test. Every layer is decoded on the GPU and compared
+# on all 32 sequences x 128 heads with the absorbed oracle; four layers also
+# on two seeded sequences x all heads with the non-absorbed one.
+C5_LAYERS = 61
+C5_GROUP = 4
+C5_NONABSORBED_LAYERS = (0, 20, 40, 60)
+
+
+def c5_sample_sequences(layer):
+    return sorted(np.random.default_rng(5000 + layer).choice(32, size=2, replace=False).tolist())
+
+
+@pytest.mark.parametrize("group", range((C5_LAYERS + C5_GROUP - 1) // C5_GROUP))
+def test_config5_fp8_layers(gpu, group):
+    """fp8 cache + bf16 scale per row, B=32, N=32768: layers
+    4 group .. 4 group + 3 of the 61-layer step, every sequence and head."""
+    for layer in range(group * C5_GROUP, min(C5_LAYERS, (group + 1) * C5_GROUP)):
+        print(f"[case] cfg=5 layer={layer} B=32 N=32768 fp8 cache", flush=True)
+        dev = synth.make_inputs(5, layer=layer, device="cuda", gen_device="cuda")
+        out, lse = gpu.decode_inputs(dev)
+        torch.cuda.synchronize()
+        got, got_lse = gpu_f64(out), lse.cpu().double().numpy()
+        inp = dev.to("cpu")
+        del dev
+        assert np.isfinite(got).all()
+        ref, ref_lse = oracle_decode_seq(inp)
+        compare(f"cfg 5 layer {layer} all 32x128 rows", got, got_lse, ref, ref_lse, "fp8")
+        if layer in C5_NONABSORBED_LAYERS:
+            bs = c5_sample_sequences(layer)
+            nref, nref_lse = oracle_decode(inp, batch_ids=bs)
+            compare(f"cfg 5 layer {layer} non-absorbed b={bs} all heads", got[bs], got_lse[bs],
+                    nref, nref_lse, "fp8")
         del inp
         torch.cuda.empty_cache()

@@ -121,6 +121,22 @@ def m_absorbed_missing_uv(o):
     o.decode_head_absorbed = f
 
 
+def m_seq_heads_reversed(o):
+    # the absorbed query of head h built with the W_UK of another head
+    orig = o.decode_seq_absorbed
+    o.decode_seq_absorbed = lambda qn, qp, wuk, wuv, C, R, sc: orig(qn, qp, wuk[::-1], wuv, C, R, sc)
+
+
+def m_seq_softmax_over_heads(o):
+    def f(q_nope, q_pe, w_uk, w_uv, C, R, scale):
+        q_lat = np.einsum("hk,hkc->hc", q_nope, w_uk)
+        S = scale * (C @ q_lat.T + R @ q_pe.T)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        P = E / E.sum(axis=1, keepdims=True)
+        return np.einsum("hc,hcv->hv", P.T @ C, w_uv), np.log(E.sum(axis=0))
+    o.decode_seq_absorbed = f
+
+
 def m_proj_transposed(o):
     o.kv_down_project = lambda h, w_dkv, w_kr: (w_dkv.T @ h, w_kr.T @ h)
 
@@ -144,6 +160,7 @@ def m_proj_key_not_rotated(o):
 MUTATIONS = [m_drop_rope_term, m_wrong_scale, m_head_index, m_uv_for_uk_layout,
              m_unnormalised, m_lse_without_max, m_rope_sign, m_rope_half_split, m_rope_freq,
              m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv,
+             m_seq_heads_reversed, m_seq_softmax_over_heads,
              m_proj_transposed, m_proj_last_term_dropped, m_proj_key_from_latent_weights,
              m_proj_key_not_rotated]
 
