@@ -326,6 +326,32 @@ def causal_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
     return P @ V
 
 
+def chunked_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+    """One head of prefill over a chunk of T new queries whose rows are the
+    last T of the n cached rows (n >= T, the context before the chunk being
+    the first n - T rows): query i sits at position n - T + i and attends to
+    rows 0 .. n - T + i ([WL] "Classic attention and the cost of the KV
+    cache": softmax(Q K^T / sqrt(d_k) + M) V with the causal mask M; [KV]
+    "KV Cache": each token sees itself and the tokens before it).
+
+    Recompute (non-absorbed) form: every key k_t = [W_UK[h] c_t ; k^R_t] and
+    value v_t = c_t W_UV[h] is decompressed from the latent rows ([TN]
+    equations for K and V), then plain causal softmax attention.
+    q_nope [T, d_nope], q_pe [T, d_rope], C [n, d_c], R [n, d_rope].
+    Returns out [T, d_v] and lse [T] (natural log)."""
+    T = q_nope.shape[0]
+    n = C.shape[0]
+    K = C @ w_uk_h.T                                  # [n, d_nope]
+    V = C @ w_uv_h                                    # [n, d_v]
+    S = scale * (q_nope @ K.T + q_pe @ R.T)           # [T, n]
+    pos = (n - T) + np.arange(T)
+    S = np.where(np.arange(n)[None, :] > pos[:, None], -np.inf, S)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ V, (m + np.log(l))[:, 0]
+
+
 # ---------------------------------------------------------------------------
 # Cache append (write the new token's row)
 # ---------------------------------------------------------------------------

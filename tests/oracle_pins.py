@@ -195,6 +195,35 @@ def pin_causal_prefill(orc):
     assert np.allclose(full[0], C[0] @ Wuv[0], rtol=1e-14)
 
 
+def pin_chunked_prefill(orc):
+    """Chunked prefill, query by query: query i of a chunk of T over n rows is
+    the decode of the first n - T + i + 1 rows (the definition of causal
+    attention; decode itself is pinned by brute force). A chunk covering the
+    whole sequence (T = n) is full causal attention."""
+    H, d_c, d_n, d_r, d_v = 2, 8, 4, 2, 3
+    r = _rng(31)
+    Wuk = r.standard_normal((H, d_n, d_c))
+    Wuv = r.standard_normal((H, d_c, d_v))
+    sc = 1 / math.sqrt(d_n + d_r)
+    for n, T in ((9, 4), (7, 7), (5, 1)):
+        C = r.standard_normal((n, d_c))
+        R = r.standard_normal((n, d_r))
+        Qn = r.standard_normal((T, H, d_n))
+        Qp = r.standard_normal((T, H, d_r))
+        for h in range(H):
+            out, lse = orc.chunked_prefill(Qn[:, h], Qp[:, h], Wuk[h], Wuv[h], C, R, sc)
+            assert out.shape == (T, d_v) and lse.shape == (T,)
+            for i in range(T):
+                k = n - T + i + 1
+                o, l = orc.decode(Qn[i:i + 1], Qp[i:i + 1], Wuk, Wuv, [C[:k]], [R[:k]], sc,
+                                  heads=[h])
+                assert np.allclose(o[0, h], out[i], rtol=1e-12, atol=1e-14), (n, T, h, i)
+                assert abs(l[0, h] - lse[i]) <= 1e-12 * max(1.0, abs(lse[i]))
+            if T == n:
+                full = orc.causal_prefill(Qn[:, h], Qp[:, h], Wuk[h], Wuv[h], C, R, sc)
+                assert np.allclose(full, out, rtol=1e-12, atol=1e-14)
+
+
 def pin_lse_combine(orc):
     """Split the rows in two, decode each part, merge with the log-sum-exp
     weights e^{lse_i - lse}: the merge equals the decode over all rows. This
@@ -320,4 +349,4 @@ PROJECTION_PINS = [pin_projection_hand_example, pin_projection_basis, pin_projec
 
 ALL_DECODE_PINS = [pin_bruteforce, pin_single_row, pin_zero_query, pin_rope_shift,
                    pin_permutation, pin_absorption, pin_seq_absorbed, pin_hand_example,
-                   pin_causal_prefill, pin_lse_combine, pin_empty]
+                   pin_causal_prefill, pin_chunked_prefill, pin_lse_combine, pin_empty]

@@ -113,6 +113,29 @@ def m_causal_mask(o):
     o.causal_prefill = f
 
 
+def m_chunk_offset(o):
+    # the chunk's queries placed at positions 0 .. T-1 instead of n-T .. n-1
+    orig = o.chunked_prefill
+
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        T = q_nope.shape[0]
+        return orig(q_nope, q_pe, w_uk_h, w_uv_h, C[:T], R[:T], scale)
+    o.chunked_prefill = f
+
+
+def m_chunk_mask_excludes_self(o):
+    def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
+        T, n = q_nope.shape[0], C.shape[0]
+        S = scale * (q_nope @ (C @ w_uk_h.T).T + q_pe @ R.T)
+        pos = (n - T) + np.arange(T)
+        S = np.where(np.arange(n)[None, :] >= pos[:, None], -np.inf, S)
+        S[0, 0] = 0.0 if n - T == 0 else S[0, 0]
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        return (E / E.sum(1, keepdims=True)) @ (C @ w_uv_h), (m + np.log(E.sum(1, keepdims=True)))[:, 0]
+    o.chunked_prefill = f
+
+
 def m_absorbed_missing_uv(o):
     def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
         q_lat = q_nope @ w_uk_h
@@ -160,7 +183,8 @@ def m_proj_key_not_rotated(o):
 MUTATIONS = [m_drop_rope_term, m_wrong_scale, m_head_index, m_uv_for_uk_layout,
              m_unnormalised, m_lse_without_max, m_rope_sign, m_rope_half_split, m_rope_freq,
              m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv,
-             m_seq_heads_reversed, m_seq_softmax_over_heads,
+             m_seq_heads_reversed, m_seq_softmax_over_heads, m_chunk_offset,
+             m_chunk_mask_excludes_self,
              m_proj_transposed, m_proj_last_term_dropped, m_proj_key_from_latent_weights,
              m_proj_key_not_rotated]
 
