@@ -22,7 +22,9 @@ D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 
 SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
-           "mla_project_append", "mla_project_workspace_size", "mla_project")
+           "mla_project_append", "mla_project_workspace_size", "mla_project",
+           "mla_decode_paged_noalloc")
+NOALLOC_SCRATCH_BYTES = 80 << 20      # MLA_NOALLOC_SCRATCH_BYTES
 
 
 class MLAError(RuntimeError):
@@ -86,6 +88,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode.argtypes = common + [_I64] + tail
     lib.mla_decode_paged.restype = ctypes.c_int
     lib.mla_decode_paged.argtypes = common + [_P, _I32, _I32] + tail
+    lib.mla_decode_paged_noalloc.restype = ctypes.c_int
+    lib.mla_decode_paged_noalloc.argtypes = (common + [_P, _I32, _I32]
+                                             + [_P, _I32, _I32, _F, _P, _P,
+                                                ctypes.POINTER(DecodeOptions), _P])
     lib.mla_project_workspace_size.restype = _SZ
     lib.mla_project_workspace_size.argtypes = [_I32, _I32]
     lib.mla_project.restype = ctypes.c_int
@@ -256,6 +262,29 @@ def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
     else:
         st = lib.mla_decode(*head, seq_capacity, *tail)
     _check(st)
+    return out, lse
+
+
+def decode_paged_noalloc(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
+                         block_table, block_size=64, scales=None, softmax_scale=None, out=None,
+                         lse=None, num_splits=0, append=None, stream=None):
+    """mla_decode_paged_noalloc: as decode_paged, with the library's own
+    scratch instead of a workspace. Returns (out, lse)."""
+    lib = load()
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    d = dims(H)
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, H, D_V), dtype=q_nope.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib.mla_decode_paged_noalloc(
+        ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        dtype_code(q_nope.dtype), _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+        _ptr(scales), dtype_code(latent.dtype), latent.shape[0], _ptr(block_table),
+        block_table.shape[1], block_size, _ptr(lengths), B, max_len,
+        0.0 if softmax_scale is None else softmax_scale, _ptr(out), _ptr(lse),
+        _opts(num_splits, None, append), _stream(stream)))
     return out, lse
 
 

@@ -1,6 +1,7 @@
 // C ABI of the MLA decode library: argument validation, split planning and
 // kernel launches on the caller's stream. See include/mla.h for the contract.
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -124,6 +125,32 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // the attention kernels form a tile's buffer records and lane offsets as
 // 32-bit products of up to 32 rows times the stride.
 constexpr int64_t kMaxRowStrideBytes = (int64_t)1 << 24;
+
+// Scratch of mla_decode_paged_noalloc: the absorbed queries and split
+// partials that mla_decode_paged keeps in the caller's workspace. Each device
+// holds its own copy (from the module's load until the process ends). Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // guarded by g_scratch_mu
+
+mla_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    if (((uintptr_t)p & 255) != 0) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
 
 mla_status launch_status() {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -471,6 +498,31 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* q_nope, const void
   return run_decode(dims, q_nope, q_pe, w_uk, w_uv, act, latent, ls, rope, rs, scales, cdt, rows,
                     0, block_table, max_blocks, block_size, lengths, batch, max_len,
                     softmax_scale, out, lse, workspace, workspace_bytes, opts, stream);
+}
+
+mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                                    const void* w_uk, const void* w_uv, mla_dtype act,
+                                    const void* latent, int64_t ls, const void* rope, int64_t rs,
+                                    const void* scales, mla_dtype cdt, int64_t rows,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    int32_t block_size, const int32_t* lengths, int32_t batch,
+                                    int32_t max_len, float softmax_scale, void* out, float* lse,
+                                    const mla_decode_options* opts, hipStream_t stream) {
+  MLA_TRY(check_decode(dims, q_nope, q_pe, w_uk, w_uv, act, latent, ls, rope, rs, scales, cdt,
+                       rows, lengths, batch, max_len, softmax_scale, out));
+  if (batch == 0) return MLA_OK;
+  if (!block_table || block_size <= 0 || block_size % TILE != 0 || max_blocks <= 0 ||
+      (int64_t)max_blocks * block_size < max_len || rows < block_size)
+    return MLA_ERR_INVALID_ARG;
+  // the scratch this call needs, before touching the device's copy
+  const size_t need = ws_layout(batch, dims->heads, make_plan(batch, dims->heads, max_len, act, opts),
+                                act).total;
+  if (need > kScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MLA_TRY(scratch_address(&ws));
+  return run_decode(dims, q_nope, q_pe, w_uk, w_uv, act, latent, ls, rope, rs, scales, cdt, rows,
+                    0, block_table, max_blocks, block_size, lengths, batch, max_len,
+                    softmax_scale, out, lse, ws, kScratchBytes, opts, stream);
 }
 
 mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* k_pe,

@@ -299,6 +299,38 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* q_nope, const void
                             size_t workspace_bytes, const mla_decode_options* opts,
                             hipStream_t stream);
 
+/*
+ * mla_decode_paged_noalloc: mla_decode_paged without a workspace argument,
+ * for callers that cannot allocate device memory or pass a buffer of their
+ * own around: code captured into a HIP graph, serving loops that must not
+ * call hipMalloc, harnesses that forbid allocation. It calls no allocating
+ * routine; the absorbed queries and split partials go to a scratch array
+ * inside the library, of MLA_NOALLOC_SCRATCH_BYTES bytes per device (one
+ * copy per GPU the library runs on, held until the process ends; its device
+ * address is looked up once per device on the first call there).
+ *
+ * Arguments, results and errors are those of mla_decode_paged. A call whose
+ * plan needs more than MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size
+ * with the same arguments) returns MLA_ERR_WORKSPACE and launches nothing;
+ * 80 MiB covers, for example, 64 sequences of 4096 tokens or 32 of 32768 at
+ * 128 heads. Every call on one GPU uses the same scratch, which keeps the
+ * last call's contents (nothing in it needs clearing: each call writes every
+ * byte it reads). Calls that can overlap on one GPU (other streams, other
+ * host threads) race on it: order them on one stream, or use
+ * mla_decode_paged with separate workspaces.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+
+mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                                    const void* w_uk, const void* w_uv, mla_dtype act_dtype,
+                                    const void* latent, int64_t latent_stride, const void* rope,
+                                    int64_t rope_stride, const void* scales,
+                                    mla_dtype cache_dtype, int64_t cache_rows,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    int32_t block_size, const int32_t* lengths, int32_t batch,
+                                    int32_t max_len, float softmax_scale, void* out, float* lse,
+                                    const mla_decode_options* opts, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,3 +179,24 @@ def test_projected_append_buffer_checks():
     assert call(far, 0) == 3
     assert call(ws_addr + 256, need) == 3                           # inside the workspace
     assert call(ws_addr - need + 16, need) == 3                     # overlaps its start
+
+
+def test_noalloc_rejects_oversize_plans_before_any_launch():
+    """mla_decode_paged_noalloc refuses a call whose plan needs more scratch
+    than the library holds, before touching the device; other argument
+    errors are those of mla_decode_paged."""
+    lib = mla.load()
+    d = mla.dims(128)
+    p = ctypes.c_void_p(16)
+
+    def call(batch, max_len, ptr=p, bs=64):
+        mb = (max_len + bs - 1) // bs
+        return lib.mla_decode_paged_noalloc(ctypes.byref(d), ptr, ptr, ptr, ptr, 1, ptr, 576,
+                                            ptr, 576, None, 1, 1 << 24, ptr, mb, bs, ptr, batch,
+                                            max_len, 0.0, ptr, None, None, None)
+    need = mla.workspace_size(128, 512, 4096, mla.MLA_BF16, mla.MLA_BF16)
+    assert need > mla.NOALLOC_SCRATCH_BYTES
+    assert call(512, 4096) == 3
+    assert call(0, 4096) == 0                     # no-op
+    assert call(4, 4096, ptr=None) == 1           # null pointers
+    assert call(4, 4096, bs=48) == 1              # block size not a multiple of 32
