@@ -338,7 +338,9 @@ def chunked_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
     value v_t = c_t W_UV[h] is decompressed from the latent rows ([TN]
     equations for K and V), then plain causal softmax attention.
     q_nope [T, d_nope], q_pe [T, d_rope], C [n, d_c], R [n, d_rope].
-    Returns out [T, d_v] and lse [T] (natural log)."""
+    Returns out [T, d_v] and lse [T] (natural log). When n < T the first
+    T - n queries sit before position 0 and see no row: their attention is
+    empty (zeros and -inf, as for an empty sequence in decode)."""
     T = q_nope.shape[0]
     n = C.shape[0]
     K = C @ w_uk_h.T                                  # [n, d_nope]
@@ -346,10 +348,17 @@ def chunked_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
     S = scale * (q_nope @ K.T + q_pe @ R.T)           # [T, n]
     pos = (n - T) + np.arange(T)
     S = np.where(np.arange(n)[None, :] > pos[:, None], -np.inf, S)
-    m = S.max(axis=1, keepdims=True)
-    E = np.exp(S - m)
-    l = E.sum(axis=1, keepdims=True)
-    return (E / l) @ V, (m + np.log(l))[:, 0]
+    out = np.zeros((T, w_uv_h.shape[1]))
+    lse = np.full(T, -math.inf)
+    seen = pos >= 0                                   # queries with at least row 0
+    if np.any(seen):
+        Ss = S[seen]
+        m = Ss.max(axis=1, keepdims=True)
+        E = np.exp(Ss - m)
+        l = E.sum(axis=1, keepdims=True)
+        out[seen] = (E / l) @ V
+        lse[seen] = (m + np.log(l))[:, 0]
+    return out, lse
 
 
 # ---------------------------------------------------------------------------

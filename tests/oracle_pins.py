@@ -205,7 +205,7 @@ def pin_chunked_prefill(orc):
     Wuk = r.standard_normal((H, d_n, d_c))
     Wuv = r.standard_normal((H, d_c, d_v))
     sc = 1 / math.sqrt(d_n + d_r)
-    for n, T in ((9, 4), (7, 7), (5, 1)):
+    for n, T in ((9, 4), (7, 7), (5, 1), (3, 5)):
         C = r.standard_normal((n, d_c))
         R = r.standard_normal((n, d_r))
         Qn = r.standard_normal((T, H, d_n))
@@ -215,6 +215,9 @@ def pin_chunked_prefill(orc):
             assert out.shape == (T, d_v) and lse.shape == (T,)
             for i in range(T):
                 k = n - T + i + 1
+                if k <= 0:        # before position 0: no row is visible
+                    assert np.all(out[i] == 0) and lse[i] == -math.inf
+                    continue
                 o, l = orc.decode(Qn[i:i + 1], Qp[i:i + 1], Wuk, Wuv, [C[:k]], [R[:k]], sc,
                                   heads=[h])
                 assert np.allclose(o[0, h], out[i], rtol=1e-12, atol=1e-14), (n, T, h, i)
