@@ -412,18 +412,25 @@ def write_mfma(counters_csv: str, trace_csv: str, config: str, kernel: str):
     dur_ns = durs[len(durs) // 2]
     util = mean["MfmaUtil"]
     busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"]
+    # MfmaUtil divides by the busiest instance of GRBM_GUI_ACTIVE (one per
+    # XCD), so that count follows from the two; the counter window of a
+    # dispatch is longer than the kernel, so cycles / duration over-states the
+    # clock (an upper bound)
     grbm_max = busy / (util / 100.0 * SIMD_COUNT) if util > 0 else None
     flops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
     rec = {"kernel": kernel, "workload": config, "kernel_source_hash": kernel_source_hash(),
            "dispatches": len(rows) // max(1, len(by)), "counters_mean": mean,
            "median_duration_us": dur_ns / 1e3,
            "mfma_util_pct": util,
+           "mfma_busy_cycles_per_simd": busy / SIMD_COUNT,
            "mfma_bf16_flop_per_dispatch": flops,
            "mfma_bf16_tflops": flops / dur_ns / 1e3,
            "mfma_bf16_frac_of_peak": flops / dur_ns / 1e3 / MFMA_BF16_PEAK_TFLOPS,
            "gpu_active_cycles_max_instance": grbm_max,
-           "clock_ghz": grbm_max / dur_ns if grbm_max else None,
-           "peak_used": {"bf16_dense_tflops": MFMA_BF16_PEAK_TFLOPS, "simds": SIMD_COUNT}}
+           "clock_ghz_upper_bound": grbm_max / dur_ns if grbm_max else None,
+           "mfma_busy_frac_at_2p4ghz": busy / SIMD_COUNT / (dur_ns * 2.4),
+           "peak_used": {"bf16_dense_tflops": MFMA_BF16_PEAK_TFLOPS, "simds": SIMD_COUNT,
+                         "clock_ghz": 2.4}}
     out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_mfma.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -441,7 +448,7 @@ def measured_mfma(workload: str, kernel: str):
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return {k: t[k] for k in ("mfma_util_pct", "mfma_bf16_tflops", "mfma_bf16_frac_of_peak",
-                              "clock_ghz", "median_duration_us")}
+                              "mfma_bf16_flop_per_dispatch", "median_duration_us")}
 
 
 def percentile(vals, q):
