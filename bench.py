@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, default=None)
     ap.add_argument("--write-mfma", nargs=2, default=None, metavar=("COUNTERS_CSV", "TRACE_CSV"))
     ap.add_argument("--project", action="store_true")
+    ap.add_argument("--prefill", action="store_true")
     ap.add_argument("--with-projection", action="store_true")
     return ap.parse_args()
 
@@ -376,6 +377,118 @@ def bench_project(args):
 D_QK_ROWS = 576    # rows of W_DKV (512) and W_KR (64)
 
 
+PREFILL_WORKLOAD = "mla_prefill_b1_t4096_n4096_h128_bf16"
+
+
+def cpu_baseline_prefill(seconds: float, T: int, heads: int):
+    """The oracle's chunked_prefill (float64, recompute form) on the host
+    cores: heads of the same 4096-token prompt one at a time until `seconds`
+    elapse, scaled to prompt tokens per second (all heads)."""
+    import torch
+    import synth
+    from oracle import mla_oracle as orc
+    threads = _host_threads()
+    inp = synth.make_inputs(2, B=1, N=T, lengths=torch.tensor([T], dtype=torch.int32))
+    qn, qp = synth.prefill_queries(6100, 1, T, heads)
+
+    def f64(t):
+        return orc.decode_storage(synth.raw_bits(t), "bf16")
+
+    wuk, wuv, qn64, qp64 = f64(inp.w_uk), f64(inp.w_uv), f64(qn)[0], f64(qp)[0]
+    vals = f64(inp.cache[:T])
+    C, R = vals[:, :512], vals[:, 512:]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        h = done % heads
+        orc.chunked_prefill(qn64[:, h], qp64[:, h], wuk[h], wuv[h], C, R, inp.scale)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": T / (dt / done * heads), "unit": "prompt tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of the {heads} heads of the same {T}-token prompt, float64 "
+                      f"recompute-form oracle, {dt:.1f} s, scaled to all heads"}
+
+
+def bench_prefill(args):
+    """Time mla_prefill on one 4096-token prompt (B=1, T=N=4096, 128 heads,
+    bf16): W_UV transpose, decompression of K and V for every head, causal
+    attention. The roofline is the attention kernel's against the dense
+    matrix-core peak (its operands are fp16, whose peak equals bf16's)."""
+    import torch
+    import head_latent_attention_07_amd as mla
+    import synth
+
+    mla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, T, H = 1, 4096, 128
+    layers = []
+    for layer in range(2):
+        inp = synth.make_inputs(2, B=B, N=T, H=H, layer=layer,
+                                lengths=torch.tensor([T], dtype=torch.int32)).to(dev)
+        qn, qp = synth.prefill_queries(6100 + 10 * layer, B, T, H, device=dev)
+        lat, rope = mla.split_cache(inp.cache)
+        ws = torch.empty(mla.prefill_workspace_size(H, B, T), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        layers.append(dict(inp=inp, qn=qn, qp=qp, lat=lat, rope=rope, ws=ws, out=out, lse=lse))
+    ev = HipEvents()
+
+    def call(L, events=None, expand_events=None):
+        inp = L["inp"]
+        mla.prefill(L["qn"], L["qp"], inp.w_uk, inp.w_uv, L["lat"], L["rope"], inp.lengths, T,
+                    seq_capacity=inp.seq_capacity, out=L["out"], lse=L["lse"], workspace=L["ws"],
+                    events=events, expand_events=expand_events)
+
+    for i in range(args.warmup):
+        call(layers[i % 2])
+    torch.cuda.synchronize()
+    pairs = [((ev.create(), ev.create()), (ev.create(), ev.create())) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(layers[i % 2], events=pairs[i][0], expand_events=pairs[i][1])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms = [ev.elapsed_ms(*pr[0]) for pr in pairs]
+    exp_ms = [ev.elapsed_ms(*pr[1]) for pr in pairs]
+    for pr in pairs:
+        for e in pr[0] + pr[1]:
+            ev.destroy(e)
+    ms = (t1 - t0) * 1e3 / args.steps
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    exp_avg = sum(exp_ms) / len(exp_ms)
+    # causal attention: query i sees i + 1 keys; (192 + 128) x 2 FLOP per
+    # (query, key, head); decompression: 2 x 512 x 256 FLOP per (token, head)
+    attn_flop = H * (T * (T + 1) // 2) * (192 + 128) * 2
+    exp_flop = B * T * H * 512 * 256 * 2
+    achieved = attn_flop / (attn_avg * 1e-3) / 1e12
+    line = {
+        "metric": "MLA prefill prompt tokens/s (recompute mode: decompress K and V, causal attention)",
+        "value": B * T / (ms * 1e-3), "unit": "prompt tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (attention operands fp16)",
+        "data": "synthetic (seeded normals; random-init weights of the DeepSeek-V3 MLA widths)",
+        "config": {"workload": PREFILL_WORKLOAD, "B": B, "T": T, "N": T, "H": H,
+                   "d_qk": 192, "d_v": 128},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "mla_prefill_attn_kernel",
+                     "flop_per_launch": attn_flop, "avg_launch_us": attn_avg * 1e3,
+                     "launch_us_p10_p50_p90": [percentile(attn_ms, q) * 1e3 for q in (10, 50, 90)]},
+        "expand": {"kernel": "mla_prefill_expand_kernel", "flop_per_launch": exp_flop,
+                   "avg_launch_us": exp_avg * 1e3,
+                   "tflops": exp_flop / (exp_avg * 1e-3) / 1e12,
+                   "frac_of_bf16_peak": exp_flop / (exp_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_prefill(min(args.cpu_seconds, 10.0), T, H)
+    print(json.dumps(line), flush=True)
+
+
 SIMD_COUNT = 1024            # MI355X: 256 CUs x 4 SIMDs
 
 WORKLOADS = {"1": "mla_decode_b1_h16_n512_f32", "2": "mla_decode_b1_h128_n4096_bf16",
@@ -461,6 +574,11 @@ def percentile(vals, q):
 
 def main():
     args = parse()
+    if args.prefill:
+        args.steps = 50 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
+        bench_prefill(args)
+        return
     if args.project and not args.write_traffic:
         args.steps = 1000 if args.steps is None else args.steps
         args.warmup = 300 if args.warmup is None else args.warmup

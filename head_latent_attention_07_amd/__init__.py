@@ -23,7 +23,7 @@ D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
            "mla_project_append", "mla_project_workspace_size", "mla_project",
-           "mla_decode_paged_noalloc")
+           "mla_decode_paged_noalloc", "mla_prefill_workspace_size", "mla_prefill")
 NOALLOC_SCRATCH_BYTES = 80 << 20      # MLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -49,6 +49,11 @@ class DecodeOptions(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p),
                 ("append", ctypes.POINTER(AppendArgs))]
+
+
+class PrefillOptions(ctypes.Structure):
+    _fields_ = [("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p),
+                ("expand_begin", ctypes.c_void_p), ("expand_end", ctypes.c_void_p)]
 
 
 _lib = None
@@ -92,6 +97,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_decode_paged_noalloc.argtypes = (common + [_P, _I32, _I32]
                                              + [_P, _I32, _I32, _F, _P, _P,
                                                 ctypes.POINTER(DecodeOptions), _P])
+    lib.mla_prefill_workspace_size.restype = _SZ
+    lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _I32, _I32]
+    lib.mla_prefill.restype = ctypes.c_int
+    lib.mla_prefill.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, _P, ctypes.c_int, _P, _I64, _P,
+                                _I64, ctypes.c_int, _I64, _I64, _P, _I32, _I32, _P, _I32, _I32,
+                                _I32, _F, _P, _P, _P, _SZ, ctypes.POINTER(PrefillOptions), _P]
     lib.mla_project_workspace_size.restype = _SZ
     lib.mla_project_workspace_size.argtypes = [_I32, _I32]
     lib.mla_project.restype = ctypes.c_int
@@ -310,3 +321,42 @@ def decode_inputs(inp, **kw):
                             scales=inp.scales, softmax_scale=inp.scale, **kw)
     return decode(inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, lat, rop, inp.lengths, inp.max_len,
                   seq_capacity=inp.seq_capacity, scales=inp.scales, softmax_scale=inp.scale, **kw)
+
+
+def prefill_workspace_size(heads: int, batch: int, max_len: int) -> int:
+    return int(load().mla_prefill_workspace_size(ctypes.byref(dims(heads)), batch, max_len))
+
+
+def prefill(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *, seq_capacity=0,
+            block_table=None, block_size=64, softmax_scale=None, out=None, lse=None,
+            workspace=None, events=None, expand_events=None, stream=None, want_lse=True):
+    """mla_prefill: causal attention of the last T cached rows' queries
+    (q_nope [B, T, H, 128], q_pe [B, T, H, 64]) over their sequences, in the
+    recompute mode. Returns (out [B, T, H, 128], lse [B, T, H])."""
+    lib = load()
+    B, T, H = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+    d = dims(H)
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, T, H, D_V), dtype=q_nope.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(H, B, max_len), dtype=torch.uint8,
+                                device=dev)
+    opts = None
+    if events is not None or expand_events is not None:
+        o = PrefillOptions()
+        if events is not None:
+            o.attn_begin, o.attn_end = events
+        if expand_events is not None:
+            o.expand_begin, o.expand_end = expand_events
+        opts = ctypes.byref(o)
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    _check(lib.mla_prefill(
+        ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        dtype_code(q_nope.dtype), _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+        dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table), max_blocks,
+        block_size, _ptr(lengths), B, T, max_len, 0.0 if softmax_scale is None else softmax_scale,
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), opts, _stream(stream)))
+    return out, lse

@@ -13,6 +13,7 @@
 #include "decode_mfma.hpp"
 #include "fp32_path.hpp"
 #include "kv_project.hpp"
+#include "prefill_mfma.hpp"
 #include "project_mfma.hpp"
 
 using namespace mla;
@@ -125,6 +126,26 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // the attention kernels form a tile's buffer records and lane offsets as
 // 32-bit products of up to 32 rows times the stride.
 constexpr int64_t kMaxRowStrideBytes = (int64_t)1 << 24;
+
+// Prefill workspace: W_UV transposed [H, 128, 512] (bf16), decompressed keys
+// and values [B, H, cap, 128] each, RoPE keys [B, cap, 64] (fp16), with cap
+// = max_len rounded up to the expansion tile.
+struct PrefillWs {
+  size_t wuvt, kx, vx, kpx, total;
+  int cap;
+};
+
+PrefillWs prefill_ws(int B, int H, int max_len) {
+  PrefillWs w;
+  w.cap = (int)(((int64_t)max_len + EX_ROWS - 1) / EX_ROWS * EX_ROWS);
+  const size_t kv = (size_t)B * H * w.cap * D_N * 2;
+  w.wuvt = 0;
+  w.kx = align_up((size_t)H * D_V * D_C * 2, 256);
+  w.vx = align_up(w.kx + kv, 256);
+  w.kpx = align_up(w.vx + kv, 256);
+  w.total = align_up(w.kpx + (size_t)B * w.cap * D_R * 2, 256);
+  return w;
+}
 
 // Scratch of mla_decode_paged_noalloc: the absorbed queries and split
 // partials that mla_decode_paged keeps in the caller's workspace. Each device
@@ -523,6 +544,111 @@ mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, co
   return run_decode(dims, q_nope, q_pe, w_uk, w_uv, act, latent, ls, rope, rs, scales, cdt, rows,
                     0, block_table, max_blocks, block_size, lengths, batch, max_len,
                     softmax_scale, out, lse, ws, kScratchBytes, opts, stream);
+}
+
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_len) {
+  if (!dims_supported(dims) || batch < 0 || max_len < 0 || max_len > (1 << 30)) return 0;
+  if (batch == 0 || max_len == 0) return 256;
+  return prefill_ws(batch, dims->heads, max_len).total;
+}
+
+mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                       const void* w_uk, const void* w_uv, mla_dtype act, const void* latent,
+                       int64_t ls, const void* rope, int64_t rs, mla_dtype cdt, int64_t rows,
+                       int64_t seq_capacity, const int32_t* block_table, int32_t max_blocks,
+                       int32_t block_size, const int32_t* lengths, int32_t batch, int32_t chunk,
+                       int32_t max_len, float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, const mla_prefill_options* opts,
+                       hipStream_t stream) {
+  if (!dims) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || chunk < 0 || max_len < 0 || max_len > (1 << 30)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (act != MLA_BF16 || cdt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (dims->heads % 32 != 0) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0 || chunk == 0) return MLA_OK;
+  if (chunk > max_len) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_pe || !w_uk || !w_uv || !latent || !rope || !lengths || !out)
+    return MLA_ERR_INVALID_ARG;
+  if (ls < D_C || rs < D_R || rows < 1 || rows > INT32_MAX) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(latent) || !aligned16(rope) || (ls * 2) % 16 != 0 || (rs * 2) % 16 != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)q_nope | (uintptr_t)q_pe | (uintptr_t)w_uk | (uintptr_t)w_uv |
+       (uintptr_t)out) % 16 != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (block_size <= 0 || block_size % TILE != 0 || max_blocks <= 0 ||
+        (int64_t)max_blocks * block_size < max_len || rows < block_size)
+      return MLA_ERR_INVALID_ARG;
+  } else {
+    if (seq_capacity < max_len || seq_capacity < 1 || (int64_t)batch * seq_capacity > rows)
+      return MLA_ERR_INVALID_ARG;
+  }
+  const int B = batch, H = dims->heads;
+  const PrefillWs wl = prefill_ws(B, H, max_len);
+  if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
+    return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  if (softmax_scale == 0.f) softmax_scale = 1.0f / std::sqrt((float)(D_N + D_R));
+  (void)hipGetLastError();
+
+  bf16* wuvt = (bf16*)(ws + wl.wuvt);
+  hipLaunchKernelGGL(mla_wuv_transpose_kernel, dim3(H * 16), dim3(256), 0, stream,
+                     (const bf16*)w_uv, wuvt, H);
+  MLA_TRY(launch_status());
+
+  ExpandParams ep;
+  ep.latent = (const bf16*)latent;
+  ep.latent_stride = ls;
+  ep.rope = (const bf16*)rope;
+  ep.rope_stride = rs;
+  ep.rows = rows;
+  ep.seq_capacity = seq_capacity;
+  ep.block_table = block_table;
+  ep.max_blocks = max_blocks;
+  ep.block_size = block_size;
+  ep.lengths = lengths;
+  ep.w_uk = (const bf16*)w_uk;
+  ep.w_uvt = wuvt;
+  ep.kx = (_Float16*)(ws + wl.kx);
+  ep.vx = (_Float16*)(ws + wl.vx);
+  ep.kpx = (_Float16*)(ws + wl.kpx);
+  ep.B = B;
+  ep.H = H;
+  ep.cap = wl.cap;
+  ep.max_len = max_len;
+  const int ntile = ceil_div(max_len, EX_ROWS);
+  const dim3 egrid((unsigned)((int64_t)8 * (H / 8) * B * ntile));
+  hipEvent_t e0 = opts ? opts->expand_begin : nullptr, e1 = opts ? opts->expand_end : nullptr;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(mla_prefill_expand_kernel, egrid, dim3(256), 0, stream, e0, e1, 0, ep);
+  else
+    hipLaunchKernelGGL(mla_prefill_expand_kernel, egrid, dim3(256), 0, stream, ep);
+  MLA_TRY(launch_status());
+
+  PrefillParams pp;
+  pp.q_nope = (const bf16*)q_nope;
+  pp.q_pe = (const bf16*)q_pe;
+  pp.kx = ep.kx;
+  pp.vx = ep.vx;
+  pp.kpx = ep.kpx;
+  pp.lengths = lengths;
+  pp.B = B;
+  pp.H = H;
+  pp.T = chunk;
+  pp.cap = wl.cap;
+  pp.max_len = max_len;
+  pp.c = softmax_scale * LOG2E;
+  pp.out = (bf16*)out;
+  pp.lse = lse;
+  const int nqt = ceil_div(chunk, PF_Q);
+  const dim3 agrid((unsigned)((int64_t)8 * ceil_div((int64_t)B * H, 8) * nqt));
+  hipEvent_t a0 = opts ? opts->attn_begin : nullptr, a1 = opts ? opts->attn_end : nullptr;
+  if (a0 || a1)
+    hipExtLaunchKernelGGL(mla_prefill_attn_kernel, agrid, dim3(256), 0, stream, a0, a1, 0, pp);
+  else
+    hipLaunchKernelGGL(mla_prefill_attn_kernel, agrid, dim3(256), 0, stream, pp);
+  return launch_status();
 }
 
 mla_status mla_cache_append(const mla_dims* dims, const void* c_kv, const void* k_pe,

@@ -299,6 +299,80 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* q_nope, const void
                             size_t workspace_bytes, const mla_decode_options* opts,
                             hipStream_t stream);
 
+/* Optional timing events of mla_prefill (pass NULL for none): if non-NULL,
+ * attn_begin / attn_end record the start and end of the causal attention
+ * kernel, expand_begin / expand_end those of the key/value decompression,
+ * on `stream`. */
+typedef struct {
+  hipEvent_t attn_begin;
+  hipEvent_t attn_end;
+  hipEvent_t expand_begin;
+  hipEvent_t expand_end;
+} mla_prefill_options;
+
+/* Workspace bytes needed by mla_prefill (0 on invalid sizes): W_UV
+ * transposed, and the decompressed keys and values of every head for
+ * max_len tokens of each sequence (256 bytes per token and head, plus 128
+ * bytes per token for the RoPE keys). */
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_len);
+
+/*
+ * mla_prefill: attention of a chunk of new tokens (a prompt, or a chunk of
+ * one) over their sequence's cache, in the recompute mode.
+ *
+ * The chunk's `chunk` tokens of sequence b are the last rows of its cache:
+ * the cache holds lengths[b] rows, and query i (0 <= i < chunk) sits at
+ * position p = lengths[b] - chunk + i and attends to rows 0 .. p (the causal
+ * mask of "How DeepSeek Rewrote the Transformer [MLA]", section "Classic
+ * attention and the cost of the KV cache"; the cache rows of the chunk are
+ * written beforehand, e.g. by mla_cache_append). Queries with p < 0 see no
+ * row: out = 0 and lse = -inf. For every head h, with keys
+ * k_t = [W_UK[h] c_t | k^R_t] and values v_t = c_t W_UV[h] decompressed from
+ * the latent rows ("DeepSeek AI efficiency, architecture, benchmarks",
+ * section "Architectural Innovations: Multi-Head Latent Attention (MLA)",
+ * equations for K and V; "Como a MLA da DeepSeek cortou 93% da memoria",
+ * section "O preco da economia: mais contas": with many queries the
+ * recompute of K and V is cheaper than absorbing every query):
+ *   s_t        = softmax_scale * (q_nope . W_UK[h] c_t + q_pe . k^R_t),  t <= p
+ *   out[b,i,h] = sum_t softmax(s)_t c_t W_UV[h]
+ *   lse[b,i,h] = ln sum_t exp(s_t)
+ * This equals mla_decode of each query over its own prefix.
+ *
+ * Arguments
+ *   q_nope [batch, chunk, H, 128], q_pe [batch, chunk, H, 64] (already
+ *               rotated): bf16, row-major
+ *   w_uk [H, 128, 512], w_uv [H, 512, 128]: bf16
+ *   act_dtype   MLA_BF16: bf16 queries, weights and output. The
+ *               decompression runs on bf16 MFMA with fp32 accumulation; the
+ *               attention products take the queries, keys, values and
+ *               softmax weights in fp16 (fp32 accumulation), so queries and
+ *               decompressed keys and values beyond +-65504 saturate
+ *   latent, rope, strides, cache_dtype (MLA_BF16), cache_rows: the cache
+ *   block_table NULL: contiguous cache, sequence b at rows
+ *               [b*seq_capacity, b*seq_capacity + lengths[b]);
+ *               otherwise paged as in mla_decode_paged (block_size a
+ *               positive multiple of 32)
+ *   lengths     [batch] int32 (device): rows of each sequence, chunk included
+ *   chunk       queries per sequence (>= 1)
+ *   max_len     host upper bound of lengths (sizes the workspace)
+ *   softmax_scale  as for mla_decode (0 selects 1/sqrt(d_nope + d_rope))
+ *   out [batch, chunk, H, 128] bf16;  lse [batch, chunk, H] fp32 or NULL
+ *   workspace   at least mla_prefill_workspace_size(dims, batch, max_len)
+ *               bytes, 256-byte aligned
+ * Errors: INVALID_ARG, UNSUPPORTED (dtypes other than bf16, heads not a
+ * multiple of 32), WORKSPACE, HIP, as for mla_decode. batch == 0 is a valid
+ * no-op. Three launches on `stream`.
+ */
+mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_pe,
+                       const void* w_uk, const void* w_uv, mla_dtype act_dtype,
+                       const void* latent, int64_t latent_stride, const void* rope,
+                       int64_t rope_stride, mla_dtype cache_dtype, int64_t cache_rows,
+                       int64_t seq_capacity, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, int32_t block_size, const int32_t* lengths,
+                       int32_t batch, int32_t chunk, int32_t max_len, float softmax_scale,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       const mla_prefill_options* opts, hipStream_t stream);
+
 /*
  * mla_decode_paged_noalloc: mla_decode_paged without a workspace argument,
  * for callers that cannot allocate device memory or pass a buffer of their

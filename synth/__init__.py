@@ -204,6 +204,14 @@ def append_inputs(seed: int, B: int, in_dtype: str, device="cpu"):
     return c, k
 
 
+def prefill_queries(seed: int, B: int, T: int, H: int, act: str = "bf16", device="cpu"):
+    """Queries of a prefill chunk: q_nope [B, T, H, 128] and q_pe [B, T, H, 64]
+    (already rotated) ~ N(0,1). Seeds: seed, seed + 1."""
+    qn = to_storage(normal((B, T, H, D_NOPE), seed, device), act)
+    qp = to_storage(normal((B, T, H, D_ROPE), seed + 1, device), act)
+    return qn, qp
+
+
 D_MODEL = 7168    # hidden width of the DeepSeek-V3 setting
 
 

@@ -200,3 +200,32 @@ def test_noalloc_rejects_oversize_plans_before_any_launch():
     assert call(0, 4096) == 0                     # no-op
     assert call(4, 4096, ptr=None) == 1           # null pointers
     assert call(4, 4096, bs=48) == 1              # block size not a multiple of 32
+
+
+def test_prefill_argument_errors():
+    """mla_prefill validates before launching: dtypes (bf16 only), heads a
+    multiple of 32, chunk <= max_len, pointers, layout and workspace."""
+    lib = mla.load()
+    p = ctypes.c_void_p(16)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(mla.dims(128)), 1, 4096) > \
+        2 * 128 * 4096 * 256
+    assert lib.mla_prefill_workspace_size(ctypes.byref(mla.dims(128)), -1, 4096) == 0
+
+    def call(heads=128, act=1, cdt=1, batch=1, chunk=16, max_len=64, ptr=p, cap=64, rows=64,
+             table=None, bs=64, mb=0, ws_bytes=1 << 30, ws=None, scale=0.0):
+        d = mla.dims(heads)
+        return lib.mla_prefill(ctypes.byref(d), ptr, ptr, ptr, ptr, act, ptr, 576, ptr, 576, cdt,
+                               rows, cap, table, mb, bs, ptr, batch, chunk, max_len, scale, ptr,
+                               None, ws if ws is not None else ctypes.c_void_p(1 << 20), ws_bytes,
+                               None, None)
+    assert call(batch=0) == 0 and call(chunk=0) == 0           # no-ops
+    assert call(act=0) == 2 and call(cdt=2) == 2               # f32 / fp8: unsupported
+    assert call(heads=48) == 2
+    assert call(chunk=65) == 1                                 # chunk > max_len
+    assert call(ptr=None) == 1
+    assert call(cap=32) == 1                                   # capacity < max_len
+    assert call(scale=float("inf")) == 1
+    assert call(table=p, bs=48, mb=2) == 1                     # block size not a multiple of 32
+    assert call(table=p, bs=32, mb=1) == 1                     # table shorter than max_len
+    assert call(ws_bytes=1024) == 3
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == 3       # misaligned workspace
