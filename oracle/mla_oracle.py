@@ -310,6 +310,58 @@ def decode_seq_absorbed(q_nope, q_pe, w_uk, w_uv, C, R, scale):
     return np.einsum("hc,hcv->hv", o_lat, w_uv), m + np.log(l)
 
 
+def decode_model_io(x, q_pe, w_q, w_uk, w_uv, w_o, C, R, scale):
+    """Decode of one token from its model-width input to its model-width
+    output, unfused (the definition): q_nope[h] = W_Q[h] x (column
+    convention of [TN]'s projections; W_Q[h] is [d_nope, d_model]), each
+    head's attention over the cache as in decode_head_nonabsorbed, then the
+    output projection y = sum_h o[h] W_O[h] (W_O[h] is [d_v, d_model]: head
+    h's rows of the output matrix W_O that [WL] "MLA: compress the pair, not
+    the heads" names).
+
+    x [d_model], q_pe [H, d_rope] (already rotated), C [n, d_c], R [n, d_rope].
+    Returns y [d_model] and lse [H]."""
+    H = w_q.shape[0]
+    y = np.zeros(w_o.shape[2])
+    lse = np.empty(H)
+    for h in range(H):
+        q_nope = w_q[h] @ x
+        o, lse[h] = decode_head_nonabsorbed(q_nope, q_pe[h], w_uk[h], w_uv[h], C, R, scale)
+        y += o @ w_o[h]
+    return y, lse
+
+
+def fuse_query_weight(w_q_h, w_uk_h):
+    """W_UK absorbed into the query projection, offline ([WL] "MLA: compress
+    the pair, not the heads": absorb W_UK into the Q matrix before serving):
+    q_lat = q_nope W_UK[h] = (W_Q[h] x)^T W_UK[h], so q_lat = W_QK[h] x with
+    W_QK[h] = W_UK[h]^T W_Q[h], [d_c, d_model]."""
+    return w_uk_h.T @ w_q_h
+
+
+def fuse_output_weight(w_uv_h, w_o_h):
+    """W_UV absorbed into the output matrix, offline (same passage: W_UV goes
+    into W_O): o W_O[h] = (o_lat W_UV[h]) W_O[h] = o_lat W_VO[h] with
+    W_VO[h] = W_UV[h] W_O[h], [d_c, d_model]."""
+    return w_uv_h @ w_o_h
+
+
+def decode_model_io_fused(x, q_pe, w_qk, w_vo, C, R, scale):
+    """The same decode with the fused weights: every head scores its absorbed
+    query W_QK[h] x against the latent rows, mixes them, and the mixed latent
+    goes through W_VO[h] straight to the model width.
+    Returns y [d_model] and lse [H]."""
+    H = w_qk.shape[0]
+    y = np.zeros(w_vo.shape[2])
+    lse = np.empty(H)
+    for h in range(H):
+        q_lat = w_qk[h] @ x
+        s = scale * (C @ q_lat + R @ q_pe[h])
+        o_lat, lse[h] = softmax_attend(s, C)
+        y += o_lat @ w_vo[h]
+    return y, lse
+
+
 def causal_prefill(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
     """Full causal self-attention of T queries over T cached rows for one head:
     row t attends to rows 0..t ([KV] "KV Cache": the causal mask hides the

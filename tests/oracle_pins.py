@@ -227,6 +227,59 @@ def pin_chunked_prefill(orc):
                 assert np.allclose(full, out, rtol=1e-12, atol=1e-14)
 
 
+def _io_case(seed, n=6, H=3, d_c=8, d_n=4, d_r=2, d_v=3, d_model=5):
+    r = _rng(seed)
+    return dict(x=r.standard_normal(d_model), q_pe=r.standard_normal((H, d_r)),
+                w_q=r.standard_normal((H, d_n, d_model)), w_uk=r.standard_normal((H, d_n, d_c)),
+                w_uv=r.standard_normal((H, d_c, d_v)), w_o=r.standard_normal((H, d_v, d_model)),
+                C=r.standard_normal((n, d_c)), R=r.standard_normal((n, d_r)),
+                scale=1 / math.sqrt(d_n + d_r))
+
+
+def pin_fused_io(orc):
+    """Offline absorption: decoding with the fused weights W_QK[h] =
+    W_UK[h]^T W_Q[h] and W_VO[h] = W_UV[h] W_O[h] equals the unfused
+    definition to float64 rounding (associativity, the identity the pages
+    rest the absorption on); the unfused definition with one head and
+    W_O = I reduces to decode (pinned by brute force) with q_nope = W_Q x."""
+    for seed in (70, 71, 72):
+        c = _io_case(seed)
+        y, lse = orc.decode_model_io(c["x"], c["q_pe"], c["w_q"], c["w_uk"], c["w_uv"], c["w_o"],
+                                     c["C"], c["R"], c["scale"])
+        w_qk = np.stack([orc.fuse_query_weight(c["w_q"][h], c["w_uk"][h]) for h in range(3)])
+        w_vo = np.stack([orc.fuse_output_weight(c["w_uv"][h], c["w_o"][h]) for h in range(3)])
+        assert w_qk.shape == (3, 8, 5) and w_vo.shape == (3, 8, 5)
+        y2, lse2 = orc.decode_model_io_fused(c["x"], c["q_pe"], w_qk, w_vo, c["C"], c["R"],
+                                             c["scale"])
+        assert np.max(np.abs(y - y2)) <= 1e-12 * np.max(np.abs(y))
+        assert np.max(np.abs(lse - lse2)) <= 1e-12 * max(1.0, np.max(np.abs(lse)))
+    c = _io_case(73, H=1, d_v=5, d_model=5)
+    c["w_o"] = np.eye(5)[None]
+    y, lse = orc.decode_model_io(c["x"], c["q_pe"], c["w_q"], c["w_uk"], c["w_uv"], c["w_o"],
+                                 c["C"], c["R"], c["scale"])
+    o, l = orc.decode((c["w_q"][0] @ c["x"])[None, None], c["q_pe"][None], c["w_uk"], c["w_uv"],
+                      [c["C"]], [c["R"]], c["scale"])
+    assert np.allclose(y, o[0, 0], rtol=1e-13, atol=1e-14) and abs(lse[0] - l[0, 0]) < 1e-13
+
+
+def pin_fused_hand_example(orc):
+    """Hand-worked fusion with square, non-symmetric 2x2 blocks, so that a
+    product in the wrong order or of a transposed operand gives other
+    numbers: W_UK = [[1,2],[3,4]] (d_nope x d_c), W_Q = [[0,1],[2,1]]
+    (d_nope x d_model): W_UK^T W_Q = [[6,4],[8,6]] (W_Q^T W_UK = [[6,8],[4,6]],
+    W_UK W_Q^T = [[2,4],[4,10]]). W_UV = [[1,0],[2,1]], W_O = [[1,1],[0,2]]:
+    W_UV W_O = [[1,1],[2,4]] (W_O W_UV = [[3,1],[4,2]])."""
+    w_uk = np.array([[1.0, 2.0], [3.0, 4.0]])
+    w_q = np.array([[0.0, 1.0], [2.0, 1.0]])
+    assert np.array_equal(orc.fuse_query_weight(w_q, w_uk), [[6.0, 4.0], [8.0, 6.0]])
+    w_uv = np.array([[1.0, 0.0], [2.0, 1.0]])
+    w_o = np.array([[1.0, 1.0], [0.0, 2.0]])
+    assert np.array_equal(orc.fuse_output_weight(w_uv, w_o), [[1.0, 1.0], [2.0, 4.0]])
+    # a non-square case: fused shapes are [d_c, d_model]
+    assert orc.fuse_query_weight(np.ones((4, 7)), np.ones((4, 9))).shape == (9, 7)
+    assert orc.fuse_output_weight(np.ones((9, 4)), np.ones((4, 7))).shape == (9, 7)
+
+
 def pin_lse_combine(orc):
     """Split the rows in two, decode each part, merge with the log-sum-exp
     weights e^{lse_i - lse}: the merge equals the decode over all rows. This
@@ -352,4 +405,5 @@ PROJECTION_PINS = [pin_projection_hand_example, pin_projection_basis, pin_projec
 
 ALL_DECODE_PINS = [pin_bruteforce, pin_single_row, pin_zero_query, pin_rope_shift,
                    pin_permutation, pin_absorption, pin_seq_absorbed, pin_hand_example,
-                   pin_causal_prefill, pin_chunked_prefill, pin_lse_combine, pin_empty]
+                   pin_causal_prefill, pin_chunked_prefill, pin_fused_io,
+                   pin_fused_hand_example, pin_lse_combine, pin_empty]

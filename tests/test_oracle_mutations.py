@@ -136,6 +136,23 @@ def m_chunk_mask_excludes_self(o):
     o.chunked_prefill = f
 
 
+def m_fused_query_transposed(o):
+    o.fuse_query_weight = lambda w_q_h, w_uk_h: (w_q_h.T @ w_uk_h).T if w_q_h.shape == w_uk_h.shape \
+        else w_uk_h.T @ w_q_h[::-1]
+
+
+def m_fused_output_order(o):
+    o.fuse_output_weight = lambda w_uv_h, w_o_h: (w_o_h.T @ w_uv_h.T).T[::-1]
+
+
+def m_io_output_one_head(o):
+    def f(x, q_pe, w_q, w_uk, w_uv, w_o, C, R, scale):
+        q_nope = w_q[0] @ x
+        out, l = o.decode_head_nonabsorbed(q_nope, q_pe[0], w_uk[0], w_uv[0], C, R, scale)
+        return out @ w_o[0], np.full(w_q.shape[0], l)
+    o.decode_model_io = f
+
+
 def m_absorbed_missing_uv(o):
     def f(q_nope, q_pe, w_uk_h, w_uv_h, C, R, scale):
         q_lat = q_nope @ w_uk_h
@@ -184,7 +201,8 @@ MUTATIONS = [m_drop_rope_term, m_wrong_scale, m_head_index, m_uv_for_uk_layout,
              m_unnormalised, m_lse_without_max, m_rope_sign, m_rope_half_split, m_rope_freq,
              m_paged_slot, m_paged_block, m_causal_mask, m_absorbed_missing_uv,
              m_seq_heads_reversed, m_seq_softmax_over_heads, m_chunk_offset,
-             m_chunk_mask_excludes_self,
+             m_chunk_mask_excludes_self, m_fused_query_transposed, m_fused_output_order,
+             m_io_output_one_head,
              m_proj_transposed, m_proj_last_term_dropped, m_proj_key_from_latent_weights,
              m_proj_key_not_rotated]
 
