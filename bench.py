@@ -76,6 +76,7 @@ def parse():
     ap.add_argument("--write-mfma", nargs=2, default=None, metavar=("COUNTERS_CSV", "TRACE_CSV"))
     ap.add_argument("--project", action="store_true")
     ap.add_argument("--prefill", action="store_true")
+    ap.add_argument("--fused", action="store_true")
     ap.add_argument("--with-projection", action="store_true")
     return ap.parse_args()
 
@@ -489,6 +490,99 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_fused(args):
+    """Offline absorption decided by measurement: one decode step from the
+    tokens' model-width input x (B=64, d_model 7168) to the attention output
+    at model width, over the B=64 H=128 N=4096 paged bf16 cache,
+      fused:   mla_decode_fused with W_QK = W_UK^T W_Q and W_VO = W_UV W_O
+               (mla_fuse_weights, offline);
+      unfused: q_nope = x W_Q^T and y = o W_O as library GEMMs (torch.matmul)
+               around mla_decode_paged (runtime absorption of W_UK, W_UV).
+    Both run in the same process, alternating, on two weight sets each."""
+    import torch
+    import head_latent_attention_07_amd as mla
+    import synth
+
+    mla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, D = 64, 128, synth.D_MODEL
+    sets = []
+    for layer in range(2):
+        inp = synth.make_inputs("3u", layer=layer, gen_device="cuda").to(dev)
+        x, w_q, w_o = synth.model_io_inputs(4400 + 10 * layer, B, H, D, device=dev)
+        w_qk, w_vo = mla.fuse_weights(w_q, inp.w_uk, inp.w_uv, w_o)
+        lat, rope = mla.split_cache(inp.cache)
+        ws = torch.empty(mla.decode_fused_workspace_size(H, B, inp.max_len, D), dtype=torch.uint8,
+                         device=dev)
+        ws_u = torch.empty(mla.workspace_size(H, B, inp.max_len, mla.MLA_BF16, mla.MLA_BF16),
+                           dtype=torch.uint8, device=dev)
+        sets.append(dict(inp=inp, x=x, wq=w_q.reshape(H * 128, D), wo=w_o.reshape(H * 128, D),
+                         w_qk=w_qk, w_vo=w_vo, lat=lat, rope=rope, ws=ws, ws_u=ws_u,
+                         y=torch.empty((B, D), dtype=torch.bfloat16, device=dev),
+                         o=torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    def fused(S):
+        inp = S["inp"]
+        mla.decode_fused(S["x"], inp.q_pe, S["w_qk"], S["w_vo"], S["lat"], S["rope"], inp.lengths,
+                         inp.max_len, block_table=inp.block_table, block_size=inp.block_size,
+                         out=S["y"], workspace=S["ws"])
+
+    def unfused(S):
+        inp = S["inp"]
+        q_nope = torch.matmul(S["x"], S["wq"].t()).view(B, H, 128)
+        mla.decode_paged(q_nope, inp.q_pe, inp.w_uk, inp.w_uv, S["lat"], S["rope"], inp.lengths,
+                         inp.max_len, block_table=inp.block_table, block_size=inp.block_size,
+                         out=S["o"], workspace=S["ws_u"])
+        torch.matmul(S["o"].view(B, H * 128), S["wo"], out=S["y"])
+
+    def timed(fn, steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            fn(sets[i % 2])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    for _ in range(max(1, args.warmup // 2)):
+        fused(sets[0]); unfused(sets[0]); fused(sets[1]); unfused(sets[1])
+    torch.cuda.synchronize()
+    tf, tu = [], []
+    for _ in range(4):   # alternate in rounds, so both see the same clock history
+        tf += timed(fused, args.steps // 4)
+        tu += timed(unfused, args.steps // 4)
+    fms, ums = sum(tf) / len(tf), sum(tu) / len(tu)
+    inp0 = sets[0]["inp"]
+    cache_bytes = int(inp0.lengths.sum()) * 1152
+    fused_w = 2 * H * 512 * D * 2
+    unfused_w = 2 * H * 128 * D * 2 + 2 * H * 128 * 512 * 2
+    fb = fused_w + cache_bytes
+    line = {
+        "metric": "MLA decode step from model-width input, weights fused offline (tokens/s)",
+        "value": B / (fms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": len(tf),
+        "warmup": args.warmup, "ms_per_step": fms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normals; random-init weights of the DeepSeek-V3 MLA widths)",
+        "config": {"workload": "mla_decode_fused_b64_h128_n4096_paged_bf16_d7168", "B": B, "H": H,
+                   "N": 4096, "d_model": D},
+        "roofline": {"bound": "hbm", "achieved": fb / (fms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "mla_decode_fused (all launches)",
+                     "bytes_per_launch": fb,
+                     "launch_us_p10_p50_p90": [percentile(tf, q) * 1e3 for q in (10, 50, 90)]},
+        "fused_weight_bytes": fused_w,
+        "unfused": {"ms_per_step": ums, "tokens_per_s": B / (ums * 1e-3),
+                    "weight_bytes": unfused_w,
+                    "step_us_p10_p50_p90": [percentile(tu, q) * 1e3 for q in (10, 50, 90)],
+                    "what": "torch.matmul(x, W_Q^T) + mla_decode_paged + torch.matmul(o, W_O)"},
+        "fused_over_unfused_time": fms / ums,
+    }
+    print(json.dumps(line), flush=True)
+
+
 SIMD_COUNT = 1024            # MI355X: 256 CUs x 4 SIMDs
 
 WORKLOADS = {"1": "mla_decode_b1_h16_n512_f32", "2": "mla_decode_b1_h128_n4096_bf16",
@@ -574,6 +668,11 @@ def percentile(vals, q):
 
 def main():
     args = parse()
+    if args.fused:
+        args.steps = 200 if args.steps is None else args.steps
+        args.warmup = 40 if args.warmup is None else args.warmup
+        bench_fused(args)
+        return
     if args.prefill:
         args.steps = 50 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup

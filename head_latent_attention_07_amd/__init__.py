@@ -23,7 +23,8 @@ D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
            "mla_project_append", "mla_project_workspace_size", "mla_project",
-           "mla_decode_paged_noalloc", "mla_prefill_workspace_size", "mla_prefill")
+           "mla_decode_paged_noalloc", "mla_prefill_workspace_size", "mla_prefill",
+           "mla_fuse_weights", "mla_decode_fused_workspace_size", "mla_decode_fused")
 NOALLOC_SCRATCH_BYTES = 80 << 20      # MLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -103,6 +104,17 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mla_prefill.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, _P, ctypes.c_int, _P, _I64, _P,
                                 _I64, ctypes.c_int, _I64, _I64, _P, _I32, _I32, _P, _I32, _I32,
                                 _I32, _F, _P, _P, _P, _SZ, ctypes.POINTER(PrefillOptions), _P]
+    lib.mla_fuse_weights.restype = ctypes.c_int
+    lib.mla_fuse_weights.argtypes = [ctypes.POINTER(Dims), _I32, _P, _P, _P, _P, ctypes.c_int, _P,
+                                     _P, _P]
+    lib.mla_decode_fused_workspace_size.restype = _SZ
+    lib.mla_decode_fused_workspace_size.argtypes = [ctypes.POINTER(Dims), _I32, _I32, _I32,
+                                                    ctypes.POINTER(DecodeOptions)]
+    lib.mla_decode_fused.restype = ctypes.c_int
+    lib.mla_decode_fused.argtypes = [ctypes.POINTER(Dims), _P, _P, _P, _P, _I32, ctypes.c_int, _P,
+                                     _I64, _P, _I64, _P, ctypes.c_int, _I64, _I64, _P, _I32, _I32,
+                                     _P, _I32, _I32, _F, _P, _P, _P, _SZ,
+                                     ctypes.POINTER(DecodeOptions), _P]
     lib.mla_project_workspace_size.restype = _SZ
     lib.mla_project_workspace_size.argtypes = [_I32, _I32]
     lib.mla_project.restype = ctypes.c_int
@@ -359,4 +371,51 @@ def prefill(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *, seq_cap
         dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table), max_blocks,
         block_size, _ptr(lengths), B, T, max_len, 0.0 if softmax_scale is None else softmax_scale,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), opts, _stream(stream)))
+    return out, lse
+
+
+def fuse_weights(w_q, w_uk, w_uv, w_o, *, w_qk=None, w_vo=None, stream=None):
+    """mla_fuse_weights: W_QK[h] = W_UK[h]^T W_Q[h] ([H, 512, d_model]) and
+    W_VO stored [d_model, 512 H]. Returns (w_qk, w_vo)."""
+    H, _, D = w_q.shape
+    if w_qk is None:
+        w_qk = torch.empty((H, D_C, D), dtype=w_q.dtype, device=w_q.device)
+    if w_vo is None:
+        w_vo = torch.empty((D, H * D_C), dtype=w_q.dtype, device=w_q.device)
+    _check(load().mla_fuse_weights(ctypes.byref(dims(H)), D, _ptr(w_q), _ptr(w_uk), _ptr(w_uv),
+                                   _ptr(w_o), dtype_code(w_q.dtype), _ptr(w_qk), _ptr(w_vo),
+                                   _stream(stream)))
+    return w_qk, w_vo
+
+
+def decode_fused_workspace_size(heads: int, batch: int, max_len: int, d_model: int,
+                                num_splits: int = 0) -> int:
+    return int(load().mla_decode_fused_workspace_size(ctypes.byref(dims(heads)), batch, max_len,
+                                                      d_model, _opts(num_splits)))
+
+
+def decode_fused(x, q_pe, w_qk, w_vo, latent, rope, lengths, max_len, *, seq_capacity=0,
+                 block_table=None, block_size=64, scales=None, softmax_scale=None, out=None,
+                 lse=None, workspace=None, num_splits=0, events=None, stream=None):
+    """mla_decode_fused: model-width input x [B, d_model] to model-width
+    output [B, d_model] through the fused weights. Returns (out, lse)."""
+    lib = load()
+    B, D = x.shape
+    H = q_pe.shape[1]
+    dev = x.device
+    if out is None:
+        out = torch.empty((B, D), dtype=x.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(decode_fused_workspace_size(H, B, max_len, D, num_splits),
+                                dtype=torch.uint8, device=dev)
+    max_blocks = 0 if block_table is None else block_table.shape[1]
+    _check(lib.mla_decode_fused(
+        ctypes.byref(dims(H)), _ptr(x), _ptr(q_pe), _ptr(w_qk), _ptr(w_vo), D,
+        dtype_code(x.dtype), _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+        _ptr(scales), dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table),
+        max_blocks, block_size, _ptr(lengths), B, max_len,
+        0.0 if softmax_scale is None else softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _opts(num_splits, events), _stream(stream)))
     return out, lse

@@ -12,6 +12,7 @@
 #include "append.hpp"
 #include "decode_mfma.hpp"
 #include "fp32_path.hpp"
+#include "fused_io.hpp"
 #include "kv_project.hpp"
 #include "prefill_mfma.hpp"
 #include "project_mfma.hpp"
@@ -301,6 +302,114 @@ mla_status check_decode(const mla_dims* dims, const void* q_nope, const void* q_
   return MLA_OK;
 }
 
+// Parameters of the split attention kernels (bf16 / fp8 cache).
+DecodeParams decode_params(const bf16* q, const void* latent, int64_t ls, const void* rope,
+                           int64_t rs, const void* scales, int64_t rows, int64_t seq_capacity,
+                           const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                           const int32_t* lengths, int32_t max_len, int B, int H, const Plan& pl,
+                           _Float16* part_h, float* part_scale, float* part_lse) {
+  DecodeParams dp;
+  dp.q = q;
+  dp.latent = latent;
+  dp.latent_stride = ls;
+  dp.rope = rope;
+  dp.rope_stride = rs;
+  dp.scales = (const bf16*)scales;
+  dp.rows = rows;
+  dp.seq_capacity = seq_capacity;
+  dp.block_table = block_table;
+  dp.max_blocks = max_blocks;
+  dp.block_size = block_size;
+  dp.lengths = lengths;
+  dp.max_len = max_len;
+  dp.B = B;
+  dp.H = H;
+  dp.S = pl.S;
+  dp.tokens_per_split = pl.TS;
+  dp.G = pl.G;
+  dp.part_o = part_h;
+  dp.part_scale = part_scale;
+  dp.part_lse = part_lse;
+  return dp;
+}
+
+// Launch of the split attention kernel for the plan; with timing events, the
+// launch itself records the kernel's start and end (the dispatch's own
+// timestamps, not those of separate event packets).
+mla_status launch_attention(const DecodeParams& dp, const Plan& pl, bool fp8,
+                            const mla_decode_options* opts, hipStream_t stream) {
+  const int nq = dp.B * pl.S;
+  const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
+  hipEvent_t ev0 = opts ? opts->attn_begin : nullptr, ev1 = opts ? opts->attn_end : nullptr;
+  auto launch = [&](auto kern, int threads) {
+    if (ev0 || ev1)
+      hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, ev0, ev1, 0, dp);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, dp);
+  };
+  switch (pl.NW * 2 + (fp8 ? 1 : 0)) {
+    case 8: launch(mla_decode_bf16_kernel<4>, 256); break;
+    case 9: launch(mla_decode_fp8_kernel<4>, 256); break;
+    case 4: launch(mla_decode_bf16_kernel<2>, 128); break;
+    case 5: launch(mla_decode_fp8_kernel<2>, 128); break;
+    case 2: launch(mla_decode_bf16_kernel<1>, 64); break;
+    case 3: launch(mla_decode_fp8_kernel<1>, 64); break;
+    default: return MLA_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+// Split-K plan of a weight-streaming GEMM (M x K) . (N x K)^T: enough
+// workgroups (32-column tiles x K slices x batch groups of 128) to cover the
+// chip several times; every slice non-empty.
+struct SkPlan {
+  int S, cps, mgroups, msub;
+};
+
+SkPlan skinny_plan(int M, int N, int K) {
+  SkPlan pl;
+  const int nchunks = K / SG_CHUNK;
+  pl.mgroups = ceil_div(M, SG_MG);
+  pl.msub = pl.mgroups > 1 ? 4 : ceil_div(M, 32);
+  const int tiles = (N / 32) * pl.mgroups;
+  int S = std::max(1, std::min(ceil_div(1024, tiles), nchunks));
+  pl.cps = ceil_div(nchunks, S);
+  pl.S = ceil_div(nchunks, pl.cps);
+  return pl;
+}
+
+void launch_skinny(const SkinnyParams& sp, const SkPlan& pl, hipStream_t stream) {
+  const dim3 grid((unsigned)((sp.N / 32) * pl.S * pl.mgroups));
+  switch (pl.msub) {
+    case 1: hipLaunchKernelGGL(mla_skinny_gemm_kernel<1>, grid, dim3(256), 0, stream, sp); break;
+    case 2: hipLaunchKernelGGL(mla_skinny_gemm_kernel<2>, grid, dim3(256), 0, stream, sp); break;
+    case 3: hipLaunchKernelGGL(mla_skinny_gemm_kernel<3>, grid, dim3(256), 0, stream, sp); break;
+    default: hipLaunchKernelGGL(mla_skinny_gemm_kernel<4>, grid, dim3(256), 0, stream, sp); break;
+  }
+}
+
+// Workspace of mla_decode_fused: that of the decode (queries, split
+// partials) followed by the query GEMM's partials [Sq, B, 512 H] fp32, the
+// merged latent rows [B, 512 H] bf16 and the output GEMM's partials
+// [So, B, d_model] fp32.
+struct FusedWs {
+  WsLayout dec;
+  SkPlan qp, op;
+  size_t qpart, olat, opart, total;
+};
+
+FusedWs fused_ws(int B, int H, int D, const Plan& pl) {
+  FusedWs f;
+  f.dec = ws_layout(B, H, pl, MLA_BF16);
+  f.qp = skinny_plan(B, H * D_C, D);
+  f.op = skinny_plan(B, D, H * D_C);
+  f.qpart = f.dec.total;
+  f.olat = align_up(f.qpart + (size_t)f.qp.S * B * H * D_C * 4, 256);
+  f.opart = align_up(f.olat + (size_t)B * H * D_C * 2, 256);
+  f.total = align_up(f.opart + (size_t)f.op.S * B * D * 4, 256);
+  return f;
+}
+
 mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe,
                       const void* w_uk, const void* w_uv, mla_dtype act, const void* latent,
                       int64_t ls, const void* rope, int64_t rs, const void* scales,
@@ -401,50 +510,10 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
     hipLaunchKernelGGL(mla_absorb_kernel, dim3(absorb_blocks), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());
 
-  DecodeParams dp;
-  dp.q = q;
-  dp.latent = latent;
-  dp.latent_stride = ls;
-  dp.rope = rope;
-  dp.rope_stride = rs;
-  dp.scales = (const bf16*)scales;
-  dp.rows = rows;
-  dp.seq_capacity = seq_capacity;
-  dp.block_table = block_table;
-  dp.max_blocks = max_blocks;
-  dp.block_size = block_size;
-  dp.lengths = lengths;
-  dp.max_len = max_len;
-  dp.B = B;
-  dp.H = H;
-  dp.S = pl.S;
-  dp.tokens_per_split = pl.TS;
-  dp.G = pl.G;
-  dp.part_o = part_h;
-  dp.part_scale = part_scale;
-  dp.part_lse = part_lse;
-  const int nq = B * pl.S;
-  const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
-  // with timing events, the launch itself records the kernel's start and end
-  // (the dispatch's own timestamps, not those of separate event packets)
-  hipEvent_t ev0 = opts ? opts->attn_begin : nullptr, ev1 = opts ? opts->attn_end : nullptr;
-  auto launch = [&](auto kern, int threads) {
-    if (ev0 || ev1)
-      hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, ev0, ev1, 0, dp);
-    else
-      hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, dp);
-  };
-  const bool fp8 = (cdt == MLA_FP8_E4M3);
-  switch (pl.NW * 2 + (fp8 ? 1 : 0)) {
-    case 8: launch(mla_decode_bf16_kernel<4>, 256); break;
-    case 9: launch(mla_decode_fp8_kernel<4>, 256); break;
-    case 4: launch(mla_decode_bf16_kernel<2>, 128); break;
-    case 5: launch(mla_decode_fp8_kernel<2>, 128); break;
-    case 2: launch(mla_decode_bf16_kernel<1>, 64); break;
-    case 3: launch(mla_decode_fp8_kernel<1>, 64); break;
-    default: return MLA_ERR_UNSUPPORTED;
-  }
-  MLA_TRY(launch_status());
+  const DecodeParams dp = decode_params(q, latent, ls, rope, rs, scales, rows, seq_capacity,
+                                        block_table, max_blocks, block_size, lengths, max_len, B,
+                                        H, pl, part_h, part_scale, part_lse);
+  MLA_TRY(launch_attention(dp, pl, cdt == MLA_FP8_E4M3, opts, stream));
 
   CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
   hipLaunchKernelGGL(pl.S <= CB_G ? mla_combine_s4_kernel : mla_combine_kernel,
@@ -648,6 +717,109 @@ mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_p
     hipExtLaunchKernelGGL(mla_prefill_attn_kernel, agrid, dim3(256), 0, stream, a0, a1, 0, pp);
   else
     hipLaunchKernelGGL(mla_prefill_attn_kernel, agrid, dim3(256), 0, stream, pp);
+  return launch_status();
+}
+
+mla_status mla_fuse_weights(const mla_dims* dims, int32_t d_model, const void* w_q,
+                            const void* w_uk, const void* w_uv, const void* w_o, mla_dtype act,
+                            void* w_qk, void* w_vo, hipStream_t stream) {
+  if (!dims) return MLA_ERR_INVALID_ARG;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (act != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d_model <= 0 || d_model % 64 != 0) return MLA_ERR_INVALID_ARG;
+  if (!w_q || !w_uk || !w_uv || !w_o || !w_qk || !w_vo) return MLA_ERR_INVALID_ARG;
+  const int H = dims->heads, D = d_model;
+  (void)hipGetLastError();
+  const int per_head = (D_C / 64) * (D / 64);
+  // W_QK[h][c][k] = sum_j W_UK[h][j][c] W_Q[h][j][k]
+  FuseParams fq{(const bf16*)w_uk, D_C, 1, (int64_t)D_N * D_C,
+                (const bf16*)w_q, D, 1, (int64_t)D_N * D,
+                (bf16*)w_qk, D, 1, (int64_t)D_C * D, D_C, D, H};
+  hipLaunchKernelGGL(mla_fuse_weights_kernel, dim3(H * per_head), dim3(256), 0, stream, fq);
+  MLA_TRY(launch_status());
+  // W_VO stored [d_model][512 H]: entry (n, 512 h + c) = sum_j W_UV[h][c][j] W_O[h][j][n]
+  FuseParams fo{(const bf16*)w_uv, 1, D_V, (int64_t)D_C * D_V,
+                (const bf16*)w_o, D, 1, (int64_t)D_V * D,
+                (bf16*)w_vo, 1, (int64_t)H * D_C, D_C, D_C, D, H};
+  hipLaunchKernelGGL(mla_fuse_weights_kernel, dim3(H * per_head), dim3(256), 0, stream, fo);
+  return launch_status();
+}
+
+size_t mla_decode_fused_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_len,
+                                       int32_t d_model, const mla_decode_options* opts) {
+  if (!dims_supported(dims) || batch < 0 || max_len < 0 || d_model <= 0 || d_model % 64 != 0)
+    return 0;
+  if (batch == 0) return 256;
+  const Plan pl = make_plan(batch, dims->heads, max_len, MLA_BF16, opts);
+  return fused_ws(batch, dims->heads, d_model, pl).total;
+}
+
+mla_status mla_decode_fused(const mla_dims* dims, const void* x, const void* q_pe,
+                            const void* w_qk, const void* w_vo, int32_t d_model, mla_dtype act,
+                            const void* latent, int64_t ls, const void* rope, int64_t rs,
+                            const void* scales, mla_dtype cdt, int64_t rows, int64_t seq_capacity,
+                            const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                            const int32_t* lengths, int32_t batch, int32_t max_len,
+                            float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, const mla_decode_options* opts,
+                            hipStream_t stream) {
+  // the decode's own checks (x and the fused weights stand in for the
+  // query and weight arguments), then those of the fused form
+  MLA_TRY(check_decode(dims, x, q_pe, w_qk, w_vo, act, latent, ls, rope, rs, scales, cdt, rows,
+                       lengths, batch, max_len, softmax_scale, out));
+  if (act != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (opts && opts->append) return MLA_ERR_UNSUPPORTED;
+  if (d_model <= 0 || d_model % 64 != 0) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (block_table) {
+    if (block_size <= 0 || block_size % TILE != 0 || max_blocks <= 0 ||
+        (int64_t)max_blocks * block_size < max_len || rows < block_size)
+      return MLA_ERR_INVALID_ARG;
+  } else {
+    if (seq_capacity < max_len || seq_capacity < 1 || (int64_t)batch * seq_capacity > rows)
+      return MLA_ERR_INVALID_ARG;
+  }
+  const int B = batch, H = dims->heads, D = d_model;
+  const Plan pl = make_plan(B, H, max_len, MLA_BF16, opts);
+  const FusedWs fw = fused_ws(B, H, D, pl);
+  if (!workspace || workspace_bytes < fw.total || ((uintptr_t)workspace & 255) != 0)
+    return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  if (softmax_scale == 0.f) softmax_scale = 1.0f / std::sqrt((float)(D_N + D_R));
+  (void)hipGetLastError();
+  bf16* q = (bf16*)(ws + fw.dec.q_off);
+  float* qpart = (float*)(ws + fw.qpart);
+  bf16* olat = (bf16*)(ws + fw.olat);
+  float* opart = (float*)(ws + fw.opart);
+  // 1. q_lat = W_QK[h] x for every head: [B, D] x [512 H, D]^T
+  SkinnyParams sq{(const bf16*)x, (const bf16*)w_qk, qpart, D, D, B, H * D_C, D, fw.qp.S,
+                  fw.qp.cps};
+  launch_skinny(sq, fw.qp, stream);
+  MLA_TRY(launch_status());
+  const int64_t qpieces = (int64_t)B * H * 72;
+  hipLaunchKernelGGL(mla_fused_q_finish_kernel, dim3((unsigned)ceil_div(qpieces, 256)), dim3(256),
+                     0, stream, (const float*)qpart, fw.qp.S, (const bf16*)q_pe, q, B, H,
+                     softmax_scale * LOG2E);
+  MLA_TRY(launch_status());
+  // 2. attention over the latent cache
+  _Float16* part_h = (_Float16*)(ws + fw.dec.po_off);
+  float* part_scale = (float*)(ws + fw.dec.ps_off);
+  float* part_lse = (float*)(ws + fw.dec.pl_off);
+  const DecodeParams dp = decode_params(q, latent, ls, rope, rs, scales, rows, seq_capacity,
+                                        block_table, max_blocks, block_size, lengths, max_len, B,
+                                        H, pl, part_h, part_scale, part_lse);
+  MLA_TRY(launch_attention(dp, pl, cdt == MLA_FP8_E4M3, opts, stream));
+  // 3. merged latent rows, then y = o_lat [B, 512 H] x W_VO^T [D, 512 H]^T
+  hipLaunchKernelGGL(mla_merge_latent_kernel, dim3(B * H), dim3(128), 0, stream,
+                     (const _Float16*)part_h, (const float*)part_scale, (const float*)part_lse,
+                     olat, lse, B, H, pl.S);
+  MLA_TRY(launch_status());
+  SkinnyParams so{olat, (const bf16*)w_vo, opart, (int64_t)H * D_C, (int64_t)H * D_C, B, D,
+                  H * D_C, fw.op.S, fw.op.cps};
+  launch_skinny(so, fw.op, stream);
+  MLA_TRY(launch_status());
+  hipLaunchKernelGGL(mla_fused_out_finish_kernel, dim3((unsigned)ceil_div((int64_t)B * D, 1024)),
+                     dim3(256), 0, stream, (const float*)opart, fw.op.S, (bf16*)out, B, D);
   return launch_status();
 }
 

@@ -374,6 +374,60 @@ mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_p
                        const mla_prefill_options* opts, hipStream_t stream);
 
 /*
+ * mla_fuse_weights: the offline absorption of "How DeepSeek Rewrote the
+ * Transformer [MLA]", section "MLA: compress the pair, not the heads" (W_UK
+ * absorbed into the query matrix, W_UV into the output matrix W_O before
+ * serving). For every head h, with the query projection q_nope[h] = W_Q[h] x
+ * and the output y = sum_h o[h] W_O[h] of a model of width d_model:
+ *   w_qk[h]                  = W_UK[h]^T W_Q[h]        [H, 512, d_model]
+ *   w_vo[n][512 h + c]       = (W_UV[h] W_O[h])[c][n]  [d_model, 512 H]
+ * (each fused weight is stored with its contraction index contiguous, the
+ * layout mla_decode_fused streams). fp32 accumulation, one bf16 rounding.
+ *   w_q [H, 128, d_model], w_uk [H, 128, 512], w_uv [H, 512, 128],
+ *   w_o [H, 128, d_model]: bf16, row-major; act_dtype MLA_BF16.
+ * d_model: a positive multiple of 64. Errors as for mla_decode.
+ */
+mla_status mla_fuse_weights(const mla_dims* dims, int32_t d_model, const void* w_q,
+                            const void* w_uk, const void* w_uv, const void* w_o,
+                            mla_dtype act_dtype, void* w_qk, void* w_vo, hipStream_t stream);
+
+/* Workspace bytes needed by mla_decode_fused (0 on invalid sizes). */
+size_t mla_decode_fused_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_len,
+                                       int32_t d_model, const mla_decode_options* opts);
+
+/*
+ * mla_decode_fused: one decode step from each token's model-width input x to
+ * its model-width attention output, with the weights fused offline by
+ * mla_fuse_weights:
+ *   q_lat[b,h] = w_qk[h] x[b];  s_t = softmax_scale (q_lat . c_t + q_pe[b,h] . k^R_t)
+ *   y[b]       = sum_h (sum_t softmax(s)_t c_t) W_VO[h];  lse[b,h] = ln sum_t exp(s_t)
+ * which equals the unfused y = sum_h o[b,h] W_O[h] of mla_decode with
+ * q_nope[b,h] = W_Q[h] x[b], up to rounding (the identity the absorption
+ * rests on).
+ *   x [batch, d_model], q_pe [batch, H, 64] (already rotated): bf16
+ *   w_qk, w_vo: as written by mla_fuse_weights; act_dtype MLA_BF16
+ *   cache arguments, lengths, max_len, softmax_scale, lse, opts: as for
+ *   mla_decode (the cache bf16 or fp8); block_table NULL selects the
+ *   contiguous layout of mla_decode (seq_capacity), otherwise the paged
+ *   layout of mla_decode_paged
+ *   out [batch, d_model] bf16
+ *   workspace   at least mla_decode_fused_workspace_size(...) bytes,
+ *               256-byte aligned
+ * opts->append is not supported here (MLA_ERR_UNSUPPORTED): append with
+ * mla_cache_append first. Errors as for mla_decode.
+ */
+mla_status mla_decode_fused(const mla_dims* dims, const void* x, const void* q_pe,
+                            const void* w_qk, const void* w_vo, int32_t d_model,
+                            mla_dtype act_dtype, const void* latent, int64_t latent_stride,
+                            const void* rope, int64_t rope_stride, const void* scales,
+                            mla_dtype cache_dtype, int64_t cache_rows, int64_t seq_capacity,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, const int32_t* lengths, int32_t batch,
+                            int32_t max_len, float softmax_scale, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            const mla_decode_options* opts, hipStream_t stream);
+
+/*
  * mla_decode_paged_noalloc: mla_decode_paged without a workspace argument,
  * for callers that cannot allocate device memory or pass a buffer of their
  * own around: code captured into a HIP graph, serving loops that must not

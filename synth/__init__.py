@@ -215,6 +215,21 @@ def prefill_queries(seed: int, B: int, T: int, H: int, act: str = "bf16", device
 D_MODEL = 7168    # hidden width of the DeepSeek-V3 setting
 
 
+def model_io_inputs(seed: int, B: int, H: int, d_model: int = 7168, act: str = "bf16",
+                    device="cpu"):
+    """Model-width decode inputs: x [B, d_model] ~ N(0,1), query projection
+    W_Q [H, 128, d_model] ~ N(0, 1/d_model) and output projection
+    W_O [H, 128, d_model] ~ N(0, 1/(128 H)) (standard deviation
+    1/sqrt(fan_in): d_model inputs per query, 128 H per output).
+    Seeds: seed (x), seed + 1 (W_Q), seed + 2 (W_O)."""
+    x = to_storage(normal((B, d_model), seed, device), act)
+    w_q = to_storage(normal((H, D_NOPE, d_model), seed + 1, device,
+                            std=1.0 / math.sqrt(d_model)), act)
+    w_o = to_storage(normal((H, D_V, d_model), seed + 2, device,
+                            std=1.0 / math.sqrt(D_V * H)), act)
+    return x, w_q, w_o
+
+
 def projection_inputs(seed: int, B: int, act: str, d_model: int = D_MODEL, device="cpu"):
     """Hidden states h [B, d_model] ~ N(0,1) and the down-projection weights
     W_DKV [512, d_model], W_KR [64, d_model] ~ N(0, 1/d_model) (standard
