@@ -77,6 +77,7 @@ def parse():
     ap.add_argument("--project", action="store_true")
     ap.add_argument("--prefill", action="store_true")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--restart", action="store_true")
     ap.add_argument("--with-projection", action="store_true")
     return ap.parse_args()
 
@@ -111,6 +112,13 @@ class HipEvents:
 # the files whose text defines the split attention kernels (the launch code
 # in mla_api.hip only passes them their parameters), and the down-projection's
 KERNEL_SOURCES = ("common.hpp", "decode_mfma.hpp")
+# sources per attention kernel (the fp8 matrix-core kernel builds on the
+# decode kernels' header)
+SOURCES_OF = {"mla_decode_fp8mma_kernel": ("common.hpp", "decode_mfma.hpp", "decode_fp8mma.hpp")}
+
+
+def sources_of(kernel: str):
+    return SOURCES_OF.get(kernel, KERNEL_SOURCES)
 PROJECT_SOURCES = ("common.hpp", "append.hpp", "kv_project.hpp")
 PROJECT_KERNELS = ("mla_kv_project_kernel", "mla_project_append_kernel")
 PROJECT_WORKLOAD = "b64_d7168_bf16"
@@ -126,7 +134,7 @@ def kernel_source_hash(files=KERNEL_SOURCES) -> str:
 
 
 def measured_traffic(workload: str, per_launch_bytes: float, kernel="mla_decode_bf16_kernel",
-                     sources=KERNEL_SOURCES):
+                     sources=None):
     """HBM bytes per launch of the measured kernel(s) from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
@@ -134,7 +142,7 @@ def measured_traffic(workload: str, per_launch_bytes: float, kernel="mla_decode_
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash(sources):
+    if t.get("kernel_source_hash") != kernel_source_hash(sources or sources_of(kernel)):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -276,7 +284,7 @@ def _counter_mean(csv_path: str, kernel_substr: str, counter: str) -> float:
     return sum(vals) / len(vals)
 
 
-def write_traffic(paths, config: str, kernels, copy_mib: int = 1024, sources=KERNEL_SOURCES):
+def write_traffic(paths, config: str, kernels, copy_mib: int = 1024, sources=None):
     """HBM bytes per launch of `kernels` (summed: the launches of one call)
     from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
     the factor between the true bytes of a plain copy of copy_mib MiB and
@@ -289,7 +297,7 @@ def write_traffic(paths, config: str, kernels, copy_mib: int = 1024, sources=KER
     write = sum(_counter_mean(w, k, "WRITE_SIZE") for k in kernels) * 1024.0 * wf
     kernel = kernels[0]
     rec = {"kernel": " + ".join(kernels), "workload": config,
-           "kernel_source_hash": kernel_source_hash(sources),
+           "kernel_source_hash": kernel_source_hash(sources or sources_of(kernels[0])),
            "read_factor": rf, "write_factor": wf, "hbm_read_bytes_per_launch": fetch,
            "hbm_write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write}
     out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
@@ -583,6 +591,67 @@ def bench_fused(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_restart(args):
+    """Worst-case cost of the attention kernel's overflow restart: the B=64
+    N=4096 paged bf16 workload with, in every split of every sequence, one row
+    set along the part of one head's absorbed query that is orthogonal to the
+    other heads', scaled to outscore the split's first tile by far more than
+    64 in log2 units. Every workgroup then takes the second pass (scores of
+    the whole split for the true maximum, then the split again). Timed against
+    the unmodified cache in the same run (decode launches only, no append)."""
+    import numpy as np
+    import torch
+    import head_latent_attention_07_amd as mla
+    import synth
+
+    mla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = synth.make_inputs("3u")
+    hot = synth.make_inputs("3u")
+    B, H = base.B, base.H
+    wuk = base.w_uk.double()
+    S = 4
+    per = base.max_len // S
+    table = base.block_table
+    for b in range(B):
+        qlat = torch.einsum("hn,hnc->hc", base.q_nope[b].double(), wuk).numpy()
+        hh = b % H
+        others = np.delete(qlat, hh, axis=0)
+        coef = np.linalg.lstsq(others.T, qlat[hh], rcond=None)[0]
+        qperp = qlat[hh] - others.T @ coef
+        x = torch.zeros(576, dtype=torch.float32)
+        x[:512] = torch.from_numpy(100.0 / (qperp @ qperp * base.scale * np.log2(np.e)) * qperp)
+        for s in range(S):
+            t = s * per + per // 2
+            row = int(table[b, t // base.block_size]) * base.block_size + t % base.block_size
+            hot.cache[row] = x.to(torch.bfloat16)
+    ev = HipEvents()
+    out = {}
+    for name, inp in (("normal", base), ("restart_every_split", hot)):
+        d = inp.to(dev)
+        ws = torch.empty(mla.workspace_size(H, B, d.max_len, mla.MLA_BF16, mla.MLA_BF16,
+                                            num_splits=S), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            mla.decode_inputs(d, workspace=ws, num_splits=S)
+        pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            mla.decode_inputs(d, workspace=ws, num_splits=S, events=pairs[i])
+        torch.cuda.synchronize()
+        ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        out[name] = {"attn_us_mean": sum(ms) / len(ms) * 1e3,
+                     "attn_us_p10_p50_p90": [percentile(ms, q) * 1e3 for q in (10, 50, 90)]}
+        del d
+    line = {"metric": "attention kernel time with the overflow restart in every split",
+            "workload": "mla_decode_b64_h128_n4096_paged_bf16, 4 splits", "steps": args.steps,
+            "warmup": args.warmup, **out,
+            "slowdown": out["restart_every_split"]["attn_us_mean"] / out["normal"]["attn_us_mean"]}
+    print(json.dumps(line), flush=True)
+
+
 SIMD_COUNT = 1024            # MI355X: 256 CUs x 4 SIMDs
 
 WORKLOADS = {"1": "mla_decode_b1_h16_n512_f32", "2": "mla_decode_b1_h128_n4096_bf16",
@@ -593,9 +662,15 @@ WORKLOADS = {"1": "mla_decode_b1_h16_n512_f32", "2": "mla_decode_b1_h128_n4096_b
 FULL_STEP_WORKLOAD = "mla_decode_61layer_step_b32_h128_n32768_fp8cache"
 
 
+# the fp8 cache's attention kernel: the fp8 matrix-core kernel, unless
+# MLA_FP8_KERNEL=widen selects the widening one
+FP8_KERNEL = ("mla_decode_fp8_kernel" if os.environ.get("MLA_FP8_KERNEL") == "widen"
+              else "mla_decode_fp8mma_kernel")
+
+
 def decode_kernel_name(cache_dtype: str) -> str:
     return {"f32": "mla_decode_f32_kernel", "bf16": "mla_decode_bf16_kernel",
-            "fp8": "mla_decode_fp8_kernel"}[cache_dtype]
+            "fp8": FP8_KERNEL}[cache_dtype]
 
 
 def write_mfma(counters_csv: str, trace_csv: str, config: str, kernel: str):
@@ -624,19 +699,29 @@ def write_mfma(counters_csv: str, trace_csv: str, config: str, kernel: str):
     # dispatch is longer than the kernel, so cycles / duration over-states the
     # clock (an upper bound)
     grbm_max = busy / (util / 100.0 * SIMD_COUNT) if util > 0 else None
-    flops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
-    rec = {"kernel": kernel, "workload": config, "kernel_source_hash": kernel_source_hash(),
+    # every matrix-core data type the run counted (bf16 for the bf16 and
+    # widening kernels, f8 / f6f4 for the fp8 matrix-core kernel)
+    mops = {k: v for k, v in mean.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_")}
+    flops = sum(mops.values()) * 512
+    rec = {"kernel": kernel, "workload": config,
+           "kernel_source_hash": kernel_source_hash(sources_of(kernel)),
            "dispatches": len(rows) // max(1, len(by)), "counters_mean": mean,
            "median_duration_us": dur_ns / 1e3,
            "mfma_util_pct": util,
            "mfma_busy_cycles_per_simd": busy / SIMD_COUNT,
-           "mfma_bf16_flop_per_dispatch": flops,
-           "mfma_bf16_tflops": flops / dur_ns / 1e3,
-           "mfma_bf16_frac_of_peak": flops / dur_ns / 1e3 / MFMA_BF16_PEAK_TFLOPS,
+           "mfma_flop_per_dispatch": flops,
+           "mfma_flop_by_type": {k[len("SQ_INSTS_VALU_MFMA_MOPS_"):]: v * 512
+                                 for k, v in mops.items()},
+           "mfma_tflops": flops / dur_ns / 1e3,
+           # against the dense peak of the type executed (fp8 twice bf16's)
+           "mfma_frac_of_peak": sum(v * 512 / (MFMA_BF16_PEAK_TFLOPS * (2 if k.endswith(("F8", "F6F4"))
+                                                                         else 1))
+                                    for k, v in mops.items()) / dur_ns / 1e3,
            "gpu_active_cycles_max_instance": grbm_max,
            "clock_ghz_upper_bound": grbm_max / dur_ns if grbm_max else None,
            "mfma_busy_frac_at_2p4ghz": busy / SIMD_COUNT / (dur_ns * 2.4),
-           "peak_used": {"bf16_dense_tflops": MFMA_BF16_PEAK_TFLOPS, "simds": SIMD_COUNT,
+           "peak_used": {"bf16_dense_tflops": MFMA_BF16_PEAK_TFLOPS,
+                         "fp8_dense_tflops": 2 * MFMA_BF16_PEAK_TFLOPS, "simds": SIMD_COUNT,
                          "clock_ghz": 2.4}}
     out = os.path.join(ROOT, "profiles", f"{kernel}_{config}_mfma.json")
     with open(out, "w") as fh:
@@ -652,10 +737,11 @@ def measured_mfma(workload: str, kernel: str):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(sources_of(kernel)):
         return None
-    return {k: t[k] for k in ("mfma_util_pct", "mfma_bf16_tflops", "mfma_bf16_frac_of_peak",
-                              "mfma_bf16_flop_per_dispatch", "median_duration_us")}
+    keys = ("mfma_util_pct", "mfma_tflops", "mfma_frac_of_peak", "mfma_flop_per_dispatch",
+            "mfma_flop_by_type", "median_duration_us")
+    return {k: t[k] for k in keys if k in t}
 
 
 def percentile(vals, q):
@@ -668,6 +754,11 @@ def percentile(vals, q):
 
 def main():
     args = parse()
+    if args.restart:
+        args.steps = 200 if args.steps is None else args.steps
+        args.warmup = 50 if args.warmup is None else args.warmup
+        bench_restart(args)
+        return
     if args.fused:
         args.steps = 200 if args.steps is None else args.steps
         args.warmup = 40 if args.warmup is None else args.warmup
@@ -688,11 +779,11 @@ def main():
             write_traffic(args.write_traffic, PROJECT_WORKLOAD, PROJECT_KERNELS,
                           sources=PROJECT_SOURCES)
         else:
-            kern = "mla_decode_fp8_kernel" if args.config == "5" else "mla_decode_bf16_kernel"
+            kern = FP8_KERNEL if args.config == "5" else "mla_decode_bf16_kernel"
             write_traffic(args.write_traffic, args.config, (kern,))
         return
     if args.write_mfma:
-        kern = "mla_decode_fp8_kernel" if args.config == "5" else "mla_decode_bf16_kernel"
+        kern = FP8_KERNEL if args.config == "5" else "mla_decode_bf16_kernel"
         write_mfma(*args.write_mfma, args.config, kern)
         return
     if args.copy_calibration > 0:

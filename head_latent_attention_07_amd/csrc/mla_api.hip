@@ -10,6 +10,7 @@
 
 #include "mla.h"
 #include "append.hpp"
+#include "decode_fp8mma.hpp"
 #include "decode_mfma.hpp"
 #include "fp32_path.hpp"
 #include "fused_io.hpp"
@@ -98,6 +99,31 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   if (act == MLA_F32) ts = std::min(ts, F32_MAX_SPLIT);
   pl.TS = ts;
   pl.S = ceil_div(len, ts);
+  return pl;
+}
+
+// The fp8 cache goes to the fp8 matrix cores (decode_fp8mma.hpp) when its
+// layout fits that kernel: four waves of 32 heads per workgroup, splits of
+// whole 64-token tiles (at most 32 of them), and page blocks holding whole
+// tiles; MLA_FP8_KERNEL=widen selects the widening kernel instead.
+bool use_fp8mma(mla_dtype cdt, const Plan& pl, const int32_t* block_table, int block_size) {
+  if (cdt != MLA_FP8_E4M3 || pl.NW != 4) return false;
+  if (block_table && block_size % F8_TILE != 0) return false;
+  const char* e = std::getenv("MLA_FP8_KERNEL");
+  return !(e && std::strcmp(e, "widen") == 0);
+}
+
+// Plan of a decode call: make_plan, with the splits rounded to whole 64-token
+// tiles for the fp8 matrix-core kernel (never more splits than make_plan's,
+// so the workspace make_plan sizes is enough).
+Plan decode_plan(int B, int H, int max_len, mla_dtype act, mla_dtype cdt,
+                 const int32_t* block_table, int block_size, const mla_decode_options* opts) {
+  Plan pl = make_plan(B, H, max_len, act, opts);
+  if (act != MLA_F32 && use_fp8mma(cdt, pl, block_table, block_size)) {
+    const int len = max_len > 0 ? max_len : 1;
+    pl.TS = std::min(ceil_div(pl.TS, F8_TILE) * F8_TILE, F8_MAX_TILES * F8_TILE);
+    pl.S = ceil_div(len, pl.TS);
+  }
   return pl;
 }
 
@@ -338,6 +364,7 @@ DecodeParams decode_params(const bf16* q, const void* latent, int64_t ls, const 
 // timestamps, not those of separate event packets).
 mla_status launch_attention(const DecodeParams& dp, const Plan& pl, bool fp8,
                             const mla_decode_options* opts, hipStream_t stream) {
+  const bool mma = fp8 && use_fp8mma(MLA_FP8_E4M3, pl, dp.block_table, dp.block_size);
   const int nq = dp.B * pl.S;
   const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
   hipEvent_t ev0 = opts ? opts->attn_begin : nullptr, ev1 = opts ? opts->attn_end : nullptr;
@@ -347,6 +374,10 @@ mla_status launch_attention(const DecodeParams& dp, const Plan& pl, bool fp8,
     else
       hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, dp);
   };
+  if (mma) {
+    launch(mla_decode_fp8mma_kernel, 256);
+    return launch_status();
+  }
   switch (pl.NW * 2 + (fp8 ? 1 : 0)) {
     case 8: launch(mla_decode_bf16_kernel<4>, 256); break;
     case 9: launch(mla_decode_fp8_kernel<4>, 256); break;
@@ -438,7 +469,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
       app.part_slices = project_plan(batch, a->d_model).S;
     }
   }
-  const Plan pl = make_plan(B, H, max_len, act, opts);
+  const Plan pl = decode_plan(B, H, max_len, act, cdt, block_table, block_size, opts);
   const WsLayout wl = ws_layout(B, H, pl, act);
   if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
     return MLA_ERR_WORKSPACE;
@@ -780,7 +811,7 @@ mla_status mla_decode_fused(const mla_dims* dims, const void* x, const void* q_p
       return MLA_ERR_INVALID_ARG;
   }
   const int B = batch, H = dims->heads, D = d_model;
-  const Plan pl = make_plan(B, H, max_len, MLA_BF16, opts);
+  const Plan pl = decode_plan(B, H, max_len, MLA_BF16, cdt, block_table, block_size, opts);
   const FusedWs fw = fused_ws(B, H, D, pl);
   if (!workspace || workspace_bytes < fw.total || ((uintptr_t)workspace & 255) != 0)
     return MLA_ERR_WORKSPACE;
