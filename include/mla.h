@@ -239,7 +239,12 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t ma
 /*
  * mla_decode: one decode step of MLA attention for `batch` sequences over a
  * contiguous cache (sequence b owns rows [b*seq_capacity, b*seq_capacity +
- * lengths[b])).
+ * lengths[b])). (Sources: "How DeepSeek Rewrote the Transformer [MLA]",
+ * section "MLA: compress the pair, not the heads": the query absorbs W_UK,
+ * every head scores against and mixes the shared latent rows, W_UV is
+ * applied after attention; section "Classic attention and the cost of the
+ * KV cache": softmax attention of the new token over the cached rows, the
+ * causal mask being the length mask for a single query.)
  *
  * For every sequence b and head h, with N = lengths[b] (the causal length,
  * counting the current token once it has been appended):
@@ -255,7 +260,10 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t ma
  *   q_nope [batch, H, 128], q_pe [batch, H, 64] (already rotated): act_dtype
  *   w_uk   [H, 128, 512], w_uv [H, 512, 128]: act_dtype, row-major
  *   act_dtype   MLA_F32 (requires an MLA_F32 cache) or MLA_BF16 (bf16 or fp8
- *               cache); bf16 math uses bf16 MFMA operands, fp32 accumulation
+ *               cache); bf16 math uses bf16 MFMA operands, fp32 accumulation;
+ *               an fp8 cache goes to the fp8 matrix cores as stored, with the
+ *               query and the softmax weights split into two e4m3 parts (hi
+ *               and lo, power-of-two scales per 32-wide block)
  *   latent, rope, strides, scales (fp8 only), cache_dtype: the cache
  *   cache_rows  total rows of the cache arrays, at most 2^31 - 1
  *               (MLA_ERR_UNSUPPORTED otherwise)
@@ -282,11 +290,14 @@ mla_status mla_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
                       const mla_decode_options* opts, hipStream_t stream);
 
 /*
- * mla_decode_paged: as mla_decode, over a paged cache. Token t of sequence b
- * lives in row block_table[b * max_blocks_per_seq + t / block_size] *
- * block_size + t % block_size. block_size must be a positive multiple of 32
- * (the kernel's token tile). Block-table indexing is exact: the result equals
- * mla_decode on the same rows laid out contiguously.
+ * mla_decode_paged: as mla_decode (same sources), over a paged cache. Token t
+ * of sequence b lives in row block_table[b * max_blocks_per_seq +
+ * t / block_size] * block_size + t % block_size. block_size must be a
+ * positive multiple of 32 (the kernel's token tile; fp8 caches with blocks
+ * that are not multiples of 64 take the widening kernel). Block-table
+ * indexing is exact: the result equals mla_decode on the same rows laid out
+ * contiguously. (The pages give no paging scheme; the paged layout is the
+ * one of the batched ragged workload this library is measured on.)
  */
 mla_status mla_decode_paged(const mla_dims* dims, const void* q_nope, const void* q_pe,
                             const void* w_uk, const void* w_uv, mla_dtype act_dtype,
