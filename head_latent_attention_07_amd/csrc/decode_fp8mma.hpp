@@ -310,36 +310,38 @@ void mla_decode_fp8mma_kernel(DecodeParams p) {
   // scores of one tile (both halves), scaled by the rows' scales, masked
   // past the split's end
   const uint32_t unit = F8_UNIT_SCALE;
-  auto tile_scores = [&](const char* buf, int k, f32x16 (&s)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      s[u] = f32x16{};
-      static_for<F8_KS>([&](auto kc) {
-        constexpr int ks = decltype(kc)::value;
-        const i32x8 a = k_operand(buf, u, ks);
-        const i32x8 bl = qlo_operand(ks);
-        f8_mfma_vgpr<ks & 3>(s[u], a, qhi[ks], unit, sc_hi[ks >> 2]);
-        f8_mfma_vgpr<ks & 3>(s[u], a, bl, unit, sc_lo[ks >> 2]);
-      });
-      f8_settle(s[u]);
-    }
+  // scores of half u of tile k: the rows' scales applied, masked past the
+  // split's end (register r is token 32 u + 16 g + r)
+  auto scale_mask = [&](int k, int u, f32x16& s) {
     const float* sc = scl_all + F8_TILE * k;
     const int tk0 = wi.t0 + F8_TILE * k;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // register r is token 32 u + 16 g + r
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 s4 = *(const f32x4*)(sc + 32 * u + 16 * g + 4 * q4);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 s4 = *(const f32x4*)(sc + 32 * u + 16 * g + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[u][4 * q4 + e] *= s4[e];
-      }
-      if (tk0 + F8_TILE > wi.t1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (tk0 + 32 * u + 16 * g + r >= wi.t1) s[u][r] = -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) s[4 * q4 + e] *= s4[e];
     }
+    if (tk0 + F8_TILE > wi.t1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (tk0 + 32 * u + 16 * g + r >= wi.t1) s[r] = -INFINITY;
+    }
+  };
+  auto half_scores = [&](const char* buf, int k, int u, f32x16& s) {
+    s = f32x16{};
+    static_for<F8_KS>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      const i32x8 a = k_operand(buf, u, ks);
+      const i32x8 bl = qlo_operand(ks);
+      f8_mfma_vgpr<ks & 3>(s, a, qhi[ks], unit, sc_hi[ks >> 2]);
+      f8_mfma_vgpr<ks & 3>(s, a, bl, unit, sc_lo[ks >> 2]);
+    });
+    f8_settle(s);
+    scale_mask(k, u, s);
+  };
+  auto tile_scores = [&](const char* buf, int k, f32x16 (&s)[2]) {
+    half_scores(buf, k, 0, s[0]);
+    half_scores(buf, k, 1, s[1]);
   };
 
   for (int attempt = 0; attempt < 2; ++attempt) {
@@ -354,48 +356,77 @@ void mla_decode_fp8mma_kernel(DecodeParams p) {
       if (j + 1 < ntiles)
         issue(bufs + ((j + 1) & 1) * F8_TILE_BYTES,
               __builtin_amdgcn_readlane(trow, min(j + 1, ntiles - 1)), nvalid(j + 1));
-      f32x16 s[2];
-      tile_scores(buf, j, s);
-      if (st.m_ref == -INFINITY) {   // the split's first tile fixes the exponent reference
+      // S^T of the tile's first half; then the second half's chain, under
+      // whose MFMAs the first half's weights are formed and split (slices
+      // pinned between the MFMAs); then the second half's weights.
+      const float* sc = scl_all + F8_TILE * j;
+      f32x16 s0, s1;
+      half_scores(buf, j, 0, s0);
+      if (st.m_ref == -INFINITY) {   // the split's first half-tile fixes the reference
         float m = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) m = fmaxf(m, s[u][r]);
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, s0[r]);
         st.m_ref = pair_max(m);
       }
-      // weights times the rows' scales (the scale of a V row), split into
-      // hi / lo with a power-of-two scale per 32-token block; block u is
-      // this lane's half u and its partner's
-      const float* sc = scl_all + F8_TILE * j;
-      float pw[2][16];
-      float am[2] = {0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 s4 = *(const f32x4*)(sc + 32 * u + 16 * g + 4 * q4);
+      i32x8 phi, plo;
+      float pw0[16];
+      float am0 = 0.f;
+      int f0 = 0;
+      s1 = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<F8_KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        const i32x8 a = k_operand(buf, 1, ks);
+        const i32x8 bl = qlo_operand(ks);
+        f8_mfma_vgpr<ks & 3>(s1, a, qhi[ks], unit, sc_hi[ks >> 2]);
+        f8_mfma_vgpr<ks & 3>(s1, a, bl, unit, sc_lo[ks >> 2]);
+        if constexpr (ks < 4) {   // weights of tokens 16 g + 4 ks .. +3
+          const f32x4 s4 = *(const f32x4*)(sc + 16 * g + 4 * ks);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pr = fast_exp2(s[u][4 * q4 + e] - st.m_ref);
+            const float pr = fast_exp2(s0[4 * ks + e] - st.m_ref);
             st.lsum += pr;
-            pw[u][4 * q4 + e] = pr * s4[e];
-            am[u] = fmaxf(am[u], pw[u][4 * q4 + e]);
+            pw0[4 * ks + e] = pr * s4[e];
+            am0 = fmaxf(am0, pw0[4 * ks + e]);
           }
+        } else if constexpr (ks == 4) {
+          f0 = f8_exp(pair_max(am0));
+        } else {                  // hi / lo of word ks - 5
+          constexpr int k = ks - 5;
+          const float m = ldexpf(1.0f, f0);
+          uint32_t hi = 0, lo = 0;
+          f8_split2<false>(pw0[4 * k] * m, pw0[4 * k + 1] * m, hi, lo);
+          f8_split2<true>(pw0[4 * k + 2] * m, pw0[4 * k + 3] * m, hi, lo);
+          phi[k] = (int)hi;
+          plo[k] = (int)lo;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      f8_settle(s1);
+      scale_mask(j, 1, s1);
+      float pw1[16];
+      float am1 = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 s4 = *(const f32x4*)(sc + 32 + 16 * g + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = fast_exp2(s1[4 * q4 + e] - st.m_ref);
+          st.lsum += pr;
+          pw1[4 * q4 + e] = pr * s4[e];
+          am1 = fmaxf(am1, pw1[4 * q4 + e]);
         }
       }
-      const int f0 = f8_exp(pair_max(am[0])), f1 = f8_exp(pair_max(am[1]));
-      i32x8 phi, plo;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float m = ldexpf(1.0f, u ? f1 : f0);
+      const int f1 = f8_exp(pair_max(am1));
+      {
+        const float m = ldexpf(1.0f, f1);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           uint32_t hi = 0, lo = 0;
-          f8_split2<false>(pw[u][4 * k] * m, pw[u][4 * k + 1] * m, hi, lo);
-          f8_split2<true>(pw[u][4 * k + 2] * m, pw[u][4 * k + 3] * m, hi, lo);
-          phi[4 * u + k] = (int)hi;
-          plo[4 * u + k] = (int)lo;
+          f8_split2<false>(pw1[4 * k] * m, pw1[4 * k + 1] * m, hi, lo);
+          f8_split2<true>(pw1[4 * k + 2] * m, pw1[4 * k + 3] * m, hi, lo);
+          phi[4 + k] = (int)hi;
+          plo[4 + k] = (int)lo;
         }
       }
       const int fe = g ? f1 : f0;

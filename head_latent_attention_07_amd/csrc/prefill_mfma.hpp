@@ -302,7 +302,9 @@ void mla_prefill_attn_kernel(PrefillParams p) {
   const int wkmax = min(len, max(p0 + qw0 + 32, 0));
   const int ntiles = (kmax + PF_KEYS - 1) / PF_KEYS;
 
-  // queries of this lane, in fp16 (clamped past the chunk: never stored)
+  // queries of this lane, in fp16 and pre-multiplied by softmax_scale
+  // log2(e), so the scores come out of the products in log2 units (clamped
+  // past the chunk: never stored)
   f16x8 qop[12];
   {
     const int qc = min(q, p.T - 1);
@@ -315,7 +317,7 @@ void mla_prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
     for (int s = 0; s < 12; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qop[s][e] = f16_sat((float)x[s][e]);
+      for (int e = 0; e < 8; ++e) qop[s][e] = f16_sat((float)x[s][e] * p.c);
   }
 
   // per-lane offsets of this wave's direct-to-LDS pieces of a tile (relative
@@ -400,20 +402,27 @@ void mla_prefill_attn_kernel(PrefillParams p) {
       }
     }
     if (act[0]) {
-      // scores in log2 units, masked past the query's position; register r
-      // of block kb is key kt0 + 32 kb + 8 (r / 4) + 4 h + r % 4
+      // scores (log2 units); register r of block kb is key
+      // kt0 + 32 kb + 8 (r / 4) + 4 h + r % 4. Only tiles that reach past the
+      // wave's first query position are masked (wave-uniform test).
+      if (!act[1]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[1][r] = -INFINITY;
+      }
+      if (kt0 + PF_KEYS - 1 > p0 + qw0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            sacc[kb][r] = (key > pos) ? -INFINITY : sacc[kb][r];
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          float s = act[kb] ? sacc[kb][r] * p.c : -INFINITY;
-          s = (key > pos) ? -INFINITY : s;
-          sacc[kb][r] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      }
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
       tmax = pair_max(tmax);
       const float m_new = fmaxf(m_run, tmax);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -430,10 +439,13 @@ void mla_prefill_attn_kernel(PrefillParams p) {
           pb[kb][r >> 3][r & 7] = (_Float16)e;
         }
       l_run = l_run * alpha + psum;
+      // the accumulator is rescaled only when some lane's maximum moved
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (act[kb]) {
