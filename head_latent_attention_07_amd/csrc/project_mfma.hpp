@@ -64,8 +64,13 @@ constexpr int AB_OPITCH = 32 * 2 + 16;     // 80 B: output staging row (32 bf16 
 
 __device__ __forceinline__ void absorb_workgroup(const AbsorbParams& p, int x) {
   __shared__ __attribute__((aligned(1024))) char w_lds[D_N * AB_ROW];   // 32 KB
-  __shared__ __attribute__((aligned(16))) char a_lds[2][32 * AB_APITCH];  // two chunks of 32 seq
-  __shared__ __attribute__((aligned(16))) char o_lds[4][32 * AB_OPITCH];  // per wave: 32 seq x 32 cols
+  // two chunks of 32 sequences; after a pass's products every wave stages
+  // its outputs (32 sequences x 32 columns) in its own 2.5 KB of this space,
+  // so the workgroup takes 49 KB of LDS and three fit on a CU (with the
+  // cache-append workgroups of the same launch, 4 H + B / 4 workgroups at
+  // H = 128 all run at once)
+  __shared__ __attribute__((aligned(16))) char a_lds[2][32 * AB_APITCH];
+  static_assert(4 * 32 * AB_OPITCH <= 2 * 32 * AB_APITCH, "output staging fits");
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
@@ -133,24 +138,32 @@ __device__ __forceinline__ void absorb_workgroup(const AbsorbParams& p, int x) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // W_UK slice landed (first pass)
     __syncthreads();
-    for (int cb = 0; cb < 2 && b0 + 32 * cb < p.B; ++cb) {
-      const int bc0 = b0 + 32 * cb;
-      f32x16 acc = f32x16{};
+    f32x16 acc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      acc[cb] = f32x16{};
+      if (b0 + 32 * cb >= p.B) continue;   // (uniform)
 #pragma unroll
       for (int ks = 0; ks < D_N / 16; ++ks) {
         const bf16x8 a = *(const bf16x8*)(a_lds[cb] + l32 * AB_APITCH + 2 * (16 * ks + 8 * h));
         const int ra = 16 * ks + r1, rb = ra + 4;
         const bf16x8 bop = tr_read_8(w_lds + ra * AB_ROW + 16 * (chunk ^ wrow_swizzle(ra)) + off,
                                      w_lds + rb * AB_ROW + 16 * (chunk ^ wrow_swizzle(rb)) + off);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc, 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[cb], 0, 0, 0);
       }
-      // lane holds column 32w + l32 of the slice, rows b = 8(r/4) + 4h + r%4:
-      // transpose through LDS so each lane stores 8 consecutive columns of
-      // one sequence (one 16-byte piece of the query layout)
-      char* ol = o_lds[w];
+    }
+    __syncthreads();   // every wave is done reading a_lds
+    // lane holds column 32w + l32 of the slice, rows b = 8(r/4) + 4h + r%4:
+    // transpose through LDS so each lane stores 8 consecutive columns of one
+    // sequence (one 16-byte piece of the query layout)
+    char* const ol = &a_lds[0][0] + w * (32 * AB_OPITCH);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int bc0 = b0 + 32 * cb;
+      if (bc0 >= p.B) break;   // (uniform)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        *(bf16*)(ol + (8 * (r >> 2) + 4 * h + (r & 3)) * AB_OPITCH + 2 * l32) = (bf16)(acc[r] * p.c);
+        *(bf16*)(ol + (8 * (r >> 2) + 4 * h + (r & 3)) * AB_OPITCH + 2 * l32) = (bf16)(acc[cb][r] * p.c);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int id = l + 64 * i, r = id >> 2, c8 = id & 3;
@@ -170,9 +183,9 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
 // absorb and cache append in one launch (the absorb neither reads nor
 // writes the cache, so the two are independent). The append workgroups come
 // first (one sequence per wave, their count rounded up to a multiple of 8 so
-// the absorb workgroups keep their XCD placement): dispatched first, they
-// run beside the absorb from the start; placed after it, they would wait for
-// absorb workgroups to retire (two fit per CU) and end the launch late.
+// the absorb workgroups keep their XCD placement) and run beside the absorb
+// from the start: at 128 heads the launch's 512 + B/4 workgroups are all
+// resident at once (three fit per CU).
 __host__ __device__ constexpr int append_blocks(int B) { return ((B + 3) / 4 + 7) / 8 * 8; }
 
 __global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, AppendParams a) {
