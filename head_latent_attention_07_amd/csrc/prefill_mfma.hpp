@@ -21,11 +21,14 @@
 //   * mla_prefill_expand_kernel: for a tile of 128 tokens and one head,
 //     [K_h | V_h]^T = [W_UK[h] ; W_UV[h]^T] C^T on bf16 MFMA (A = weight
 //     rows, B = latent rows, both read 16 bytes at a time from swizzled LDS
-//     stages), stored as fp16 [B, H, cap, 128]; the head-0 workgroups also
+//     stages); K_h is stored as fp16 [B, H, cap, 128], V_h transposed, as
+//     fp16 [B, H, 128, cap] with the tokens of every 16 in the order the PV
+//     product consumes them (vt_pos), so that the attention kernel reads its
+//     PV operand with plain 16-byte LDS reads; the head-0 workgroups also
 //     copy the tokens' RoPE keys to a contiguous fp16 [B, cap, 64] array;
 //   * mla_prefill_attn_kernel: causal flash attention for 128 queries of one
 //     (sequence, head) (4 waves x 32 queries). Key tiles of 64 keys (K | k^R
-//     | V, 40 KB) stream through two LDS stages with direct-to-LDS loads;
+//     | V^T, 40 KB) stream through two LDS stages with direct-to-LDS loads;
 //     S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_f16 with the
 //     same token-slot permutation as the decode kernel (the S^T accumulator
 //     is the PV B operand as is), online softmax in base 2 with one rescale
@@ -83,10 +86,18 @@ struct ExpandParams {
   const bf16* w_uk;    // [H, 128, 512]
   const bf16* w_uvt;   // [H, 128, 512]
   _Float16* kx;        // [B, H, cap, 128]
-  _Float16* vx;        // [B, H, cap, 128]
+  _Float16* vx;        // [B, H, 128, cap], tokens in vt_pos order
   _Float16* kpx;       // [B, cap, 64]
   int B, H, cap, max_len;
 };
+
+// Position of token k of an aligned group of 16 in the transposed values:
+// the PV B operand (the S^T accumulator as is) gives lane half h of k-step
+// ks the tokens 4h .. 4h+3 and 8+4h .. 8+4h+3 of its 16, in that order, so
+// they are stored at 8h .. 8h+7: order 0-3, 8-11, 4-7, 12-15.
+__host__ __device__ constexpr int vt_pos(int k) {
+  return 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+}
 
 __device__ __forceinline__ _Float16 f16_sat(float x) {
   return (_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f);
@@ -116,7 +127,8 @@ __device__ __forceinline__ int64_t prefill_row(const int32_t* __restrict__ table
   return (r >= 0 && r < rows) ? r : 0;
 }
 
-__global__ __launch_bounds__(256) void mla_prefill_expand_kernel(ExpandParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mla_prefill_expand_kernel(ExpandParams p) {
   __shared__ __attribute__((aligned(16))) char lds[2 * EX_STAGE];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,19 +226,47 @@ __global__ __launch_bounds__(256) void mla_prefill_expand_kernel(ExpandParams p)
 
   // acc[a][u]: lane holds token t = t0 + 64 wr + 32 u + l32 and output rows
   // 32 a + 8 g + 4 kg + (0..3) in registers 4 g .. 4 g + 3
-  _Float16* dst = (wc == 0 ? p.kx : p.vx) + ((int64_t)b * p.H + head) * p.cap * D_N;
+  if (wc == 0) {
+    _Float16* dst = p.kx + ((int64_t)b * p.H + head) * p.cap * D_N;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = t0 + 64 * wr + 32 * u + l32;
-    if (t < len) {
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + 64 * wr + 32 * u + l32;
+      if (t < len) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f16x4 v = {f16_sat(acc[a][u][4 * g]), f16_sat(acc[a][u][4 * g + 1]),
+                             f16_sat(acc[a][u][4 * g + 2]), f16_sat(acc[a][u][4 * g + 3])};
+            *(f16x4*)(dst + (int64_t)t * D_N + 32 * a + 8 * g + 4 * kg) = v;
+          }
+      }
+    }
+  } else {
+    // V^T of this wave's 64 tokens: through its own 16 KB of the (now idle)
+    // stages as [128 rows][64 tokens in vt_pos order], then out as 16-byte
+    // runs of 8 tokens. Every token of the tile is stored (those past the
+    // sequence's end from its last row: finite, and weighted 0 by the
+    // attention's mask).
+    char* const tb = lds + wr * (D_V * 128);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tl = 32 * u + l32;
+      const int pos = (tl & ~15) + vt_pos(tl & 15);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f16x4 v = {f16_sat(acc[a][u][4 * g]), f16_sat(acc[a][u][4 * g + 1]),
-                           f16_sat(acc[a][u][4 * g + 2]), f16_sat(acc[a][u][4 * g + 3])};
-          *(f16x4*)(dst + (int64_t)t * D_N + 32 * a + 8 * g + 4 * kg) = v;
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+          *(_Float16*)(tb + row * 128 + 2 * pos) = f16_sat(acc[a][u][r]);
         }
+    }
+    _Float16* dst = p.vx + ((int64_t)b * p.H + head) * D_V * p.cap + t0 + 64 * wr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = 64 * i + l, row = id >> 3, c = id & 7;
+      const u32x4 v = *(const u32x4*)(tb + row * 128 + 16 * c);
+      *(u32x4*)(dst + (int64_t)row * p.cap + 8 * c) = v;
     }
   }
   // the RoPE keys of the tile, once (head 0), to a contiguous array
@@ -268,20 +308,19 @@ constexpr int PF_Q = 128;                        // queries per workgroup (4 wav
 constexpr int PF_KEYS = 64;                      // keys per LDS tile
 constexpr int PF_KN = 0;                         // K rows: 64 x 256 B
 constexpr int PF_KP = PF_KEYS * 256;             // RoPE keys: 64 x 128 B
-constexpr int PF_V = PF_KP + PF_KEYS * 128;      // V rows: 64 x 256 B
+constexpr int PF_V = PF_KP + PF_KEYS * 128;      // V^T rows: 128 x 128 B
 constexpr int PF_STAGE = PF_V + PF_KEYS * 256;   // 40 KB
 
 // Swizzles (16-byte chunk XOR per row):
 //   K rows (256 B), read 16 bytes per lane from 16 consecutive keys:  c ^ (key & 15)
 //   RoPE keys (128 B), same reads:                                    c ^ ((key >> 1) & 7)
-//   V rows (256 B), read transposed, 4 keys x 64 B per half-wave:     c ^ (4 (key & 3))
+//   V^T rows (128 B = 64 keys of one value dim), same reads:          c ^ ((dim >> 1) & 7)
 __device__ __forceinline__ int pf_kswz(int k) { return k & 15; }
-__device__ __forceinline__ int pf_vswz(int k) { return 4 * (k & 3); }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * PF_STAGE];
-  const int tid = threadIdx.x, l = tid & 63, h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5, l32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqt = (p.T + PF_Q - 1) / PF_Q;
   // XCD-major order: XCD x takes the (sequence, head) pairs = x mod 8, each
@@ -322,13 +361,14 @@ void mla_prefill_attn_kernel(PrefillParams p) {
 
   // per-lane offsets of this wave's direct-to-LDS pieces of a tile (relative
   // to the tile's first key): 4 K pieces (4 keys x 256 B), 2 RoPE-key pieces
-  // (8 keys x 128 B), 4 V pieces
+  // (8 keys x 128 B), 4 V^T pieces (8 value dims x 64 keys x 2 B)
   int vo_k[4], vo_p[2], vo_v[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int key = 4 * (4 * w + m) + (l >> 4);
     vo_k[m] = key * 256 + 16 * ((l & 15) ^ pf_kswz(key));
-    vo_v[m] = key * 256 + 16 * ((l & 15) ^ pf_vswz(key));
+    const int dim = 8 * (4 * w + m) + (l >> 3);
+    vo_v[m] = dim * (p.cap * 2) + 16 * ((l & 7) ^ rope_swz(dim));
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -336,14 +376,17 @@ void mla_prefill_attn_kernel(PrefillParams p) {
     vo_p[m] = key * 128 + 16 * ((l & 7) ^ rope_swz(key));
   }
   const _Float16* kbase = p.kx + ((int64_t)b * p.H + head) * p.cap * D_N;
-  const _Float16* vbase = p.vx + ((int64_t)b * p.H + head) * p.cap * D_N;
+  const _Float16* vbase = p.vx + ((int64_t)b * p.H + head) * D_V * p.cap;
   const _Float16* pbase = p.kpx + (int64_t)b * p.cap * D_R;
   auto issue = [&](int j) {
     char* st = lds + (j & 1) * PF_STAGE;
     const int key0 = j * PF_KEYS;
     const int nv = __builtin_amdgcn_readfirstlane(max(min(len - key0, PF_KEYS), 0));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)key0 * D_N, (int64_t)nv * 256);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)key0 * D_N, (int64_t)nv * 256);
+    // (V^T: the 64-key segments of 128 rows; keys past the end are finite
+    // values the mask weights 0)
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(vbase + key0, (int64_t)(D_V - 1) * p.cap * 2 + PF_KEYS * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(pbase + (int64_t)key0 * D_R, (int64_t)nv * 128);
     const uint32_t mk = __builtin_amdgcn_readfirstlane(lds_u32(st + PF_KN) + 4 * w * 1024);
     const uint32_t mp = __builtin_amdgcn_readfirstlane(lds_u32(st + PF_KP) + 2 * w * 1024);
@@ -371,10 +414,9 @@ void mla_prefill_attn_kernel(PrefillParams p) {
   compiler_fence();
 
   // LDS read offsets of this lane (relative to a stage): S^T A operand (key
-  // row l32 of a 32-key block, chunk 2 s + h), PV A operand (transposed
-  // reads of keys 16 ks + 4 h + (jj >> 2) and 8 further)
-  const int trow = 4 * h + (jj >> 2);
-  const int tchunk = 2 * (g16 & 1) + ((jj & 3) >> 1);
+  // row l32 of a 32-key block, chunk 2 s + h), PV A operand (V^T row
+  // 32 dt + l32, chunk 2 ks + h: the lane half's 8 keys of k-step ks)
+  const int vsw = rope_swz(l32);
   for (int j = 0; j < ntiles; ++j) {
     const char* st = lds + (j & 1) * PF_STAGE;
     if (j + 1 < ntiles) issue(j + 1);
@@ -424,23 +466,35 @@ void mla_prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
       tmax = pair_max(tmax);
-      const float m_new = fmaxf(m_run, tmax);
+      // The exponent reference m_run moves only when a tile's maximum exceeds
+      // it by more than LAZY (log2 units): the weights stay below 2^LAZY
+      // (exact enough in fp16, far from its range), and the accumulator is
+      // rescaled only in the rare tiles where some lane's reference moved.
+      constexpr float LAZY = 8.0f;
+      const bool up = tmax > m_run + LAZY;
+      const float m_new = up ? tmax : m_run;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      const float alpha = up ? fast_exp2(m_run - m_use) : 1.0f;
       m_run = m_new;
-      float psum = 0.f;
       f16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(sacc[kb][r] - m_use);
-          psum += e;
-          pb[kb][r >> 3][r & 7] = (_Float16)e;
-        }
+        for (int r = 0; r < 16; ++r) pb[kb][r >> 3][r & 7] = (_Float16)fast_exp2(sacc[kb][r] - m_use);
+      // the denominator sums the fp16 weights the PV product uses, two per
+      // v_dot2_f32_f16
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            psum = __builtin_amdgcn_fdot2(f16x2{pb[kb][hf][e], pb[kb][hf][e + 1]}, one2, psum, false);
       l_run = l_run * alpha + psum;
-      // the accumulator is rescaled only when some lane's maximum moved
-      if (__any(alpha != 1.0f)) {
+      if (__any(up)) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -452,13 +506,10 @@ void mla_prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             const int ks = 2 * kb + hf;
-            const int rlo = 16 * ks + trow, rhi = rlo + 8;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-              const int cidx = (4 * dt + tchunk) ^ pf_vswz(rlo);   // rhi has the same swizzle
-              const f16x8 v = __builtin_bit_cast(
-                  f16x8, lds_tr8(st + PF_V + rlo * 256 + 16 * cidx + 8 * (jj & 1),
-                                 st + PF_V + rhi * 256 + 16 * cidx + 8 * (jj & 1)));
+              const f16x8 v = *(const f16x8*)(st + PF_V + (32 * dt + l32) * 128 +
+                                              16 * ((2 * ks + h) ^ vsw));
               o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v, pb[kb][hf], o[dt], 0, 0, 0);
             }
           }
