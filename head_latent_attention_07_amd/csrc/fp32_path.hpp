@@ -73,16 +73,41 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(DecodeF32Params p) 
   for (int t = tid; t < n; t += 256)
     rowof[t] = cache_row(b, t0 + t, p.seq_capacity, p.block_table, p.max_blocks, p.block_size, p.rows);
   __syncthreads();
-  // scores: one token per thread
+  // scores: wave wv takes tokens 4 wv .. 4 wv + 3, then 16 further, ...; its
+  // 64 lanes read a row
+  // together (lane l: latent dims l + 64 k, RoPE dim l: 9 coalesced 256-byte
+  // reads per row) against their 9 query values in registers, and the dot
+  // product is summed across the wave
+  float qv[9];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qv[k] = qs[lane + 64 * k];
+  qv[8] = qs[D_C + lane];
+  // (four tokens at a time, so that their reductions overlap; a token past
+  // the split's end repeats the last one and is not stored)
   float mloc = -INFINITY;
-  for (int t = tid; t < n; t += 256) {
-    const float* c = p.latent + rowof[t] * p.latent_stride;
-    const float* r = p.rope + rowof[t] * p.rope_stride;
-    float a = 0.f;
-    for (int d = 0; d < D_C; ++d) a = fmaf(qs[d], c[d], a);
-    for (int d = 0; d < D_R; ++d) a = fmaf(qs[D_C + d], r[d], a);
-    sc[t] = a;
-    mloc = fmaxf(mloc, a);
+  for (int t = 4 * wv; t < n; t += 16) {
+    float a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = rowof[min(t + u, n - 1)];
+      const float* c = p.latent + row * p.latent_stride;
+      const float* r = p.rope + row * p.rope_stride;
+      a[u] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[u] = fmaf(qv[k], c[lane + 64 * k], a[u]);
+      a[u] = fmaf(qv[8], r[lane], a[u]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += __shfl_xor(a[u], o, 64);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (t + u < n) {
+        if (lane == 0) sc[t + u] = a[u];
+        mloc = fmaxf(mloc, a[u]);
+      }
+    }
   }
   mloc = wave_max(mloc);
   if (lane == 0) red[wv] = mloc;
