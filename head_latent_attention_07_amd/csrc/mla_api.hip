@@ -102,6 +102,26 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   return pl;
 }
 
+// Rows with more than 16 splits are merged in two levels: mla_merge_splits_kernel
+// folds them into two groups, mla_combine_s4_kernel merges the groups and
+// applies W_UV. Up to 16 splits (four groups of 4 per half of the latent in
+// mla_combine_kernel's walk) one level is as fast. Returns the group count,
+// 0 for one level; MLA_MERGE_GROUPS (0-4) overrides.
+int merge_groups(int S) {
+  const char* e = std::getenv("MLA_MERGE_GROUPS");
+  if (e) return std::max(0, std::min(std::atoi(e), CB_G));
+  return S > 16 ? 2 : 0;
+}
+
+// Column split of the S <= 4 merge: when its grid has fewer workgroups than
+// the device has CUs. MLA_COMBINE_COLS (1 or 2 workgroups per head and
+// chunk of sequences) overrides.
+bool combine_col_split(int workgroups) {
+  const char* e = std::getenv("MLA_COMBINE_COLS");
+  if (e) return std::atoi(e) == 2;
+  return workgroups < device_cu_count();
+}
+
 // The fp8 cache goes to the fp8 matrix cores (decode_fp8mma.hpp) when its
 // layout fits that kernel: four waves of 32 heads per workgroup, splits of
 // whole 64-token tiles (at most 32 of them), and page blocks holding whole
@@ -546,9 +566,41 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
                                         H, pl, part_h, part_scale, part_lse);
   MLA_TRY(launch_attention(dp, pl, cdt == MLA_FP8_E4M3, opts, stream));
 
-  CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc};
-  hipLaunchKernelGGL(pl.S <= CB_G ? mla_combine_s4_kernel : mla_combine_kernel,
-                     dim3(ceil_div(H, 8) * 8 * nbc), dim3(CB_THREADS), 0, stream, cp);
+  CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc,
+                   pl.S, 1};
+  const dim3 cgrid(ceil_div(H, 8) * 8 * nbc);
+  // the S <= 4 merge takes two workgroups per (head, 32 sequences), each for
+  // half of the output columns, where one each would leave CUs idle
+  const bool col_split = combine_col_split((int)cgrid.x);
+  auto launch_s4 = [&]() {
+    if (col_split)
+      hipLaunchKernelGGL(mla_combine_s4_kernel<2>, dim3(2 * cgrid.x), dim3(CB_THREADS), 0, stream,
+                         cp);
+    else
+      hipLaunchKernelGGL(mla_combine_s4_kernel<4>, cgrid, dim3(CB_THREADS), 0, stream, cp);
+  };
+  if (pl.S <= CB_G) {
+    launch_s4();
+    return launch_status();
+  }
+  const int ng = merge_groups(pl.S);
+  if (ng == 0) {
+    hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
+    return launch_status();
+  }
+  MergeSplitsParams mp{part_h, part_scale, part_lse, B, H, pl.S, ceil_div(pl.S, ng), 0};
+  mp.NG = ceil_div(pl.S, mp.G);
+  const dim3 mgrid((unsigned)ceil_div((int64_t)B * mp.NG * H, MS_WAVES));
+  if (mp.G <= 4)
+    hipLaunchKernelGGL(mla_merge_splits_kernel<4>, mgrid, dim3(64 * MS_WAVES), 0, stream, mp);
+  else if (mp.G <= 8)
+    hipLaunchKernelGGL(mla_merge_splits_kernel<8>, mgrid, dim3(64 * MS_WAVES), 0, stream, mp);
+  else
+    hipLaunchKernelGGL(mla_merge_splits_kernel<16>, mgrid, dim3(64 * MS_WAVES), 0, stream, mp);
+  MLA_TRY(launch_status());
+  cp.S = mp.NG;
+  cp.ss = mp.G;
+  launch_s4();
   return launch_status();
 }
 

@@ -224,6 +224,7 @@ struct CombineParams {
   bf16* out;              // [B, H, 128]
   float* lse;             // [B, H] natural log, or nullptr
   int B, H, S, nbc;
+  int sp, ss;             // splits per sequence in the arrays; slots between merged splits
 };
 
 constexpr int CB_THREADS = 512;       // 8 waves
@@ -480,37 +481,139 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
 }
 
 // ----------------------------------------------------------------------------
-// merge + W_UV for S <= 4 splits (the many-sequence case), same grid and
+// First merge level for rows with many splits: the splits of each
+// (sequence, head) row are cut into NG groups of G consecutive splits, and
+// one wave merges one group into one partial of the same form (fp16 values
+// relative to the row maximum, the fp32 factor, the log2-domain lse), which
+// it writes over the group's first split. mla_combine_s4_kernel then merges
+// the NG group partials, G slots apart, and applies W_UV. Merging in groups
+// is exact up to rounding: the lse of a union of splits is the lse of the
+// groups' lse values, and each group's output is its splits' outputs
+// weighted by 2^(lse_s - lse_group). It spreads the partial bytes over
+// B * H * NG waves, where mla_combine_kernel has one workgroup per
+// (head, 32 sequences) walk its splits group after group.
+//
+// Lane l holds dims 8l .. 8l+7 of the row. The group is read MS_CH splits
+// at a time with a running maximum of the lse; past the group's last split
+// the loads read that split again with weight 0, so every load is
+// unconditional and issued before the weights are known. An empty split
+// (lse -inf, zeros, written by the attention kernels) weighs 0; a group of
+// empty splits gives zeros, factor 0 and lse -inf.
+// ----------------------------------------------------------------------------
+struct MergeSplitsParams {
+  _Float16* part_o;    // [B, S, H, 512] fp16, relative to part_scale
+  float* part_scale;   // [B, S, H]
+  float* part_lse;     // [B, S, H] log2 domain
+  int B, H, S, G, NG;  // splits, splits per group, groups (NG = ceil(S / G))
+};
+
+constexpr int MS_WAVES = 4;   // waves per workgroup (consecutive heads)
+
+template <int MS_CH>
+__global__ __launch_bounds__(64 * MS_WAVES) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void mla_merge_splits_kernel(MergeSplitsParams p) {
+  const int l = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane((int)blockIdx.x * MS_WAVES + (int)(threadIdx.x >> 6));
+  const int head = wid % p.H, rest = wid / p.H;   // (b, group, head), head fastest
+  const int g = rest % p.NG, b = rest / p.NG;
+  if (b >= p.B) return;
+  const int s0 = g * p.G, n = min(p.G, p.S - s0);
+  const int64_t row0 = ((int64_t)b * p.S + s0) * p.H + head;   // the group's first split
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = -INFINITY, wsum = 0.f;
+  for (int c = 0; c < n; c += MS_CH) {
+    f16x8 v[MS_CH];
+#pragma unroll
+    for (int k = 0; k < MS_CH; ++k)
+      v[k] = *(const f16x8*)(p.part_o + (row0 + (int64_t)min(c + k, n - 1) * p.H) * D_C + 8 * l);
+    // lane l holds the lse and factor of split c + (l mod MS_CH): one load
+    // per lane instead of a chain of uniform loads
+    const int kl = c + (l & (MS_CH - 1));
+    const int64_t ixl = row0 + (int64_t)min(kl, n - 1) * p.H;
+    float lvl = p.part_lse[ixl];
+    const float svl = p.part_scale[ixl];
+    lvl = (kl < n) ? lvl : -INFINITY;
+    float cm = fmaxf(L, lvl);
+#pragma unroll
+    for (int o = MS_CH / 2; o > 0; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+    // a new maximum rescales what is merged so far (0 when nothing is)
+    const float alpha = (L > -INFINITY) ? fast_exp2(L - cm) : 0.f;
+    L = cm;
+    float el = (lvl > -INFINITY) ? fast_exp2(lvl - L) : 0.f;
+    const float wl = el * svl;
+#pragma unroll
+    for (int o = MS_CH / 2; o > 0; o >>= 1) el += __shfl_xor(el, o, 64);
+    wsum = wsum * alpha + el;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] *= alpha;
+#pragma unroll
+    for (int k = 0; k < MS_CH; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] += wk * (float)v[k][e];
+    }
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(m[e]));
+  mx = wave_max(mx);
+  const float f = (mx > 0.f) ? 1.0f / mx : 0.f;
+  f16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)(m[e] * f);
+  // every read of the group's rows is done: each value stored depends on all of them
+  *(f16x8*)(p.part_o + row0 * D_C + 8 * l) = o;
+  if (l == 0) {
+    p.part_lse[row0] = (wsum > 0.f) ? L + __builtin_log2f(wsum) : -INFINITY;
+    p.part_scale[row0] = (wsum > 0.f) ? mx / wsum : 0.f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// merge + W_UV for S <= 4 splits (the many-sequence case, or the groups of
+// mla_merge_splits_kernel, split s at slot s * ss), same grid and
 // work split as above but without the weight table and the A staging: wave
 // w owns dims 32w .. 32w+31 of each half of the latent, lane l the sequence
 // l mod 32. A lane computes its sequence's weights from the (at most 4)
 // split lse values itself, merges its 16 dims of each half straight into
 // the MFMA A operand, and multiplies them by the 64 rows of W_UV[h] it
-// loaded into LDS itself, for all 128 output columns. The 8 waves' partial
-// products are summed through LDS (the W_UV buffer, free by then).
+// loaded into LDS itself, for the workgroup's 32 NCB output columns. The 8
+// waves' partial products are summed through LDS (the W_UV buffer, free by
+// then). NCB = 4: one workgroup per (head, 32 sequences) takes all 128
+// columns; NCB = 2: two workgroups take 64 columns each (half of W_UV[h] in
+// LDS each, twice the workgroups where one per (head, 32 sequences) would
+// leave CUs idle; both merge the same partials, the second from L2).
 // ----------------------------------------------------------------------------
+template <int NCB>
 __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParams p) {
-  __shared__ __attribute__((aligned(1024))) char w_lds[D_C * D_V * 2];   // 128 KB
+  constexpr int NCS = 4 / NCB;         // workgroups per (head, 32 sequences)
+  constexpr int ROWB = 64 * NCB;       // bytes of this workgroup's slice of a W_UV row
+  constexpr int RPI = 1024 / ROWB;     // slice rows per 1 KB direct load
+  constexpr int NI = 64 / RPI;         // direct loads per wave (its 64 rows)
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_C * ROWB];   // 128 or 64 KB
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
-  int head, bc;
+  int head, bc, cs;
   {
     const int x = blockIdx.x;
     const int q_lo = x & 7, rest = x >> 3;
     bc = __builtin_amdgcn_readfirstlane(rest % p.nbc);
-    head = __builtin_amdgcn_readfirstlane((rest / p.nbc) * 8 + q_lo);
+    const int r2 = rest / p.nbc;
+    cs = __builtin_amdgcn_readfirstlane(r2 % NCS);
+    head = __builtin_amdgcn_readfirstlane((r2 / NCS) * 8 + q_lo);
     if (head >= p.H) return;
   }
   const int S = p.S, b = bc * 32 + l32;
   const bool brow = b < p.B;
-  const int64_t row0 = (int64_t)min(b, p.B - 1) * S * p.H + head;   // (b, split 0, head)
+  const int64_t row0 = (int64_t)min(b, p.B - 1) * p.sp * p.H + head;   // (b, split 0, head)
+  const int64_t sstep = (int64_t)p.ss * p.H;                            // split s: + s * sstep
   // loads: lse and scale, half-0 partials, this wave's W_UV rows, half-1
   // partials (v[half][step][split]: dims 256 half + 32 w + 16 step + 8 h)
   float lv[CB_G], sv[CB_G];
 #pragma unroll
   for (int s = 0; s < CB_G; ++s) {
-    const int64_t ix = row0 + (int64_t)min(s, S - 1) * p.H;
+    const int64_t ix = row0 + min(s, S - 1) * sstep;
     lv[s] = p.part_lse[ix];
     sv[s] = p.part_scale[ix];
   }
@@ -520,20 +623,22 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
     for (int s = 0; s < CB_G; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        v[hf][t][s] = *(const f16x8*)(p.part_o + (row0 + (int64_t)min(s, S - 1) * p.H) * D_C +
+        v[hf][t][s] = *(const f16x8*)(p.part_o + (row0 + min(s, S - 1) * sstep) * D_C +
                                       256 * hf + 32 * w + 16 * t + 8 * h);
   };
   load_half(0);
   {
-    // rows 256 hf + 32 w .. +31 of W_UV[h] (8 KB per half) to the same
-    // rows of the LDS copy, 4 rows per 1 KB load
+    // rows 256 hf + 32 w .. +31 of W_UV[h], columns 32 NCB cs .. +32 NCB - 1
+    // (ROWB bytes of each 256-byte row), to the same rows of the LDS copy
+    // (rows ROWB apart), RPI rows per 1 KB load
     const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
+    const int vo = 256 * (l / (ROWB / 16)) + 16 * (l % (ROWB / 16));
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int line = (k >> 3) * 64 + 8 * w + (k & 7);   // line = 4 rows
+    for (int k = 0; k < NI; ++k) {
+      const int r0 = 256 * (k / (NI / 2)) + 32 * w + RPI * (k % (NI / 2));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(w_lds + line * 1024), 16, 16 * l,
-          line * 1024, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(w_lds + r0 * ROWB), 16, vo,
+          r0 * 256 + cs * ROWB, 0, 0);
     }
     asm volatile("" ::: "memory");   // later loads stay behind the DMA
   }
@@ -555,12 +660,12 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
   float wt[CB_G];
 #pragma unroll
   for (int s = 0; s < CB_G; ++s) wt[s] = e[s] * sv[s] * inv;
-  if (w == 0 && h == 0 && brow && p.lse)
+  if (cs == 0 && w == 0 && h == 0 && brow && p.lse)
     p.lse[(int64_t)b * p.H + head] = (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
 
-  f32x16 acc[4];
+  f32x16 acc[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x16{};
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
   const int colb0 = 16 * (g16 & 1) + 4 * (jj & 3);   // + 32 cb: B-operand column base
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -585,41 +690,42 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
     for (int t = 0; t < 2; ++t) {
       const int ra = 256 * hf + 32 * w + 16 * t + 8 * h + (jj >> 2);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         const int colb = 32 * cb + colb0;
-        const bf16x8 bop = tr_read_8(w_lds + ra * 256 + 2 * colb, w_lds + (ra + 4) * 256 + 2 * colb);
+        const bf16x8 bop = tr_read_8(w_lds + ra * ROWB + 2 * colb, w_lds + (ra + 4) * ROWB + 2 * colb);
         acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], bop, acc[cb], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // half 1 waits for its loads only after this
   }
   // sum over the 8 waves: wave w' stores acc[cb] registers 4 r4 .. 4 r4 + 3
-  // of lane l at f32x4 slot ((w' * 4 + cb) * 4 + r4) * 64 + l; wave w then
-  // adds up column block w / 2, registers 8 (w mod 2) .. +7
+  // of lane l at f32x4 slot ((w' * NCB + cb) * 4 + r4) * 64 + l (8 NCB
+  // 4 KB slots: the whole W_UV buffer); wave w then adds up slots
+  // j = RPW w .. RPW w + RPW - 1 of the 4 NCB (column block j / 4,
+  // registers 4 (j mod 4) .. +3)
+  constexpr int RPW = NCB / 2;
   lds_barrier();   // every wave is done with W_UV
   f32x4* const xch = (f32x4*)w_lds;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      xch[((w * 4 + cb) * 4 + r4) * 64 + l] =
+      xch[((w * NCB + cb) * 4 + r4) * 64 + l] =
           f32x4{acc[cb][4 * r4], acc[cb][4 * r4 + 1], acc[cb][4 * r4 + 2], acc[cb][4 * r4 + 3]};
   lds_barrier();
-  const int cb = w >> 1, rg = w & 1;
-  f32x4 sum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int ww = 0; ww < 8; ++ww)
+  for (int q = 0; q < RPW; ++q) {
+    const int j = RPW * w + q, cb = j >> 2, r4 = j & 3;
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 2; ++q) sum[q] += xch[((ww * 4 + cb) * 4 + 2 * rg + q) * 64 + l];
-  const int n = 32 * cb + l32;
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
+    for (int ww = 0; ww < 8; ++ww) sum += xch[((ww * NCB + cb) * 4 + r4) * 64 + l];
+    const int n = 32 * NCB * cs + 32 * cb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int r = 4 * (2 * rg + q) + c;   // accumulator register
-      const int bb = bc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)sum[q][c];
+      const int bb = bc * 32 + 8 * r4 + 4 * h + c;   // accumulator register 4 r4 + c
+      if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)sum[c];
     }
+  }
 }
 
 }  // namespace mla

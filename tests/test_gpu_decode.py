@@ -82,6 +82,35 @@ def test_many_splits(gpu, N, splits):
     run_and_compare(gpu, inp, "bf16", num_splits=splits)
 
 
+@pytest.mark.parametrize("groups", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("N,splits", [(1024, 7), (2240, 70)])
+def test_merge_levels(gpu, monkeypatch, N, splits, groups):
+    """Rows of more than 4 splits, merged in one pass (groups=0: the merge
+    with the weight table) or first folded into 1-4 groups of consecutive
+    splits that the second pass merges: 7 splits as 7, 4+3, 3+3+1, 2+2+2+1;
+    70 as 70 (16 splits per step, five steps, the last of 6), 35+35,
+    24+24+22, 18+18+18+16. The sequence of 33 tokens makes whole groups of
+    empty splits."""
+    monkeypatch.setenv("MLA_MERGE_GROUPS", str(groups))
+    lengths = torch.tensor([N, N - 700, 33], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=3, N=N, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16", num_splits=splits)
+
+
+@pytest.mark.parametrize("cols", [1, 2])
+@pytest.mark.parametrize("splits", [3, 22])
+def test_merge_column_split(gpu, monkeypatch, cols, splits):
+    """The merge of at most 4 partials with all 128 output columns per
+    workgroup (cols=1) or 64 (cols=2: two workgroups per head and chunk of
+    32 sequences): 40 sequences (a full chunk and a chunk of 8), 3 splits
+    merged directly, 22 folded into two groups first. The oracle checks
+    sequences from both chunks, the short ones included."""
+    monkeypatch.setenv("MLA_COMBINE_COLS", str(cols))
+    lengths = torch.tensor([(97 * i) % 700 + 1 for i in range(39)] + [700], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=40, N=700, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16", batch_ids=[0, 5, 31, 32, 38, 39], num_splits=splits)
+
+
 @pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("splits", [1, 0])
 def test_late_large_score_restart(gpu, cache_dtype, splits):
