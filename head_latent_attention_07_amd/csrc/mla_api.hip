@@ -793,6 +793,9 @@ mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_p
   pp.c = softmax_scale * LOG2E;
   pp.out = (bf16*)out;
   pp.lse = lse;
+  // longest query tiles first unless MLA_PREFILL_ORDER=0
+  const char* oe = std::getenv("MLA_PREFILL_ORDER");
+  pp.order = (oe && std::atoi(oe) == 0) ? 0 : 1;
   const int nqt = ceil_div(chunk, PF_Q);
   const dim3 agrid((unsigned)((int64_t)8 * ceil_div((int64_t)B * H, 8) * nqt));
   hipEvent_t a0 = opts ? opts->attn_begin : nullptr, a1 = opts ? opts->attn_end : nullptr;

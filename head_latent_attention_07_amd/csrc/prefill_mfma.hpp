@@ -300,6 +300,7 @@ struct PrefillParams {
   const int32_t* lengths;
   int B, H, T, cap, max_len;
   float c;              // softmax_scale * log2(e)
+  int order;            // work order, see pf_work
   bf16* out;            // [B, T, H, 128]
   float* lse;           // [B, T, H] natural log, or nullptr
 };
@@ -317,20 +318,34 @@ constexpr int PF_STAGE = PF_V + PF_KEYS * 256;   // 40 KB
 //   V^T rows (128 B = 64 keys of one value dim), same reads:          c ^ ((dim >> 1) & 7)
 __device__ __forceinline__ int pf_kswz(int k) { return k & 15; }
 
+// (sequence, head) pair and query tile of this workgroup. XCD x takes the
+// pairs = x mod 8 (their keys and values are read through that XCD's L2).
+// order 1 (the default): the longest query tiles of all the XCD's pairs
+// first, then the next longest, so that no long tile starts near the end of
+// the launch; order 0: each pair with all its query tiles (longest first)
+// in a row.
+__device__ __forceinline__ void pf_work(const PrefillParams& p, int nqt, int& pr, int& qt) {
+  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
+  if (p.order == 0) {
+    pr = (i / nqt) * 8 + xcd;
+    qt = nqt - 1 - (i % nqt);
+  } else {
+    const int nh = (p.B * p.H + 7) / 8;
+    pr = (i % nh) * 8 + xcd;
+    qt = nqt - 1 - i / nh;
+  }
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * PF_STAGE];
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5, l32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqt = (p.T + PF_Q - 1) / PF_Q;
-  // XCD-major order: XCD x takes the (sequence, head) pairs = x mod 8, each
-  // with all its query tiles (longest first) in a row, so their shared keys
-  // and values are read through that XCD's L2
-  const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
-  const int pr = (i / nqt) * 8 + xcd;
+  int pr, qt;
+  pf_work(p, nqt, pr, qt);
   if (pr >= p.B * p.H) return;
   const int b = pr / p.H, head = pr - b * p.H;
-  const int qt = nqt - 1 - (i % nqt);
   const int len = min(max(p.lengths[b], 0), p.max_len);
   const int p0 = len - p.T;                    // position of chunk query 0
   const int q0 = qt * PF_Q, qw0 = q0 + 32 * w;

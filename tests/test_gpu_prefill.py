@@ -90,3 +90,13 @@ def test_prefill_sequence_shorter_than_chunk(gpu):
 def test_prefill_32_heads(gpu):
     """32 heads (one (sequence, head) group per XCD slot), a prompt of 777."""
     run_case(gpu, 2, 777, [777, 777], paged=False, H=32, seed=10)
+
+
+@pytest.mark.parametrize("order", ["0", "1"])
+def test_prefill_work_orders(gpu, monkeypatch, order):
+    """Both orders of the attention launch's workgroups (each (sequence,
+    head) pair's query tiles in a row, or the longest tiles of all pairs
+    first): chunks of 300 (three query tiles, the last ragged) after
+    contexts of 1200, 400 and 0 tokens, 32 heads."""
+    monkeypatch.setenv("MLA_PREFILL_ORDER", order)
+    run_case(gpu, 3, 300, [1500, 700, 300], paged=False, H=32, seed=11)
