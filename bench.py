@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--fused", action="store_true")
     ap.add_argument("--restart", action="store_true")
     ap.add_argument("--with-projection", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from HIP graphs (one per layer)")
     return ap.parse_args()
 
 
@@ -957,10 +959,43 @@ def main():
             "fp8_mfma_floor_ms": mfma_floor_ms / 2,
             "frac_of_hbm_floor": hbm_floor_ms / ms_per_step,
             "frac_of_bf16_mfma_floor": mfma_floor_ms / ms_per_step}
+    if args.graph:
+        result["hip_graph"] = graph_timing(step, layers, full_step, n_layers, B, steps, warmup)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
         result["cpu_absorbed_f32"] = cpu_absorbed_f32(cfg, min(args.cpu_seconds, 8.0))
     print(json.dumps(result), flush=True)
+
+
+def graph_timing(step, layers, full_step, n_layers, B, steps, warmup):
+    """The same steps replayed from HIP graphs (torch.cuda.CUDAGraph on the
+    caller's stream): one graph per cycled layer (the whole step for the
+    61-layer mode), captured after a warm-up on a side stream; the step's
+    launches then go to the GPU without a host call per kernel."""
+    import torch
+    n = 1 if full_step else n_layers
+    graphs = []
+    for k in range(n):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(k)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(k)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    return {"ms_per_step": ms, "tokens_per_s": B * steps / (t1 - t0), "graphs": n}
 
 
 if __name__ == "__main__":
