@@ -102,15 +102,19 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   return pl;
 }
 
-// Rows with more than 16 splits are merged in two levels: mla_merge_splits_kernel
-// folds them into two groups, mla_combine_s4_kernel merges the groups and
-// applies W_UV. Up to 16 splits (four groups of 4 per half of the latent in
-// mla_combine_kernel's walk) one level is as fast. Returns the group count,
-// 0 for one level; MLA_MERGE_GROUPS (0-4) overrides.
-int merge_groups(int S) {
+// Rows of more than 4 splits are merged in one level (mla_combine_kernel)
+// or two (mla_merge_splits_kernel folds each row's splits into groups,
+// mla_combine_s4_kernel merges the groups and applies W_UV). Measured: two
+// levels win above 16 splits (2 groups), and from 5 splits when there are
+// at most 32 sequences (1 group; mla_combine_kernel then has only one
+// workgroup per head); with more sequences and 5-16 splits one level is
+// faster. Returns the group count, 0 for one level; MLA_MERGE_GROUPS (0-4)
+// overrides.
+int merge_groups(int S, int nbc) {
   const char* e = std::getenv("MLA_MERGE_GROUPS");
   if (e) return std::max(0, std::min(std::atoi(e), CB_G));
-  return S > 16 ? 2 : 0;
+  if (S > 16) return 2;
+  return nbc == 1 ? 1 : 0;
 }
 
 // Column split of the S <= 4 merge: when its grid has fewer workgroups than
@@ -583,7 +587,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
     launch_s4();
     return launch_status();
   }
-  const int ng = merge_groups(pl.S);
+  const int ng = merge_groups(pl.S, nbc);
   if (ng == 0) {
     hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
     return launch_status();
