@@ -77,7 +77,7 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   if (act == MLA_F32) {
     pl.NW = 0;
     pl.G = 1;
-    const int min_tok = 128;
+    const int min_tok = 64;
     S = std::max(ceil_div(len, F32_MAX_SPLIT),
                  std::min(ceil_div(cus, (int64_t)B * H), ceil_div(len, min_tok)));
   } else {
@@ -523,7 +523,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
       MLA_TRY(launch_status());
     }
     float* q = (float*)(ws + wl.q_off);
-    hipLaunchKernelGGL(mla_absorb_f32_kernel, dim3(B * H), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mla_absorb_f32_kernel, dim3(4 * B * H), dim3(256), 0, stream,
                        (const float*)q_nope, (const float*)q_pe, (const float*)w_uk, q, H, c);
     MLA_TRY(launch_status());
     DecodeF32Params dp;
@@ -549,7 +549,7 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
     hipLaunchKernelGGL(mla_decode_f32_kernel, dim3(B * H * pl.S), dim3(256), 0, stream, dp);
     MLA_TRY(launch_status());
     if (opts && opts->attn_end) (void)hipEventRecord(opts->attn_end, stream);
-    hipLaunchKernelGGL(mla_combine_f32_kernel, dim3(B * H), dim3(128), 0, stream, part_o,
+    hipLaunchKernelGGL(mla_combine_f32_kernel, dim3(4 * B * H), dim3(256), 0, stream, part_o,
                        part_lse, (const float*)w_uv, (float*)out, lse, H, pl.S);
     return launch_status();
   }
