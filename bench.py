@@ -852,7 +852,7 @@ def main():
 
     ev = HipEvents()
 
-    def layer_call(L, events=None):
+    def layer_call(L, events=None, stream=None):
         inp = L["inp"]
         new_rows = (L["c"], L["k"], L["pos"])
         if args.with_projection:
@@ -874,15 +874,17 @@ def main():
                              seq_capacity=inp.seq_capacity, block_table=inp.block_table,
                              block_size=inp.block_size)
             new_rows = None
-        mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events,
-                          append=new_rows)
+        if "call" not in L:   # the step's decode call, marshalled once per layer
+            L["call"] = mla.prepare_decode_inputs(inp, out=L["out"], lse=L["lse"],
+                                                  workspace=L["ws"], append=new_rows)
+        L["call"].run(events, stream)
 
-    def step(i, events=None):
+    def step(i, events=None, stream=None):
         if full_step:
             for k, L in enumerate(layers):
-                layer_call(L, events[k] if events else None)
+                layer_call(L, events[k] if events else None, stream)
         else:
-            layer_call(layers[i % n_layers], events[0] if events else None)
+            layer_call(layers[i % n_layers], events[0] if events else None, stream)
 
     for i in range(warmup):
         step(i)
@@ -979,12 +981,12 @@ def graph_timing(step, layers, full_step, n_layers, B, steps, warmup):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step(k)
+            step(k, stream=side.cuda_stream)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(k)
+            step(k, stream=torch.cuda.current_stream().cuda_stream)
         graphs.append(g)
     for i in range(warmup):
         graphs[i % n].replay()

@@ -59,6 +59,7 @@ class PrefillOptions(ctypes.Structure):
 
 _lib = None
 
+_CARG = type(ctypes.byref(ctypes.c_int32(0)))   # what ctypes.byref returns
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -286,6 +287,84 @@ def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
         st = lib.mla_decode(*head, seq_capacity, *tail)
     _check(st)
     return out, lse
+
+
+class PreparedDecode:
+    """One decode call (mla_decode or mla_decode_paged) with its arguments
+    marshalled once, for loops that issue the same call on the same buffers
+    many times (a serving step): run() re-issues it, optionally between the
+    given timing events, on the stream it was prepared with (torch's current
+    stream at preparation if none was given) or on a stream given to run()
+    (a graph's capture stream). The tensors passed to prepare_decode must
+    outlive the object; out, lse and workspace are the ones it was prepared
+    with."""
+
+    def __init__(self, fn, args, opts, keep):
+        self._fn = fn
+        self._args = args
+        self._opts = opts
+        self._keep = keep   # ctypes structs and tensors the arguments point to
+        self._stream = args[-1]
+
+    def run(self, events: Optional[Tuple[int, int]] = None, stream: Optional[int] = None):
+        """Issue the call; `stream` (a raw stream handle) overrides the
+        prepared stream for this run (e.g. a graph's capture stream)."""
+        o = self._opts
+        o.attn_begin, o.attn_end = events if events is not None else (None, None)
+        self._args[-1] = self._stream if stream is None else ctypes.c_void_p(stream)
+        _check(self._fn(*self._args))
+
+
+def prepare_decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
+                   out, lse, workspace, scales=None, seq_capacity=0, block_table=None,
+                   block_size=64, softmax_scale=None, num_splits=0, append=None,
+                   stream=None) -> PreparedDecode:
+    """A PreparedDecode for the call _decode would make with these arguments
+    (out, lse and workspace given)."""
+    lib = load()
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    d = dims(H)
+    act = dtype_code(q_nope.dtype)
+    cdt = dtype_code(latent.dtype)
+    opts = DecodeOptions()
+    opts.num_splits = num_splits
+    keep = [d, opts, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, out, lse, workspace,
+            scales, block_table]
+    if append is not None:
+        c_kv, k_pe, positions = append[:3]
+        theta = append[3] if len(append) > 3 else 10000.0
+        a = AppendArgs(_ptr(c_kv), _ptr(k_pe), dtype_code(c_kv.dtype), _ptr(positions), theta,
+                       None, 0, 0)
+        opts.append = ctypes.pointer(a)
+        keep += [a, c_kv, k_pe, positions]
+    head = [ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), act,
+            _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(scales), cdt,
+            latent.shape[0]]
+    tail = [_ptr(lengths), B, max_len, 0.0 if softmax_scale is None else softmax_scale,
+            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), ctypes.byref(opts),
+            _stream(stream)]
+    if paged:
+        fn = lib.mla_decode_paged
+        args = head + [_ptr(block_table), block_table.shape[1], block_size] + tail
+    else:
+        fn = lib.mla_decode
+        args = head + [seq_capacity] + tail
+    # the arguments as ctypes values of the declared types, converted once
+    args = [v if isinstance(v, _CARG) else t(v) for t, v in zip(fn.argtypes, args)]
+    return PreparedDecode(fn, args, opts, keep)
+
+
+def prepare_decode_inputs(inp, **kw) -> PreparedDecode:
+    """prepare_decode for a synthetic workload (see synth)."""
+    lat, rop = split_cache(inp.cache)
+    if inp.paged:
+        return prepare_decode(True, inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, lat, rop,
+                              inp.lengths, inp.max_len, block_table=inp.block_table,
+                              block_size=inp.block_size, scales=inp.scales,
+                              softmax_scale=inp.scale, **kw)
+    return prepare_decode(False, inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, lat, rop, inp.lengths,
+                          inp.max_len, seq_capacity=inp.seq_capacity, scales=inp.scales,
+                          softmax_scale=inp.scale, **kw)
 
 
 def decode_paged_noalloc(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,

@@ -6,7 +6,8 @@ kernels. Each case captures one call, then replays it three times with the
 program's own eager work (another decode into the same workspace, fills of
 the outputs) and synchronizations between the replays, and checks every
 replay against the eager result of the same call bit for bit (the kernels
-are deterministic)."""
+are deterministic). Also: a decode call marshalled once and re-issued (the
+benchmark's loop) against the direct call."""
 
 import pytest
 import torch
@@ -130,3 +131,41 @@ def test_graph_prefill(gpu):
     run(qn, qp, out, lse)
     torch.cuda.synchronize()
     capture_and_replay(lambda: run(qn, qp, out, lse), [out, lse], lambda: run(qn2, qp2))
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_prepared_decode_matches_direct_call(gpu, paged):
+    """A decode call marshalled once (prepare_decode, as the benchmark loop
+    issues it) gives the direct call's outputs bit for bit, on every run,
+    with and without timing events."""
+    print(f"[case] prepared decode paged={paged}", flush=True)
+    lengths = torch.tensor([700, 1, 333, 512], dtype=torch.int32)
+    inp = synth.make_inputs(3, B=4, N=700, lengths=lengths, paged=paged).to("cuda")
+    act, cdt = gpu.dtype_code(inp.q_nope.dtype), gpu.dtype_code(inp.cache.dtype)
+    ws = torch.empty(gpu.workspace_size(inp.H, 4, inp.max_len, act, cdt), dtype=torch.uint8,
+                     device="cuda")
+    c_new, k_new = synth.append_inputs(8300, 4, "bf16", device="cuda")
+    app = (c_new, k_new, (inp.lengths - 1).to("cuda"))
+    ref_out, ref_lse = gpu.decode_inputs(inp, workspace=ws, append=app)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    call = gpu.prepare_decode_inputs(inp, out=out, lse=lse, workspace=ws, append=app)
+    import bench
+    ev = bench.HipEvents()
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        pair = (ev.create(), ev.create()) if rep == 1 else None
+        call.run(pair)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(ref_out)) and torch.equal(bits(lse), bits(ref_lse))
+        if pair:
+            assert ev.elapsed_ms(*pair) > 0.0
+            ev.destroy(pair[0])
+            ev.destroy(pair[1])
+    print("[result] bit-identical on every run", flush=True)
+    # the prepared call captured in a graph (run on the capture stream)
+    other = synth.make_inputs(3, B=4, N=700, lengths=lengths, paged=paged, layer=1).to("cuda")
+    capture_and_replay(lambda: call.run(stream=torch.cuda.current_stream().cuda_stream),
+                       [out, lse], lambda: gpu.decode_inputs(other, workspace=ws))
