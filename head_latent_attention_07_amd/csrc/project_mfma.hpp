@@ -217,14 +217,15 @@ __global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, 
 // the two accumulators are summed through LDS at the end.
 // ----------------------------------------------------------------------------
 struct CombineParams {
-  const _Float16* part_o;   // [B, S, H, 512] fp16, relative to part_scale
-  const float* part_scale;  // [B, S, H]
-  const float* part_lse;    // [B, S, H] log2 domain
+  const _Float16* part_o;   // [B, sp, H, 512] fp16, relative to part_scale
+  const float* part_scale;  // [B, sp, H]
+  const float* part_lse;    // [B, sp, H] log2 domain
   const bf16* w_uv;       // [H, 512, 128]
   bf16* out;              // [B, H, 128]
   float* lse;             // [B, H] natural log, or nullptr
-  int B, H, S, nbc;
-  int sp, ss;             // splits per sequence in the arrays; slots between merged splits
+  int B, H, S, nbc;       // S: partials merged per sequence; nbc: chunks of 32 sequences
+  int sp, ss;             // split slots per sequence in the arrays; partial s is slot s * ss
+                          // (mla_combine_kernel: sp == S, ss == 1)
 };
 
 constexpr int CB_THREADS = 512;       // 8 waves
