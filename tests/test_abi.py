@@ -55,6 +55,37 @@ def test_workspace_size_grows_with_batch():
     assert mla.load().mla_decode_workspace_size(ctypes.byref(bad), 1, 16, 1, 1, None) == 0
 
 
+def _ws_for_splits(B, H, S, act):
+    """The decode workspace of a plan with S splits per sequence: absorbed
+    queries [B, H, 576], split partials [B, S, H, 512] (fp16 with an fp32
+    row factor, or fp32), split lse [B, S, H], each region 256-byte aligned."""
+    al = lambda x: (x + 255) // 256 * 256
+    qe = 4 if act == mla.MLA_F32 else 2
+    rows = B * S * H
+    po = al(B * H * 576 * qe)
+    ps = al(po + rows * 512 * qe)
+    pl = al(ps + (0 if act == mla.MLA_F32 else rows * 4))
+    return al(pl + rows * 4)
+
+
+@pytest.mark.parametrize("B,H,N,act,cdt,forced,S", [
+    (64, 128, 4096, mla.MLA_BF16, mla.MLA_BF16, 0, 4),      # one workgroup per CU (256 CUs)
+    (1, 128, 4096, mla.MLA_BF16, mla.MLA_BF16, 0, 64),      # splits down to 64 tokens
+    (4, 128, 131072, mla.MLA_BF16, mla.MLA_BF16, 0, 64),    # 2048 tokens per split
+    (32, 128, 32768, mla.MLA_BF16, mla.MLA_BF16, 0, 16),    # 8 by CUs, but <= 2048 tokens per split
+    (32, 128, 32768, mla.MLA_BF16, mla.MLA_FP8_E4M3, 0, 16),  # fp8 matrix cores: <= 32 tiles of 64
+    (32, 128, 8192, mla.MLA_BF16, mla.MLA_BF16, 0, 8),      # one workgroup per CU
+    (1, 128, 100, mla.MLA_BF16, mla.MLA_BF16, 0, 2),
+    (2, 128, 1024, mla.MLA_BF16, mla.MLA_BF16, 7, 7),       # forced: 160 tokens per split
+    (1, 128, 8192, mla.MLA_BF16, mla.MLA_BF16, 1, 4),       # forced 1, but <= 2048 tokens per split
+    (1, 16, 512, mla.MLA_F32, mla.MLA_F32, 0, 8),           # fp32: splits down to 64 tokens
+])
+def test_split_plan_through_workspace_size(B, H, N, act, cdt, forced, S):
+    """The split planner's choices, read back from the workspace size the
+    library asks for (the CU count is 256 without a device)."""
+    assert mla.workspace_size(H, B, N, act, cdt, forced) == _ws_for_splits(B, H, S, act)
+
+
 def _decode_status(dims, act=mla.MLA_BF16, cdt=mla.MLA_BF16, batch=1, max_len=16, ptr=16,
                    ls=576, rs=576, rows=64, cap=16, ws=1 << 20, scale=0.07, scales=True):
     lib = mla.load()
