@@ -25,6 +25,9 @@ Prints ONE JSON line (see the fields below). Options:
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
+  --clock SECONDS          after the timed steps, run the same steps for about
+                           SECONDS more while a host thread samples the shader
+                           clock through amdsmi (reported as "shader_clock")
   --with-projection        the step also computes the new rows from the tokens'
                            hidden states (d_model 7168): mla_project, then the
                            decode call appends from its workspace (with
@@ -81,6 +84,9 @@ def parse():
     ap.add_argument("--with-projection", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per layer)")
+    ap.add_argument("--clock", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run the same steps for about SECONDS more "
+                         "while a host thread samples the GPU's shader clock (amdsmi)")
     return ap.parse_args()
 
 
@@ -963,10 +969,79 @@ def main():
             "frac_of_bf16_mfma_floor": mfma_floor_ms / ms_per_step}
     if args.graph:
         result["hip_graph"] = graph_timing(step, layers, full_step, n_layers, B, steps, warmup)
+    if args.clock > 0:
+        n_clock = max(steps, int(args.clock / (ms_per_step * 1e-3)))
+
+        def clocked():
+            for i in range(n_clock):
+                step(i)
+            torch.cuda.synchronize()
+
+        result["shader_clock"] = sample_clocks(clocked, n_clock)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
         result["cpu_absorbed_f32"] = cpu_absorbed_f32(cfg, min(args.cpu_seconds, 8.0))
     print(json.dumps(result), flush=True)
+
+
+def sample_clocks(run, n_steps):
+    """The GPU's shader (gfx) clock while run() issues n_steps steps: a host
+    thread polls amdsmi's GPU metrics every ~2 ms (the clock fields the
+    firmware reports: per-XCD current clocks and the average, N/A values
+    dropped) and the GFX clock domain's current frequency. Returns the
+    per-field median / p10 / p90 in MHz over the samples taken while the
+    steps ran, with the steps' own time for comparison with the timed run."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 - reported in the line, not fatal
+        return {"error": f"amdsmi unavailable: {e!r}"}
+    fields, errors = {}, []
+    stop = threading.Event()
+
+    def add(name, v):
+        if isinstance(v, (list, tuple)):
+            vals = [x for x in v if isinstance(x, (int, float)) and 0 < x < 65535]
+            if vals:
+                fields.setdefault(name + "_mean_over_xcds", []).append(sum(vals) / len(vals))
+        elif isinstance(v, (int, float)) and 0 < v < 65535:
+            fields.setdefault(name, []).append(float(v))
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                for k, v in m.items():
+                    if "gfxclk" in k or "gfx_activity" in k:
+                        add("metrics." + k, v)
+                c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                add("clock_info.gfx.clk", c.get("clk"))
+            except Exception as e:  # noqa: BLE001
+                if len(errors) < 3:
+                    errors.append(repr(e))
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    run()
+    t1 = time.perf_counter()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    out = {"source": "amdsmi gpu metrics + clock info, polled every ~2 ms from a host thread",
+           "steps": n_steps, "ms_per_step": (t1 - t0) * 1e3 / n_steps, "unit": "MHz"}
+    for k, v in sorted(fields.items()):
+        out[k] = {"samples": len(v), "p10": percentile(v, 10), "median": percentile(v, 50),
+                  "p90": percentile(v, 90)}
+    if errors:
+        out["errors"] = errors
+    return out
 
 
 def graph_timing(step, layers, full_step, n_layers, B, steps, warmup):

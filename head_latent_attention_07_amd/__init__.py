@@ -8,6 +8,7 @@ library is missing, every entry point raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -24,7 +25,9 @@ SYMBOLS = ("mla_status_string", "mla_cache_bytes_per_token", "mla_cache_append",
            "mla_decode_workspace_size", "mla_decode", "mla_decode_paged",
            "mla_project_append", "mla_project_workspace_size", "mla_project",
            "mla_decode_paged_noalloc", "mla_prefill_workspace_size", "mla_prefill",
-           "mla_fuse_weights", "mla_decode_fused_workspace_size", "mla_decode_fused")
+           "mla_fuse_weights", "mla_decode_fused_workspace_size", "mla_decode_fused",
+           "mla_debug_errors")
+DEBUG_LENGTH, DEBUG_BLOCK, DEBUG_POSITION = 1, 2, 4   # bits of the debug error word
 NOALLOC_SCRATCH_BYTES = 80 << 20      # MLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -72,11 +75,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    p = path or LIB_PATH
+    # MLA_LIBRARY names another build of the same library (the host-sanitizer
+    # or the debug-checks build); the default is the release build
+    p = path or os.environ.get("MLA_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"MLA HIP library not built: {p} is missing "
                            "(run head_latent_attention_07_amd/build.py)")
     lib = ctypes.CDLL(p)
+    lib.mla_debug_errors.restype = ctypes.c_int
+    lib.mla_debug_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), _P]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_cache_bytes_per_token.restype = _SZ
@@ -127,6 +134,18 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                        _I32, _I32, _F, _P, _SZ, _P]
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route the binding's calls to another build of the library (the
+    debug-checks build, say) inside the block; the previous one afterwards."""
+    global _lib
+    saved, _lib = _lib, None
+    try:
+        yield load(path)
+    finally:
+        _lib = saved
 
 
 def _check(status: int):
@@ -244,6 +263,15 @@ def project_append(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor
         _ptr(positions), B, _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
         _ptr(scales), dtype_code(latent.dtype), latent.shape[0], seq_capacity, _ptr(block_table),
         max_blocks, block_size, rope_theta, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def debug_errors(stream=None) -> int:
+    """The error word of the debug-checks build (mla_debug_errors): waits for
+    the stream, returns the word's DEBUG_* bits and clears it. Raises
+    MLAError (MLA_ERR_UNSUPPORTED) on a library built without the checks."""
+    word = ctypes.c_uint32(0)
+    _check(load().mla_debug_errors(ctypes.byref(word), _stream(stream)))
+    return int(word.value)
 
 
 def project(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,

@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmla_hip.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# the same library with the debug checks of the device-resident integers
+# (lengths, block-table entries, append positions) compiled in
+DEBUG_LIB_PATH = os.path.join(HERE, "libmla_hip_debug.so")
 SOURCES = [os.path.join(HERE, "csrc", "mla_api.hip")]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
@@ -109,13 +112,16 @@ def scc_conflicts(asm_text: str) -> list:
     return bad
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, debug_checks: bool = False) -> str:
     """Compile the library (and, alongside, the device assembly for the M0
-    check); returns the path of the built .so."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
-    asm_path = LIB_PATH + ".s.tmp"
-    asm_flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    and SCC checks); returns the path of the built .so. `debug_checks`
+    builds libmla_hip_debug.so (MLA_DEBUG_CHECKS=1) instead."""
+    lib_path = DEBUG_LIB_PATH if debug_checks else LIB_PATH
+    flags = HIPCC_FLAGS + (["-DMLA_DEBUG_CHECKS=1"] if debug_checks else [])
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), *flags, *SOURCES, "-o", tmp]
+    asm_path = lib_path + ".s.tmp"
+    asm_flags = [f for f in flags if f not in ("-fPIC", "-shared")]
     asm_cmd = [hipcc(), *asm_flags, "--cuda-device-only", "-S", *SOURCES, "-o", asm_path]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -142,9 +148,17 @@ def build(verbose: bool = False) -> str:
         os.remove(tmp)
         raise RuntimeError("SCC read after an inline-assembly block that writes it: " +
                            "; ".join(f"{f}: {i}" for f, i in bad_scc[:5]))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_all(verbose: bool = False) -> list:
+    """The release and the debug-checks libraries, built concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        futs = [ex.submit(build, verbose, dbg) for dbg in (False, True)]
+        return [f.result() for f in futs]
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

@@ -80,13 +80,18 @@ __device__ __forceinline__ void append_write(const AppendParams& p, int b, int l
 __device__ __forceinline__ bool append_dest(const AppendParams& p, int b, int pos, int64_t* row) {
   int64_t r;
   if (p.block_table) {
-    if (pos < 0 || pos / p.block_size >= p.max_blocks) return false;
+    const bool in_cap = pos >= 0 && pos / p.block_size < p.max_blocks;
+    debug_flag(!in_cap, DBG_POSITION);
+    if (!in_cap) return false;
     r = (int64_t)p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size] * p.block_size +
         pos % p.block_size;
   } else {
-    if (pos < 0 || pos >= p.seq_capacity) return false;
+    const bool in_cap = pos >= 0 && pos < p.seq_capacity;
+    debug_flag(!in_cap, DBG_POSITION);
+    if (!in_cap) return false;
     r = (int64_t)b * p.seq_capacity + pos;
   }
+  debug_flag(r < 0 || r >= p.rows, DBG_BLOCK);
   if (r < 0 || r >= p.rows) return false;
   *row = r;
   return true;

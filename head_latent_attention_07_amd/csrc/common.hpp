@@ -30,6 +30,30 @@ constexpr float LN2 = 0.6931471805599453f;
 
 enum CacheKind { CACHE_F32 = 0, CACHE_BF16 = 1, CACHE_FP8 = 2 };
 
+// Debug-checks build (MLA_DEBUG_CHECKS=1): the device-resident integers that
+// the host cannot validate without a synchronisation (sequence lengths,
+// block-table entries, append positions) are checked where the kernels read
+// them, and each violation sets its bit in a per-device error word (read
+// and cleared by mla_debug_errors). The kernels clamp such values in every
+// build, so a violation never makes them access memory out of bounds; the
+// word only reports it. Release builds compile the checks away.
+#ifndef MLA_DEBUG_CHECKS
+#define MLA_DEBUG_CHECKS 0
+#endif
+enum DebugBit : unsigned {
+  DBG_LENGTH = 1u,       // lengths[b] outside [0, max_len]
+  DBG_BLOCK = 2u,        // block-table entry (or the row it gives) outside the cache
+  DBG_POSITION = 4u,     // append position outside the sequence's capacity
+};
+#if MLA_DEBUG_CHECKS
+__device__ unsigned int g_debug_word;
+__device__ __forceinline__ void debug_flag(bool bad, unsigned bit) {
+  if (bad) atomicOr(&g_debug_word, bit);
+}
+#else
+__device__ __forceinline__ void debug_flag(bool, unsigned) {}
+#endif
+
 // 64-lane wavefront helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -58,7 +82,9 @@ __device__ __forceinline__ int64_t cache_row(int b, int t, int64_t seq_capacity,
   } else {
     r = (int64_t)b * seq_capacity + t;
   }
-  return (r >= 0 && r < rows) ? r : 0;
+  const bool ok = r >= 0 && r < rows;
+  debug_flag(!ok, DBG_BLOCK);
+  return ok ? r : 0;
 }
 
 // Absorbed-query layout in the workspace (written by the absorb kernel,

@@ -465,7 +465,15 @@ __device__ __forceinline__ int load_block_table(const DecodeParams& p, int b, in
   const int first = t0 / p.block_size;
   const int nblk = min((t1 - 1) / p.block_size - first + 1, MAX_SPLIT_BLOCKS);
   const int32_t* src = p.block_table + (int64_t)b * p.max_blocks + first;
+#if MLA_DEBUG_CHECKS
+  const int64_t nblocks = p.rows / p.block_size;
+  for (int i = tid; i < nblk; i += NT) {
+    tab[i] = src[i];
+    debug_flag(src[i] < 0 || src[i] >= nblocks, DBG_BLOCK);
+  }
+#else
   for (int i = tid; i < nblk; i += NT) tab[i] = src[i];
+#endif
   return first;
 }
 
@@ -756,7 +764,9 @@ __device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, W
   if (q >= p.B * p.S) return false;
   wi.b = __builtin_amdgcn_readfirstlane(q / p.S);
   wi.s = __builtin_amdgcn_readfirstlane(q - wi.b * p.S);
-  const int len = min(max(__builtin_amdgcn_readfirstlane(p.lengths[wi.b]), 0), p.max_len);
+  const int raw_len = __builtin_amdgcn_readfirstlane(p.lengths[wi.b]);
+  debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
+  const int len = min(max(raw_len, 0), p.max_len);
   wi.t0 = wi.s * p.tokens_per_split;
   wi.t1 = min(wi.t0 + p.tokens_per_split, len);
   wi.head = (g * NW + w) * 32 + (l & 31);

@@ -67,7 +67,9 @@ __global__ __launch_bounds__(256) void mla_decode_f32_kernel(DecodeF32Params p) 
   const int s = blockIdx.x % p.S;
   const int bh = blockIdx.x / p.S;
   const int b = bh / p.H, head = bh % p.H;
-  const int len = min(max(p.lengths[b], 0), p.max_len);
+  const int raw_len = p.lengths[b];
+  debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
+  const int len = min(max(raw_len, 0), p.max_len);
   const int t0 = s * p.tokens_per_split;
   const int t1 = min(t0 + p.tokens_per_split, len);
   float* po = p.part_o + (((int64_t)b * p.S + s) * p.H + head) * D_C;

@@ -614,6 +614,27 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
 
 extern "C" {
 
+mla_status mla_debug_errors(uint32_t* word, hipStream_t stream) {
+  if (!word) return MLA_ERR_INVALID_ARG;
+  *word = 0;
+#if MLA_DEBUG_CHECKS
+  void* dev_word = nullptr;
+  if (hipGetSymbolAddress(&dev_word, HIP_SYMBOL(mla::g_debug_word)) != hipSuccess || !dev_word)
+    return MLA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_HIP;
+  uint32_t v = 0;
+  const uint32_t zero = 0;
+  if (hipMemcpy(&v, dev_word, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  if (hipMemcpy(dev_word, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+    return MLA_ERR_HIP;
+  *word = v;
+  return MLA_OK;
+#else
+  (void)stream;
+  return MLA_ERR_UNSUPPORTED;
+#endif
+}
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

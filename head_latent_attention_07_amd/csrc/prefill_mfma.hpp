@@ -142,7 +142,9 @@ void mla_prefill_expand_kernel(ExpandParams p) {
   const int head = hl * 8 + xcd;
   const int b = rem / ntile, rt = rem - b * ntile;
   if (head >= p.H) return;
-  const int len = min(max(p.lengths[b], 0), p.max_len);
+  const int raw_len = p.lengths[b];
+  debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
+  const int len = min(max(raw_len, 0), p.max_len);
   const int t0 = rt * EX_ROWS;
   if (t0 >= len) return;
 
@@ -346,7 +348,9 @@ void mla_prefill_attn_kernel(PrefillParams p) {
   pf_work(p, nqt, pr, qt);
   if (pr >= p.B * p.H) return;
   const int b = pr / p.H, head = pr - b * p.H;
-  const int len = min(max(p.lengths[b], 0), p.max_len);
+  const int raw_len = p.lengths[b];
+  debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
+  const int len = min(max(raw_len, 0), p.max_len);
   const int p0 = len - p.T;                    // position of chunk query 0
   const int q0 = qt * PF_Q, qw0 = q0 + 32 * w;
   const int q = qw0 + l32;                     // this lane's query

@@ -470,6 +470,29 @@ mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, co
                                     int32_t max_len, float softmax_scale, void* out, float* lse,
                                     const mla_decode_options* opts, hipStream_t stream);
 
+/* Debug checks of the device-resident integers (the preconditions the host
+ * cannot check without a synchronisation): lengths[b] within [0, max_len],
+ * every block-table entry a decode split reads (rows t < lengths[b]) within
+ * [0, cache_rows / block_size), every cache row that the append and the
+ * fp32 decode address within the cache arrays, and every append
+ * position within its sequence's capacity (seq_capacity, or max_blocks_per_seq
+ * * block_size when paged). In every build the kernels clamp such values
+ * (a length to [0, max_len], an out-of-range row to row 0, an out-of-range
+ * append is dropped), so they never access memory outside the arrays; the
+ * library built with MLA_DEBUG_CHECKS=1 also records each violation as a bit
+ * in a per-device error word: */
+#define MLA_DEBUG_LENGTH 1u     /* a length outside [0, max_len] */
+#define MLA_DEBUG_BLOCK 2u      /* a block-table entry or cache row outside the cache */
+#define MLA_DEBUG_POSITION 4u   /* an append position outside the capacity */
+
+/* Waits for `stream`, then stores the current device's error word in *word
+ * (a host pointer) and clears it. The word collects the violations of every
+ * call on that device since the last read (from any stream). Returns
+ * MLA_ERR_UNSUPPORTED (and *word = 0) from a library built without the
+ * checks, MLA_ERR_INVALID_ARG for a null `word`, MLA_ERR_HIP if a HIP call
+ * fails. Not for use under graph capture (it synchronizes). */
+mla_status mla_debug_errors(uint32_t* word, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

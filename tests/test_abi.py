@@ -260,3 +260,12 @@ def test_prefill_argument_errors():
     assert call(table=p, bs=32, mb=1) == 1                     # table shorter than max_len
     assert call(ws_bytes=1024) == 3
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == 3       # misaligned workspace
+
+
+def test_debug_errors_release_build(lib):
+    """The release build has no debug checks: a null word is rejected, any
+    other call reports MLA_ERR_UNSUPPORTED with a zero word (no HIP call)."""
+    assert lib.mla_debug_errors(None, None) == 1          # MLA_ERR_INVALID_ARG
+    word = ctypes.c_uint32(7)
+    assert lib.mla_debug_errors(ctypes.byref(word), None) == 2   # MLA_ERR_UNSUPPORTED
+    assert word.value == 0

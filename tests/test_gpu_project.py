@@ -192,7 +192,7 @@ def test_project_append_paged_fp8(gpu):
     assert not cache.cpu()[others].any()
 
 
-@pytest.mark.parametrize("cfg,cache_dtype", [(3, "bf16"), (2, "fp8")])
+@pytest.mark.parametrize("cfg,cache_dtype", [(3, "bf16"), (2, "fp8"), (1, "f32")])
 def test_decode_append_from_projection_equals_two_calls(gpu, cfg, cache_dtype):
     """mla_project, then a decode call whose append takes the projection's
     workspace (mla_append_args.projected), writes the same cache bytes and
@@ -203,9 +203,10 @@ def test_decode_append_from_projection_equals_two_calls(gpu, cfg, cache_dtype):
     lengths = torch.tensor([N, 200, 1, 64][:B], dtype=torch.int32)
     inp = synth.make_inputs(cfg, B=B, N=N, lengths=lengths, cache_dtype=cache_dtype,
                             paged=(cfg == 3)).to("cuda")
-    h, w_dkv, w_kr = [t.cuda() for t in synth.projection_inputs(66, B, "bf16", D)]
+    act = "f32" if cache_dtype == "f32" else "bf16"
+    h, w_dkv, w_kr = [t.cuda() for t in synth.projection_inputs(66, B, act, D)]
     pos = (inp.lengths - 1).contiguous()
-    print(f"[case] projected append in decode cfg={cfg} cache={cache_dtype}", flush=True)
+    print(f"[case] projected append in decode cfg={cfg} cache={cache_dtype} act={act}", flush=True)
 
     def fresh():
         return dataclasses.replace(inp, cache=inp.cache.clone(),
