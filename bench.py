@@ -25,6 +25,8 @@ Prints ONE JSON line (see the fields below). Options:
   --copy-calibration MIB   only run a plain device-to-device copy of MIB MiB
                            five times (the reference kernel that scales the
                            HBM byte counters of a profiler run) and exit
+  --length-aware           the decode calls cut the sequences by their actual
+                           lengths (mla_decode_options.length_aware)
   --clock SECONDS          after the timed steps, run the same steps for about
                            SECONDS more while a host thread samples the shader
                            clock through amdsmi (reported as "shader_clock")
@@ -84,6 +86,8 @@ def parse():
     ap.add_argument("--with-projection", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from HIP graphs (one per layer)")
+    ap.add_argument("--length-aware", action="store_true",
+                    help="decode calls use the length-aware split plan (bf16 cache)")
     ap.add_argument("--clock", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, run the same steps for about SECONDS more "
                          "while a host thread samples the GPU's shader clock (amdsmi)")
@@ -834,7 +838,7 @@ def main():
         c_new, k_new = synth.append_inputs(7000 + layer, B, inp.act, device=dev)
         pos = (inp.lengths - 1).to(dev)
         cdt = mla.dtype_code(inp.cache.dtype)
-        ws = torch.empty(mla.workspace_size(H, B, inp.max_len, act, cdt),
+        ws = torch.empty(mla.workspace_size(H, B, inp.max_len, act, cdt, 0, args.length_aware),
                          dtype=torch.uint8, device=dev)
         out = torch.empty((B, H, 128), dtype=inp.q_nope.dtype, device=dev)
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -873,7 +877,7 @@ def main():
                 mla.project(h, wd, wk, L["pws"], heads=H)
                 new_rows = (None, None, L["pos"], 10000.0, L["pws"], synth.D_MODEL)
             mla.decode_inputs(inp, out=L["out"], lse=L["lse"], workspace=L["ws"], events=events,
-                              append=new_rows)
+                              append=new_rows, length_aware=args.length_aware)
             return
         if args.separate_append:
             mla.cache_append(*new_rows, L["lat"], L["rope"], heads=H, scales=inp.scales,
@@ -882,7 +886,8 @@ def main():
             new_rows = None
         if "call" not in L:   # the step's decode call, marshalled once per layer
             L["call"] = mla.prepare_decode_inputs(inp, out=L["out"], lse=L["lse"],
-                                                  workspace=L["ws"], append=new_rows)
+                                                  workspace=L["ws"], append=new_rows,
+                                                  length_aware=args.length_aware)
         L["call"].run(events, stream)
 
     def step(i, events=None, stream=None):
@@ -916,6 +921,8 @@ def main():
     workload = FULL_STEP_WORKLOAD if full_step else WORKLOADS[cfg_key]
     if args.with_projection:
         workload += "_with_down_projection_d7168"
+    if args.length_aware:
+        workload += "_length_aware"
     kernel = decode_kernel_name(inp0.cache_dtype)
     traffic = measured_traffic(cfg_key, cache_bytes, kernel)
     dtype = {"f32": "f32", "bf16": "bf16", "fp8": "bf16+fp8cache"}[inp0.cache_dtype]

@@ -50,7 +50,7 @@ class AppendArgs(ctypes.Structure):
 
 
 class DecodeOptions(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    _fields_ = [("num_splits", ctypes.c_int32), ("length_aware", ctypes.c_int32),
                 ("attn_begin", ctypes.c_void_p), ("attn_end", ctypes.c_void_p),
                 ("append", ctypes.POINTER(AppendArgs))]
 
@@ -184,15 +184,17 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
-def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=None):
+def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=None,
+          length_aware: bool = False):
     """mla_decode_options for the call (None when every field is a default).
     `append` = (c_kv, k_pe, positions[, rope_theta]) appends those rows first;
     (None, None, positions, rope_theta, workspace, d_model) appends the rows of
     a preceding project() call whose workspace that is."""
-    if not num_splits and events is None and append is None:
+    if not num_splits and events is None and append is None and not length_aware:
         return None
     o = DecodeOptions()
     o.num_splits = num_splits
+    o.length_aware = 1 if length_aware else 0
     if events is not None:
         o.attn_begin, o.attn_end = events
     if append is not None:
@@ -211,10 +213,11 @@ def _opts(num_splits: int = 0, events: Optional[Tuple[int, int]] = None, append=
 
 
 def workspace_size(heads: int, batch: int, max_len: int, act_dtype: int, cache_dtype: int,
-                   num_splits: int = 0) -> int:
+                   num_splits: int = 0, length_aware: bool = False) -> int:
     d = dims(heads)
     return int(load().mla_decode_workspace_size(ctypes.byref(d), batch, max_len, act_dtype,
-                                                cache_dtype, _opts(num_splits)))
+                                                cache_dtype,
+                                                _opts(num_splits, length_aware=length_aware)))
 
 
 def split_cache(cache: torch.Tensor):
@@ -287,7 +290,7 @@ def project(hidden: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
 def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
             scales=None, seq_capacity=0, block_table=None, block_size=64, softmax_scale=None,
             out=None, lse=None, workspace=None, num_splits=0, events=None, append=None,
-            stream=None, want_lse=True):
+            stream=None, want_lse=True, length_aware=False):
     lib = load()
     B, H = q_nope.shape[0], q_nope.shape[1]
     d = dims(H)
@@ -301,9 +304,9 @@ def _decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     if workspace is None:
-        ws = workspace_size(H, B, max_len, act, cdt, num_splits)
+        ws = workspace_size(H, B, max_len, act, cdt, num_splits, length_aware)
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
-    opts = _opts(num_splits, events, append)
+    opts = _opts(num_splits, events, append, length_aware)
     head = [ctypes.byref(d), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), act,
             _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(scales), cdt,
             latent.shape[0]]
@@ -346,7 +349,7 @@ class PreparedDecode:
 def prepare_decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
                    out, lse, workspace, scales=None, seq_capacity=0, block_table=None,
                    block_size=64, softmax_scale=None, num_splits=0, append=None,
-                   stream=None) -> PreparedDecode:
+                   stream=None, length_aware=False) -> PreparedDecode:
     """A PreparedDecode for the call _decode would make with these arguments
     (out, lse and workspace given)."""
     lib = load()
@@ -356,6 +359,7 @@ def prepare_decode(paged: bool, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths,
     cdt = dtype_code(latent.dtype)
     opts = DecodeOptions()
     opts.num_splits = num_splits
+    opts.length_aware = 1 if length_aware else 0
     keep = [d, opts, q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, out, lse, workspace,
             scales, block_table]
     if append is not None:
@@ -397,7 +401,7 @@ def prepare_decode_inputs(inp, **kw) -> PreparedDecode:
 
 def decode_paged_noalloc(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_len, *,
                          block_table, block_size=64, scales=None, softmax_scale=None, out=None,
-                         lse=None, num_splits=0, append=None, stream=None):
+                         lse=None, num_splits=0, append=None, stream=None, length_aware=False):
     """mla_decode_paged_noalloc: as decode_paged, with the library's own
     scratch instead of a workspace. Returns (out, lse)."""
     lib = load()
@@ -414,7 +418,7 @@ def decode_paged_noalloc(q_nope, q_pe, w_uk, w_uv, latent, rope, lengths, max_le
         _ptr(scales), dtype_code(latent.dtype), latent.shape[0], _ptr(block_table),
         block_table.shape[1], block_size, _ptr(lengths), B, max_len,
         0.0 if softmax_scale is None else softmax_scale, _ptr(out), _ptr(lse),
-        _opts(num_splits, None, append), _stream(stream)))
+        _opts(num_splits, None, append, length_aware), _stream(stream)))
     return out, lse
 
 

@@ -47,6 +47,12 @@
 
 namespace mla {
 
+// One work item of a length-aware split plan: sequence b's token range
+// [t0, t1), written to its partial slot s (t0 >= t1: an empty sequence).
+struct __attribute__((aligned(16))) SplitItem {
+  int b, s, t0, t1;
+};
+
 struct DecodeParams {
   const bf16* q;               // [B, H, 576] absorbed query, pre-scaled
   const void* latent;          // cache latent array
@@ -61,7 +67,9 @@ struct DecodeParams {
   int block_size;
   const int32_t* lengths;      // [B]
   int max_len;
-  int B, H, S, tokens_per_split, G;
+  int B, H, S, tokens_per_split, G;   // S: partial slots per sequence
+  const SplitItem* items;      // length-aware plan: work item q of the launch (b < 0: none),
+  int nitems;                  // or nullptr: item q is split q % S of sequence q / S
   _Float16* part_o;            // [B, S, H, 512] normalised partial outputs / part_scale
   float* part_scale;           // [B, S, H] max |normalised output| of each partial row
   float* part_lse;             // [B, S, H] log2 sum-exp of each split
@@ -760,15 +768,26 @@ struct WorkItem {
 template <int NW>
 __device__ __forceinline__ bool work_item(const DecodeParams& p, int w, int l, WorkItem& wi) {
   int q, g;
-  xcd_map(blockIdx.x, p.G, (p.B * p.S + 7) / 8, q, g);
-  if (q >= p.B * p.S) return false;
-  wi.b = __builtin_amdgcn_readfirstlane(q / p.S);
-  wi.s = __builtin_amdgcn_readfirstlane(q - wi.b * p.S);
-  const int raw_len = __builtin_amdgcn_readfirstlane(p.lengths[wi.b]);
-  debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
-  const int len = min(max(raw_len, 0), p.max_len);
-  wi.t0 = wi.s * p.tokens_per_split;
-  wi.t1 = min(wi.t0 + p.tokens_per_split, len);
+  const int nq = p.items ? p.nitems : p.B * p.S;
+  xcd_map(blockIdx.x, p.G, (nq + 7) / 8, q, g);
+  if (q >= nq) return false;
+  if (p.items) {
+    // (the planning kernel clamped the lengths and checked them)
+    const SplitItem it = p.items[q];
+    if (__builtin_amdgcn_readfirstlane(it.b) < 0) return false;
+    wi.b = __builtin_amdgcn_readfirstlane(it.b);
+    wi.s = __builtin_amdgcn_readfirstlane(it.s);
+    wi.t0 = __builtin_amdgcn_readfirstlane(it.t0);
+    wi.t1 = __builtin_amdgcn_readfirstlane(it.t1);
+  } else {
+    wi.b = __builtin_amdgcn_readfirstlane(q / p.S);
+    wi.s = __builtin_amdgcn_readfirstlane(q - wi.b * p.S);
+    const int raw_len = __builtin_amdgcn_readfirstlane(p.lengths[wi.b]);
+    debug_flag(raw_len < 0 || raw_len > p.max_len, DBG_LENGTH);
+    const int len = min(max(raw_len, 0), p.max_len);
+    wi.t0 = wi.s * p.tokens_per_split;
+    wi.t1 = min(wi.t0 + p.tokens_per_split, len);
+  }
   wi.head = (g * NW + w) * 32 + (l & 31);
   wi.po = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + wi.head) * D_C + 4 * (l >> 5);
   wi.po_wave = p.part_o + (((int64_t)wi.b * p.S + wi.s) * p.H + (g * NW + w) * 32) * D_C;

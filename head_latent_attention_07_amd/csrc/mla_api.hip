@@ -17,6 +17,7 @@
 #include "kv_project.hpp"
 #include "prefill_mfma.hpp"
 #include "project_mfma.hpp"
+#include "split_plan.hpp"
 
 using namespace mla;
 
@@ -65,6 +66,11 @@ struct Plan {
   int TS = TILE;      // tokens per split (multiple of the 32-token tile)
   int NW = 4;         // waves per workgroup (bf16 path)
   int G = 1;          // head groups (bf16 path)
+  // length-aware plan (made on the device, split_plan.hpp): S is then the
+  // partial slots per sequence, nitems the attention launch's work items per
+  // head group, TS the longest split
+  bool length_aware = false;
+  int nitems = 0;
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -153,11 +159,24 @@ Plan decode_plan(int B, int H, int max_len, mla_dtype act, mla_dtype cdt,
   return pl;
 }
 
+// The length-aware plan (mla_decode_options.length_aware) on the bf16 cache:
+// as many work items as the default plan has splits (so the launch keeps its
+// workgroups), twice its split slots per sequence (split lengths from half
+// the default one up).
+void apply_length_aware(Plan& pl, int B, mla_dtype act, mla_dtype cdt,
+                        const mla_decode_options* opts) {
+  if (!opts || !opts->length_aware || act != MLA_BF16 || cdt != MLA_BF16 || pl.S < 2) return;
+  pl.length_aware = true;
+  pl.nitems = B * pl.S;
+  pl.S = 2 * pl.S;
+}
+
 // Workspace: absorbed queries [B, H, 576] (activation dtype), split partials
 // [B, S, H, 512] (fp32 on the fp32 path; fp16 relative to a per-row fp32
-// scale [B, S, H] otherwise), split lse [B, S, H] fp32.
+// scale [B, S, H] otherwise), split lse [B, S, H] fp32; with a length-aware
+// plan, its work items [nitems] and the splits per sequence [B].
 struct WsLayout {
-  size_t q_off, po_off, ps_off, pl_off, total;
+  size_t q_off, po_off, ps_off, pl_off, items_off, nsplit_off, total;
 };
 
 WsLayout ws_layout(int B, int H, const Plan& pl, mla_dtype act) {
@@ -169,7 +188,9 @@ WsLayout ws_layout(int B, int H, const Plan& pl, mla_dtype act) {
   w.po_off = align_up((size_t)B * H * D_QK * qe, 256);
   w.ps_off = align_up(w.po_off + rows * D_C * pe, 256);
   w.pl_off = align_up(w.ps_off + (act == MLA_F32 ? 0 : rows * 4), 256);
-  w.total = align_up(w.pl_off + rows * 4, 256);
+  w.items_off = align_up(w.pl_off + rows * 4, 256);
+  w.nsplit_off = align_up(w.items_off + (pl.length_aware ? (size_t)pl.nitems * sizeof(SplitItem) : 0), 256);
+  w.total = align_up(w.nsplit_off + (pl.length_aware ? (size_t)B * 4 : 0), 256);
   return w;
 }
 
@@ -379,6 +400,8 @@ DecodeParams decode_params(const bf16* q, const void* latent, int64_t ls, const 
   dp.S = pl.S;
   dp.tokens_per_split = pl.TS;
   dp.G = pl.G;
+  dp.items = nullptr;
+  dp.nitems = 0;
   dp.part_o = part_h;
   dp.part_scale = part_scale;
   dp.part_lse = part_lse;
@@ -391,7 +414,7 @@ DecodeParams decode_params(const bf16* q, const void* latent, int64_t ls, const 
 mla_status launch_attention(const DecodeParams& dp, const Plan& pl, bool fp8,
                             const mla_decode_options* opts, hipStream_t stream) {
   const bool mma = fp8 && use_fp8mma(MLA_FP8_E4M3, pl, dp.block_table, dp.block_size);
-  const int nq = dp.B * pl.S;
+  const int nq = pl.length_aware ? pl.nitems : dp.B * pl.S;
   const dim3 grid(ceil_div(nq, 8) * 8 * pl.G);
   hipEvent_t ev0 = opts ? opts->attn_begin : nullptr, ev1 = opts ? opts->attn_end : nullptr;
   auto launch = [&](auto kern, int threads) {
@@ -495,7 +518,8 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
       app.part_slices = project_plan(batch, a->d_model).S;
     }
   }
-  const Plan pl = decode_plan(B, H, max_len, act, cdt, block_table, block_size, opts);
+  Plan pl = decode_plan(B, H, max_len, act, cdt, block_table, block_size, opts);
+  apply_length_aware(pl, B, act, cdt, opts);
   const WsLayout wl = ws_layout(B, H, pl, act);
   if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255) != 0)
     return MLA_ERR_WORKSPACE;
@@ -558,23 +582,38 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
 
   bf16* q = (bf16*)(ws + wl.q_off);
   const int nbc = ceil_div(B, 32);
-  AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c};
-  const int absorb_blocks = ceil_div(H, 32) * 128;
+  AbsorbParams ap{(const bf16*)q_nope, (const bf16*)q_pe, (const bf16*)w_uk, q, B, H, nbc, c, {}};
+  DecodeParams dp = decode_params(q, latent, ls, rope, rs, scales, rows, seq_capacity,
+                                  block_table, max_blocks, block_size, lengths, max_len, B, H, pl,
+                                  part_h, part_scale, part_lse);
+  int32_t* nsplit = nullptr;
+  if (pl.length_aware) {
+    // one extra workgroup of the absorb launch makes the plan; it reads only
+    // the lengths, which the append of the same launch does not touch
+    SplitItem* items = (SplitItem*)(ws + wl.items_off);
+    nsplit = (int32_t*)(ws + wl.nsplit_off);
+    ap.plan = BalanceParams{lengths, B, max_len, pl.nitems, pl.S, pl.TS, items, nsplit};
+    dp.items = items;
+    dp.nitems = pl.nitems;
+  }
+  const int absorb_blocks = plan_blocks(pl.length_aware) + ceil_div(H, 32) * 128;
   if (do_append)
     hipLaunchKernelGGL(mla_absorb_append_kernel, dim3(append_blocks(B) + absorb_blocks), dim3(256),
                        0, stream, ap, app);
   else
     hipLaunchKernelGGL(mla_absorb_kernel, dim3(absorb_blocks), dim3(256), 0, stream, ap);
   MLA_TRY(launch_status());
-
-  const DecodeParams dp = decode_params(q, latent, ls, rope, rs, scales, rows, seq_capacity,
-                                        block_table, max_blocks, block_size, lengths, max_len, B,
-                                        H, pl, part_h, part_scale, part_lse);
   MLA_TRY(launch_attention(dp, pl, cdt == MLA_FP8_E4M3, opts, stream));
 
   CombineParams cp{part_h, part_scale, part_lse, (const bf16*)w_uv, (bf16*)out, lse, B, H, pl.S, nbc,
-                   pl.S, 1};
+                   pl.S, 1, nullptr};
   const dim3 cgrid(ceil_div(H, 8) * 8 * nbc);
+  if (pl.length_aware) {
+    // one level over the slots each sequence filled
+    cp.nsplit = nsplit;
+    hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
+    return launch_status();
+  }
   // the S <= 4 merge takes two workgroups per (head, 32 sequences), each for
   // half of the output columns, where one each would leave CUs idle
   const bool col_split = combine_col_split((int)cgrid.x);
@@ -657,9 +696,9 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t ma
                                  mla_dtype act, mla_dtype cdt, const mla_decode_options* opts) {
   if (!dims_supported(dims) || batch < 0 || max_len < 0) return 0;
   if (act != MLA_F32 && act != MLA_BF16) return 0;
-  (void)cdt;
   if (batch == 0) return 256;
-  const Plan pl = make_plan(batch, dims->heads, max_len, act, opts);
+  Plan pl = make_plan(batch, dims->heads, max_len, act, opts);
+  apply_length_aware(pl, batch, act, cdt, opts);
   return ws_layout(batch, dims->heads, pl, act).total;
 }
 
@@ -715,8 +754,9 @@ mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, co
       (int64_t)max_blocks * block_size < max_len || rows < block_size)
     return MLA_ERR_INVALID_ARG;
   // the scratch this call needs, before touching the device's copy
-  const size_t need = ws_layout(batch, dims->heads, make_plan(batch, dims->heads, max_len, act, opts),
-                                act).total;
+  Plan npl = make_plan(batch, dims->heads, max_len, act, opts);
+  apply_length_aware(npl, batch, act, cdt, opts);
+  const size_t need = ws_layout(batch, dims->heads, npl, act).total;
   if (need > kScratchBytes) return MLA_ERR_WORKSPACE;
   void* ws = nullptr;
   MLA_TRY(scratch_address(&ws));

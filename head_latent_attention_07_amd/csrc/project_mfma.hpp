@@ -19,6 +19,7 @@
 
 #include "append.hpp"
 #include "common.hpp"
+#include "split_plan.hpp"
 
 namespace mla {
 
@@ -55,7 +56,13 @@ struct AbsorbParams {
   bf16* q;             // [B, H, 576] in the operand layout of qop_index
   int B, H, nbc;       // nbc: unused (kept for the launch code)
   float c;             // softmax_scale * log2(e)
+  BalanceParams plan;  // a length-aware split plan to make in the same launch (or items == nullptr)
 };
+
+// Workgroups of the absorb launch before the absorb (and append) ones that
+// make the length-aware split plan: 8 (one working), so that the others keep
+// their XCD placement.
+__host__ __device__ constexpr int plan_blocks(bool planned) { return planned ? 8 : 0; }
 
 constexpr int AB_APITCH = D_N * 2 + 16;    // 272 B: 8 rows' 16-byte chunks hit distinct banks
 constexpr int AB_COLS = 128;               // output columns per workgroup
@@ -177,7 +184,12 @@ __device__ __forceinline__ void absorb_workgroup(const AbsorbParams& p, int x) {
 }
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
-  absorb_workgroup(p, blockIdx.x);
+  const int np = plan_blocks(p.plan.items != nullptr);
+  if ((int)blockIdx.x < np) {
+    if (blockIdx.x == 0) balance_plan(p.plan);
+    return;
+  }
+  absorb_workgroup(p, blockIdx.x - np);
 }
 
 // absorb and cache append in one launch (the absorb neither reads nor
@@ -189,13 +201,19 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(AbsorbParams p) {
 __host__ __device__ constexpr int append_blocks(int B) { return ((B + 3) / 4 + 7) / 8 * 8; }
 
 __global__ __launch_bounds__(256) void mla_absorb_append_kernel(AbsorbParams p, AppendParams a) {
+  const int np = plan_blocks(p.plan.items != nullptr);
+  if ((int)blockIdx.x < np) {
+    if (blockIdx.x == 0) balance_plan(p.plan);
+    return;
+  }
+  const int x = (int)blockIdx.x - np;
   const int na = append_blocks(p.B);
-  if ((int)blockIdx.x < na) {
-    const int b = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (x < na) {
+    const int b = x * 4 + (int)(threadIdx.x >> 6);
     if (b < p.B) append_row(a, b, threadIdx.x & 63);
     return;
   }
-  absorb_workgroup(p, blockIdx.x - na);
+  absorb_workgroup(p, x - na);
 }
 
 // ----------------------------------------------------------------------------
@@ -226,6 +244,8 @@ struct CombineParams {
   int B, H, S, nbc;       // S: partials merged per sequence; nbc: chunks of 32 sequences
   int sp, ss;             // split slots per sequence in the arrays; partial s is slot s * ss
                           // (mla_combine_kernel: sp == S, ss == 1)
+  const int32_t* nsplit;  // mla_combine_kernel: [B] partials of each sequence (slots
+                          // 0 .. nsplit[b] - 1; a length-aware plan), or nullptr: all S
 };
 
 constexpr int CB_THREADS = 512;       // 8 waves
@@ -265,12 +285,15 @@ __device__ __forceinline__ void lds_barrier() {
 // reads the last one again (unused, or weighted 0): the loads stay
 // unconditional, so the compiler's wait counts stay exact.
 __device__ __forceinline__ void cb_load(const CombineParams& p, const _Float16* const (&po)[CB_R],
-                                        const CbUnit& u, int d8, f16x8 (&v)[CB_R][CB_G]) {
+                                        const int (&nrow)[CB_R], const CbUnit& u, int d8,
+                                        f16x8 (&v)[CB_R][CB_G]) {
 #pragma unroll
   for (int k = 0; k < CB_G; ++k) {
-    const int64_t so = (int64_t)min(u.s0 + k, p.S - 1) * p.H * D_C + u.half * 256 + 8 * d8;
 #pragma unroll
-    for (int i = 0; i < CB_R; ++i) v[i][k] = *(const f16x8*)(po[i] + so);
+    for (int i = 0; i < CB_R; ++i) {
+      const int64_t so = (int64_t)min(u.s0 + k, nrow[i] - 1) * p.H * D_C + u.half * 256 + 8 * d8;
+      v[i][k] = *(const f16x8*)(po[i] + so);
+    }
   }
 }
 
@@ -297,19 +320,27 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
   const int wb = b0 + wr;
   const bool wrow = wb < p.B;
   const int64_t wrow0 = (int64_t)min(wb, p.B - 1) * S * p.H + head;
+  // partials of this role's sequence: the first wS slots (all S without a
+  // length-aware plan); later slots are never read (a load past them reads
+  // the last one again, with weight 0)
+  const int wS = p.nsplit ? min(max(p.nsplit[min(wb, p.B - 1)], 1), S) : S;
   float lv[CB_WJ], sv[CB_WJ];
 #pragma unroll
   for (int j = 0; j < CB_WJ; ++j) {
-    const int64_t ix = wrow0 + (int64_t)min(wp + 16 * j, S - 1) * p.H;
+    const int64_t ix = wrow0 + (int64_t)min(wp + 16 * j, wS - 1) * p.H;
     lv[j] = p.part_lse[ix];   // masked below, after the issue
     sv[j] = p.part_scale[ix];
   }
   // merge role: sequences rq + 16i, dims 8*d8 .. +7 of each half
   const int rq = tid >> 5, d8 = tid & 31;
   const _Float16* po[CB_R];
+  int nrow[CB_R];
 #pragma unroll
-  for (int i = 0; i < CB_R; ++i)
-    po[i] = p.part_o + ((int64_t)min(b0 + rq + 16 * i, p.B - 1) * S * p.H + head) * D_C;
+  for (int i = 0; i < CB_R; ++i) {
+    const int bi = min(b0 + rq + 16 * i, p.B - 1);
+    po[i] = p.part_o + ((int64_t)bi * S * p.H + head) * D_C;
+    nrow[i] = p.nsplit ? min(max(p.nsplit[bi], 1), S) : S;
+  }
   auto load_w = [&]() {
     const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
 #pragma unroll
@@ -332,13 +363,13 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
   ub.next(S);
   CbUnit un = ub;   // the next unit to load
   un.next(S);
-  cb_load(p, po, ua, d8, va);
+  cb_load(p, po, nrow, ua, d8, va);
   load_w();
-  cb_load(p, po, ub, d8, vb);
+  cb_load(p, po, nrow, ub, d8, vb);
 #pragma unroll
   for (int j = 0; j < CB_WJ; ++j) {   // (kept here: the issue above does not wait for these)
     asm volatile("" : "+v"(lv[j]));
-    lv[j] = (wrow && wp + 16 * j < S) ? lv[j] : -INFINITY;
+    lv[j] = (wrow && wp + 16 * j < wS) ? lv[j] : -INFINITY;
   }
   // 2. L = max over all splits, wsum = sum of 2^(lse - L), per sequence;
   //    the weight table of the first chunk.
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
 #pragma unroll
   for (int j = 0; j < CB_WJ; ++j) mx = fmaxf(mx, lv[j]);
   if (wrow)
-    for (int s = CB_CHUNK + wp; s < S; s += 16) mx = fmaxf(mx, p.part_lse[wrow0 + (int64_t)s * p.H]);
+    for (int s = CB_CHUNK + wp; s < wS; s += 16) mx = fmaxf(mx, p.part_lse[wrow0 + (int64_t)s * p.H]);
   red[0][wp][wr] = mx;
   lds_barrier();
   float L = -INFINITY;
@@ -357,7 +388,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
 #pragma unroll
     for (int j = 0; j < CB_WJ; ++j) sum += fast_exp2(lv[j] - L);
     if (wrow)
-      for (int s = CB_CHUNK + wp; s < S; s += 16)
+      for (int s = CB_CHUNK + wp; s < wS; s += 16)
         sum += fast_exp2(p.part_lse[wrow0 + (int64_t)s * p.H] - L);
   }
   red[1][wp][wr] = sum;
@@ -391,8 +422,8 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
 #pragma unroll
       for (int j = 0; j < CB_WJ; ++j) {
         const int s = u.c0 + wp + 16 * j;
-        const int64_t ix = wrow0 + (int64_t)min(s, S - 1) * p.H;
-        const float x = (wrow && s < S) ? p.part_lse[ix] : -INFINITY;
+        const int64_t ix = wrow0 + (int64_t)min(s, wS - 1) * p.H;
+        const float x = (wrow && s < wS) ? p.part_lse[ix] : -INFINITY;
         wts[wr * CB_CHUNK + wp + 16 * j] = (inv > 0.f) ? fast_exp2(x - L) * p.part_scale[ix] * inv : 0.f;
       }
       lds_barrier();
@@ -451,7 +482,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
       merge(ua, va, std::true_type{});
       ua = un;
       if (un.valid()) {
-        cb_load(p, po, un, d8, va);
+        cb_load(p, po, nrow, un, d8, va);
         un.next(S);
         ++issued;
       }
@@ -459,7 +490,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(CombineParams p
       merge(ub, vb, std::true_type{});
       ub = un;
       if (un.valid()) {
-        cb_load(p, po, un, d8, vb);
+        cb_load(p, po, nrow, un, d8, vb);
         un.next(S);
         ++issued;
       }

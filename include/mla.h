@@ -100,13 +100,24 @@ typedef struct mla_append_args {
 /* Optional tuning and instrumentation for the decode calls (pass NULL for the
  * defaults). Zero fields mean "choose automatically".
  *   num_splits     number of token ranges each sequence is cut into (split-KV).
+ *   length_aware   non-zero: on the bf16 cache, cut the sequences by their
+ *                  actual lengths (read on the device) instead of by max_len:
+ *                  the launch keeps its number of workgroups, and a split
+ *                  length between half and all of the default one is chosen so
+ *                  that the work items cover every sequence; long sequences
+ *                  then get more splits than short ones (up to twice the
+ *                  default count), so every workgroup has about the same
+ *                  number of tokens. For batches of unequal lengths. Costs
+ *                  one small planning launch; the workspace holds twice the
+ *                  default split slots (query mla_decode_workspace_size with
+ *                  the same options). Ignored for the f32 and fp8 caches.
  *   attn_begin/end if non-NULL, HIP events that record the start and the end
  *                  of the split attention kernel on `stream` (bf16 / fp8
  *                  path: taken from the kernel's own dispatch; f32 path:
  *                  recorded immediately before and after it), for timing it. */
 typedef struct {
   int32_t num_splits;
-  int32_t reserved0;
+  int32_t length_aware;
   hipEvent_t attn_begin;
   hipEvent_t attn_end;
   /* If non-NULL, the call first writes the new tokens' rows into the cache,

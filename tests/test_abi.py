@@ -86,6 +86,26 @@ def test_split_plan_through_workspace_size(B, H, N, act, cdt, forced, S):
     assert mla.workspace_size(H, B, N, act, cdt, forced) == _ws_for_splits(B, H, S, act)
 
 
+@pytest.mark.parametrize("B,H,N,cdt,S,la", [
+    (64, 128, 4096, mla.MLA_BF16, 4, True),         # twice the slots, 256 work items
+    (5, 128, 3001, mla.MLA_BF16, 47, True),         # 47 default splits of 64 tokens
+    (64, 128, 4096, mla.MLA_FP8_E4M3, 4, False),    # fp8 cache: the default plan
+    (300, 128, 4096, mla.MLA_BF16, 2, True),        # two splits (<= 2048 tokens each)
+    (300, 128, 2048, mla.MLA_BF16, 1, False),       # one split per sequence: the default plan
+])
+def test_length_aware_workspace(B, H, N, cdt, S, la):
+    """A length-aware plan asks for twice the default split slots plus its
+    work items (16 bytes each, one per default split) and the splits per
+    sequence (4 bytes each); where it does not apply, the default size."""
+    al = lambda x: (x + 255) // 256 * 256
+    got = mla.workspace_size(H, B, N, mla.MLA_BF16, cdt, 0, True)
+    assert mla.workspace_size(H, B, N, mla.MLA_BF16, cdt) == _ws_for_splits(B, H, S, mla.MLA_BF16)
+    if la:
+        assert got == al(al(_ws_for_splits(B, H, 2 * S, mla.MLA_BF16) + B * S * 16) + B * 4)
+    else:
+        assert got == _ws_for_splits(B, H, S, mla.MLA_BF16)
+
+
 def _decode_status(dims, act=mla.MLA_BF16, cdt=mla.MLA_BF16, batch=1, max_len=16, ptr=16,
                    ls=576, rs=576, rows=64, cap=16, ws=1 << 20, scale=0.07, scales=True):
     lib = mla.load()
