@@ -609,9 +609,19 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
                    pl.S, 1, nullptr};
   const dim3 cgrid(ceil_div(H, 8) * 8 * nbc);
   if (pl.length_aware) {
-    // one level over the slots each sequence filled
+    // one level over the slots each sequence filled: up to 8 per row in
+    // registers, more through the general merge
     cp.nsplit = nsplit;
-    hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
+    if (pl.S <= 2 * CB_G) {
+      if (combine_col_split((int)cgrid.x))
+        hipLaunchKernelGGL((mla_combine_s4_kernel<2, 2 * CB_G>), dim3(2 * cgrid.x),
+                           dim3(CB_THREADS), 0, stream, cp);
+      else
+        hipLaunchKernelGGL((mla_combine_s4_kernel<4, 2 * CB_G>), cgrid, dim3(CB_THREADS), 0,
+                           stream, cp);
+    } else {
+      hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
+    }
     return launch_status();
   }
   // the S <= 4 merge takes two workgroups per (head, 32 sequences), each for
@@ -619,10 +629,10 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   const bool col_split = combine_col_split((int)cgrid.x);
   auto launch_s4 = [&]() {
     if (col_split)
-      hipLaunchKernelGGL(mla_combine_s4_kernel<2>, dim3(2 * cgrid.x), dim3(CB_THREADS), 0, stream,
+      hipLaunchKernelGGL((mla_combine_s4_kernel<2, CB_G>), dim3(2 * cgrid.x), dim3(CB_THREADS), 0, stream,
                          cp);
     else
-      hipLaunchKernelGGL(mla_combine_s4_kernel<4>, cgrid, dim3(CB_THREADS), 0, stream, cp);
+      hipLaunchKernelGGL((mla_combine_s4_kernel<4, CB_G>), cgrid, dim3(CB_THREADS), 0, stream, cp);
   };
   if (pl.S <= CB_G) {
     launch_s4();

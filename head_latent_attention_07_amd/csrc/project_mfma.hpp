@@ -616,7 +616,7 @@ void mla_merge_splits_kernel(MergeSplitsParams p) {
 // LDS each, twice the workgroups where one per (head, 32 sequences) would
 // leave CUs idle; both merge the same partials, the second from L2).
 // ----------------------------------------------------------------------------
-template <int NCB>
+template <int NCB, int G>
 __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParams p) {
   constexpr int NCS = 4 / NCB;         // workgroups per (head, 32 sequences)
   constexpr int ROWB = 64 * NCB;       // bytes of this workgroup's slice of a W_UV row
@@ -636,23 +636,27 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
     head = __builtin_amdgcn_readfirstlane((r2 / NCS) * 8 + q_lo);
     if (head >= p.H) return;
   }
-  const int S = p.S, b = bc * 32 + l32;
+  const int b = bc * 32 + l32;
   const bool brow = b < p.B;
+  // partials of this lane's sequence: p.S, or its own count (a length-aware
+  // plan; later slots are never read: a load past them reads the last one
+  // again, weighted 0)
+  const int S = p.nsplit ? min(max(p.nsplit[min(b, p.B - 1)], 1), p.S) : p.S;
   const int64_t row0 = (int64_t)min(b, p.B - 1) * p.sp * p.H + head;   // (b, split 0, head)
   const int64_t sstep = (int64_t)p.ss * p.H;                            // split s: + s * sstep
   // loads: lse and scale, half-0 partials, this wave's W_UV rows, half-1
   // partials (v[half][step][split]: dims 256 half + 32 w + 16 step + 8 h)
-  float lv[CB_G], sv[CB_G];
+  float lv[G], sv[G];
 #pragma unroll
-  for (int s = 0; s < CB_G; ++s) {
+  for (int s = 0; s < G; ++s) {
     const int64_t ix = row0 + min(s, S - 1) * sstep;
     lv[s] = p.part_lse[ix];
     sv[s] = p.part_scale[ix];
   }
-  f16x8 v[2][2][CB_G];
+  f16x8 v[2][2][G];
   auto load_half = [&](int hf) {
 #pragma unroll
-    for (int s = 0; s < CB_G; ++s)
+    for (int s = 0; s < G; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         v[hf][t][s] = *(const f16x8*)(p.part_o + (row0 + min(s, S - 1) * sstep) * D_C +
@@ -678,20 +682,20 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
   // weights of this lane's sequence
   float L = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < CB_G; ++s) {
+  for (int s = 0; s < G; ++s) {
     lv[s] = (brow && s < S) ? lv[s] : -INFINITY;
     L = fmaxf(L, lv[s]);
   }
-  float e[CB_G], wsum = 0.f;
+  float e[G], wsum = 0.f;
 #pragma unroll
-  for (int s = 0; s < CB_G; ++s) {
+  for (int s = 0; s < G; ++s) {
     e[s] = (L > -INFINITY) ? fast_exp2(lv[s] - L) : 0.f;
     wsum += e[s];
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  float wt[CB_G];
+  float wt[G];
 #pragma unroll
-  for (int s = 0; s < CB_G; ++s) wt[s] = e[s] * sv[s] * inv;
+  for (int s = 0; s < G; ++s) wt[s] = e[s] * sv[s] * inv;
   if (cs == 0 && w == 0 && h == 0 && brow && p.lse)
     p.lse[(int64_t)b * p.H + head] = (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
 
@@ -706,7 +710,7 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
     for (int t = 0; t < 2; ++t) {
       float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < CB_G; ++s)
+      for (int s = 0; s < G; ++s)
 #pragma unroll
         for (int k = 0; k < 8; ++k) m[k] += wt[s] * (float)v[hf][t][s][k];
 #pragma unroll
@@ -716,7 +720,10 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
     // follow them, may be pending
     if (hf == 0) {
       __builtin_amdgcn_sched_barrier(0);   // the half-0 merge stays ahead of the wait
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if constexpr (G == 4)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
