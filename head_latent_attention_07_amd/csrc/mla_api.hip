@@ -134,6 +134,28 @@ bool combine_col_split(int workgroups) {
   return workgroups < device_cu_count();
 }
 
+// Merge + W_UV of at most G partials per row: mla_combine_s4_kernel (a lane
+// per sequence) for up to 4, mla_combine_rows_kernel (whole partial rows per
+// load; it issues no load past a row's own partial count) for up to 8
+// (measured: equal at 4 partials, 5 us faster at 8 slots holding 2-6);
+// MLA_SHORT_MERGE=lanes or rows overrides. Two workgroups per (head, 32
+// sequences), each for half of the output columns, where one each would
+// leave CUs idle.
+template <int G>
+void launch_short_merge(const CombineParams& cp, dim3 cgrid, hipStream_t stream) {
+  const bool col_split = combine_col_split((int)cgrid.x);
+  const char* e = std::getenv("MLA_SHORT_MERGE");
+  const bool lanes = e ? std::strcmp(e, "lanes") == 0 : G <= CB_G;
+  const dim3 grid(col_split ? 2 * cgrid.x : cgrid.x), block(CB_THREADS);
+  if (lanes) {
+    if (col_split) hipLaunchKernelGGL((mla_combine_s4_kernel<2, G>), grid, block, 0, stream, cp);
+    else hipLaunchKernelGGL((mla_combine_s4_kernel<4, G>), grid, block, 0, stream, cp);
+  } else {
+    if (col_split) hipLaunchKernelGGL((mla_combine_rows_kernel<2, G>), grid, block, 0, stream, cp);
+    else hipLaunchKernelGGL((mla_combine_rows_kernel<4, G>), grid, block, 0, stream, cp);
+  }
+}
+
 // The fp8 cache goes to the fp8 matrix cores (decode_fp8mma.hpp) when its
 // layout fits that kernel: four waves of 32 heads per workgroup, splits of
 // whole 64-token tiles (at most 32 of them), and page blocks holding whole
@@ -613,27 +635,13 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
     // registers, more through the general merge
     cp.nsplit = nsplit;
     if (pl.S <= 2 * CB_G) {
-      if (combine_col_split((int)cgrid.x))
-        hipLaunchKernelGGL((mla_combine_s4_kernel<2, 2 * CB_G>), dim3(2 * cgrid.x),
-                           dim3(CB_THREADS), 0, stream, cp);
-      else
-        hipLaunchKernelGGL((mla_combine_s4_kernel<4, 2 * CB_G>), cgrid, dim3(CB_THREADS), 0,
-                           stream, cp);
+      launch_short_merge<2 * CB_G>(cp, cgrid, stream);
     } else {
       hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(CB_THREADS), 0, stream, cp);
     }
     return launch_status();
   }
-  // the S <= 4 merge takes two workgroups per (head, 32 sequences), each for
-  // half of the output columns, where one each would leave CUs idle
-  const bool col_split = combine_col_split((int)cgrid.x);
-  auto launch_s4 = [&]() {
-    if (col_split)
-      hipLaunchKernelGGL((mla_combine_s4_kernel<2, CB_G>), dim3(2 * cgrid.x), dim3(CB_THREADS), 0, stream,
-                         cp);
-    else
-      hipLaunchKernelGGL((mla_combine_s4_kernel<4, CB_G>), cgrid, dim3(CB_THREADS), 0, stream, cp);
-  };
+  auto launch_s4 = [&]() { launch_short_merge<CB_G>(cp, cgrid, stream); };
   if (pl.S <= CB_G) {
     launch_s4();
     return launch_status();

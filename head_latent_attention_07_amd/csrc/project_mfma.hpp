@@ -767,4 +767,148 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_s4_kernel(CombineParam
   }
 }
 
+// ----------------------------------------------------------------------------
+// merge + W_UV for at most G partials per row, reading whole partial rows:
+// the grid and the W_UV staging of mla_combine_s4_kernel, but wave w merges
+// sequences 4w .. 4w+3 of the workgroup's 32, one 1 KB partial row per load
+// instruction (lane l: dims 8l .. 8l+7), where the lane-per-sequence layout
+// of mla_combine_s4_kernel makes each load touch 32 rows 32 bytes at a time
+// (four times the cache lines per instruction, and the memory pipeline, not
+// HBM, then bounds that merge). The merged rows go to LDS as bf16 (16-byte
+// chunks XOR-swizzled by the row, so the MFMA A reads of 32 rows hit
+// distinct banks), and waves 0 .. NCB-1 multiply them by the W_UV columns
+// of their 32-column block over the whole 512-long contraction. A row's
+// partial count is the plan's (p.nsplit, wave-uniform here) or p.S; the
+// loads past it are not issued.
+// ----------------------------------------------------------------------------
+template <int NCB, int G>
+__global__ __launch_bounds__(CB_THREADS) void mla_combine_rows_kernel(CombineParams p) {
+  constexpr int NCS = 4 / NCB;         // workgroups per (head, 32 sequences)
+  constexpr int ROWB = 64 * NCB;       // bytes of this workgroup's slice of a W_UV row
+  constexpr int RPI = 1024 / ROWB;     // slice rows per 1 KB direct load
+  constexpr int NI = 64 / RPI;         // direct loads per wave (its 64 rows)
+  static_assert(4 * G <= 64, "one lane per (sequence, partial) of a wave");
+  __shared__ __attribute__((aligned(1024))) char w_lds[D_C * ROWB];   // 128 or 64 KB
+  __shared__ __attribute__((aligned(1024))) char a_lds[32 * D_C * 2];  // 32 merged rows, bf16
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = l >> 5, l32 = l & 31, jj = l & 15, g16 = l >> 4;
+  int head, bc, cs;
+  {
+    const int x = blockIdx.x;
+    const int q_lo = x & 7, rest = x >> 3;
+    bc = __builtin_amdgcn_readfirstlane(rest % p.nbc);
+    const int r2 = rest / p.nbc;
+    cs = __builtin_amdgcn_readfirstlane(r2 % NCS);
+    head = __builtin_amdgcn_readfirstlane((r2 / NCS) * 8 + q_lo);
+    if (head >= p.H) return;
+  }
+  const int b_lo = bc * 32 + 4 * w;   // this wave's first sequence
+  // partials per sequence (wave-uniform) and the rows of partial 0
+  int nb[4];
+  int64_t row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = min(b_lo + i, p.B - 1);
+    nb[i] = p.nsplit ? min(max(p.nsplit[b], 1), p.S) : p.S;
+    row[i] = (int64_t)b * p.sp * p.H + head;
+  }
+  const int64_t sstep = (int64_t)p.ss * p.H;
+  // lse and factor of (sequence i, partial s) in lane i G + s
+  float lse_l = -INFINITY, scl_l = 0.f;
+  if (l < 4 * G) {
+    const int i = l / G, s = l % G;
+    int n = nb[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) n = (i == k) ? nb[k] : n;
+    int64_t r0 = row[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) r0 = (i == k) ? row[k] : r0;
+    const int64_t ix = r0 + min(s, n - 1) * sstep;
+    const float x = p.part_lse[ix];
+    scl_l = p.part_scale[ix];
+    lse_l = (s < n && b_lo + i < p.B) ? x : -INFINITY;
+  }
+  // whole partial rows (the loads past a row's count are not issued: the
+  // count is uniform over the wave)
+  f16x8 v[4][G];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      v[i][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (s < nb[i]) v[i][s] = *(const f16x8*)(p.part_o + (row[i] + s * sstep) * D_C + 8 * l);
+    }
+  {
+    // rows 256 hf + 32 w .. +31 of W_UV[h], columns 32 NCB cs .. +32 NCB - 1
+    // (ROWB bytes of each 256-byte row), to the same rows of the LDS copy
+    // (rows ROWB apart), RPI rows per 1 KB load
+    const __amdgpu_buffer_rsrc_t rs = proj_rsrc(p.w_uv + (int64_t)head * D_C * D_V, D_C * D_V * 2);
+    const int vo = 256 * (l / (ROWB / 16)) + 16 * (l % (ROWB / 16));
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r0 = 256 * (k / (NI / 2)) + 32 * w + RPI * (k % (NI / 2));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(w_lds + r0 * ROWB), 16, vo,
+          r0 * 256 + cs * ROWB, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  }
+  // weights of each sequence's partials: 2^(lse_s - L) * factor_s / sum
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lv[G], L = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      lv[s] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                            __builtin_bit_cast(int, lse_l), i * G + s));
+      L = fmaxf(L, lv[s]);
+    }
+    float e[G], wsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      e[s] = (L > -INFINITY) ? fast_exp2(lv[s] - L) : 0.f;
+      wsum += e[s];
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, scl_l), i * G + s));
+      const float wt = e[s] * sc * inv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m[k] += wt * (float)v[i][s][k];
+    }
+    const int r = 4 * w + i;   // row of the merged block
+    bf16x8 pk;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pk[k] = (bf16)m[k];
+    *(bf16x8*)(a_lds + r * (D_C * 2) + 16 * (l ^ (r & 15))) = pk;
+    if (cs == 0 && l == 0 && b_lo + i < p.B && p.lse)
+      p.lse[(int64_t)(b_lo + i) * p.H + head] =
+          (L > -INFINITY) ? (L + __builtin_log2f(wsum)) * LN2 : -INFINITY;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's W_UV rows landed
+  lds_barrier();
+  if (w >= NCB) return;
+  // output columns 32 NCB cs + 32 w .. +31: two chains (even, odd k-steps)
+  const int colb = 32 * w + 16 * (g16 & 1) + 4 * (jj & 3);   // B-operand column base
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < D_C / 16; ++ks) {
+    const int c = 2 * ks + h;   // 16-byte chunk of the row: dims 16 ks + 8 h .. +7
+    const bf16x8 a = *(const bf16x8*)(a_lds + l32 * (D_C * 2) + 16 * (c ^ (l32 & 15)));
+    const int ra = 16 * ks + 8 * h + (jj >> 2);
+    const bf16x8 bop = tr_read_8(w_lds + ra * ROWB + 2 * colb, w_lds + (ra + 4) * ROWB + 2 * colb);
+    acc[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[ks & 1], 0, 0, 0);
+  }
+  const int n = 32 * NCB * cs + 32 * w + l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int bb = bc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (bb < p.B) p.out[((int64_t)bb * p.H + head) * D_V + n] = (bf16)(acc[0][r] + acc[1][r]);
+  }
+}
+
 }  // namespace mla
