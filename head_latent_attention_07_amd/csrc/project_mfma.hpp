@@ -804,13 +804,14 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_rows_kernel(CombinePar
     if (head >= p.H) return;
   }
   const int b_lo = bc * 32 + 4 * w;   // this wave's first sequence
-  // partials per sequence (wave-uniform) and the rows of partial 0
+  // partials per sequence (wave-uniform; 0 past the batch) and the rows of
+  // partial 0
   int nb[4];
   int64_t row[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = min(b_lo + i, p.B - 1);
-    nb[i] = p.nsplit ? min(max(p.nsplit[b], 1), p.S) : p.S;
+    nb[i] = b_lo + i >= p.B ? 0 : p.nsplit ? min(max(p.nsplit[b], 1), p.S) : p.S;
     row[i] = (int64_t)b * p.sp * p.H + head;
   }
   const int64_t sstep = (int64_t)p.ss * p.H;
@@ -824,10 +825,10 @@ __global__ __launch_bounds__(CB_THREADS) void mla_combine_rows_kernel(CombinePar
     int64_t r0 = row[0];
 #pragma unroll
     for (int k = 1; k < 4; ++k) r0 = (i == k) ? row[k] : r0;
-    const int64_t ix = r0 + min(s, n - 1) * sstep;
+    const int64_t ix = r0 + min(s, max(n, 1) - 1) * sstep;
     const float x = p.part_lse[ix];
     scl_l = p.part_scale[ix];
-    lse_l = (s < n && b_lo + i < p.B) ? x : -INFINITY;
+    lse_l = (s < n) ? x : -INFINITY;
   }
   // whole partial rows (the loads past a row's count are not issued: the
   // count is uniform over the wave)
