@@ -111,3 +111,13 @@ def test_config3_full_every_row(gpu):
     print(f"[result] config 3 length-aware all rows: rel err {err:.3e}, lse {lerr:.3e}",
           flush=True)
     assert err <= TOL["bf16"] and lerr <= LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("H", [32, 64, 256])
+def test_head_counts(gpu, H):
+    """One wave (H=32), two waves (H=64) per workgroup, and two head groups
+    per sequence (H=256): the work items are shared by the head groups."""
+    lengths = torch.tensor([1500, 40, 700, 1], dtype=torch.int32)
+    inp = synth.make_inputs(3, B=4, N=1500, H=H, lengths=lengths, paged=True)
+    check(gpu, inp, heads=list(range(0, H, 7)))
+

@@ -57,3 +57,22 @@ def test_noalloc_fp8_then_smaller(gpu):
 def test_noalloc_full_benchmark_size(gpu):
     """The benchmark's workload (B=64, N=4096, paged bf16) fits the scratch."""
     compare(gpu, "3u", 64, 4096, torch.full((64,), 4096, dtype=torch.int32), append=True, seed=3)
+
+
+def test_noalloc_length_aware_matches_workspace_call(gpu):
+    """mla_decode_paged_noalloc with the length-aware plan (its items and
+    split counts in the library's scratch) gives the bits of the call with a
+    workspace."""
+    lengths = torch.tensor([3000, 64, 1200, 5, 2999], dtype=torch.int32)
+    inp = synth.make_inputs(3, B=5, N=3000, lengths=lengths, paged=True).to("cuda")
+    print("[case] length-aware noalloc vs workspace", flush=True)
+    a_out, a_lse = gpu.decode_inputs(inp, length_aware=True)
+    lat, rope = gpu.split_cache(inp.cache)
+    b_out, b_lse = gpu.decode_paged_noalloc(inp.q_nope, inp.q_pe, inp.w_uk, inp.w_uv, lat, rope,
+                                            inp.lengths, inp.max_len,
+                                            block_table=inp.block_table,
+                                            block_size=inp.block_size, softmax_scale=inp.scale,
+                                            length_aware=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.uint8), b_out.view(torch.uint8))
+    assert torch.equal(a_lse, b_lse)
