@@ -57,7 +57,7 @@ constexpr int F8_LAT_BYTES = F8_TILE * D_C;               // 32 KB of latent cod
 constexpr int F8_TILE_BYTES = F8_LAT_BYTES + F8_TILE * D_R;   // + 4 KB of RoPE codes
 constexpr int F8_KS = D_QK / 64;                          // 9 contraction steps of 64
 constexpr int F8_QLO_WAVE = F8_KS * 2048;                 // lo query parts of a wave (18 KB)
-constexpr int F8_MAX_TILES = 32;                          // 2048 tokens per split
+constexpr int F8_MAX_TILES = 64;                          // 4096 tokens per split (one tile row per lane)
 constexpr uint32_t F8_UNIT_SCALE = 0x7F7F7F7Fu;           // E8M0 127 = 2^0 in every byte
 
 __device__ __forceinline__ int f8_lat_swz(int t) { return ((t & 7) << 1) | ((t >> 4) & 1); }
@@ -136,9 +136,14 @@ void mla_decode_fp8mma_kernel(DecodeParams p) {
   constexpr int NW = 4, NT = 256;
   __shared__ __attribute__((aligned(1024))) char bufs[2 * F8_TILE_BYTES];     // 72 KB
   __shared__ __attribute__((aligned(1024))) char qlo_all[NW * F8_QLO_WAVE];   // 72 KB
-  __shared__ __attribute__((aligned(16))) float scl_all[F8_MAX_TILES * F8_TILE];   // 8 KB
-  __shared__ int blk_tab[MAX_SPLIT_BLOCKS];
-  __shared__ int flags[NW];
+  __shared__ __attribute__((aligned(16))) float scl_all[F8_MAX_TILES * F8_TILE];   // 16 KB
+  // (160 KB in all: the split's block table borrows tile buffer 1 in the
+  // prologue, before that buffer's first load; the overflow flags borrow the
+  // end of tile buffer 0 after the last tile, past write_partial's staging)
+  int* const blk_tab = (int*)(bufs + F8_TILE_BYTES);
+  int* const flags = (int*)(bufs + F8_TILE_BYTES - 64);
+  static_assert(2 * PART_SCR_BYTES <= F8_TILE_BYTES - 64, "flags past the partial staging");
+  static_assert(MAX_SPLIT_BLOCKS * 4 <= F8_TILE_BYTES, "block table fits in a tile buffer");
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 5, r32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

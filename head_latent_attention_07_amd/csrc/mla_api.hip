@@ -167,15 +167,23 @@ bool use_fp8mma(mla_dtype cdt, const Plan& pl, const int32_t* block_table, int b
   return !(e && std::strcmp(e, "widen") == 0);
 }
 
-// Plan of a decode call: make_plan, with the splits rounded to whole 64-token
-// tiles for the fp8 matrix-core kernel (never more splits than make_plan's,
-// so the workspace make_plan sizes is enough).
+// Plan of a decode call: make_plan; for the fp8 matrix-core kernel, splits
+// of whole 64-token tiles, as long as 64 of them (that kernel keeps one tile
+// row per lane of 64-token tiles, where the bf16 kernel's tiles hold 32), so
+// a sequence needs no more splits than filling the CUs asks for (never more
+// than make_plan's, so the workspace make_plan sizes is enough).
 Plan decode_plan(int B, int H, int max_len, mla_dtype act, mla_dtype cdt,
                  const int32_t* block_table, int block_size, const mla_decode_options* opts) {
   Plan pl = make_plan(B, H, max_len, act, opts);
   if (act != MLA_F32 && use_fp8mma(cdt, pl, block_table, block_size)) {
     const int len = max_len > 0 ? max_len : 1;
-    pl.TS = std::min(ceil_div(pl.TS, F8_TILE) * F8_TILE, F8_MAX_TILES * F8_TILE);
+    const bool forced = (opts && opts->num_splits > 0) || env_int("MLA_SPLITS") > 0;
+    int S = pl.S;
+    if (!forced) {
+      const int fill = std::min(ceil_div(device_cu_count(), (int64_t)B * pl.G), ceil_div(len, 64));
+      S = std::min(S, std::max(fill, ceil_div(len, F8_MAX_TILES * F8_TILE)));
+    }
+    pl.TS = std::min(ceil_div(ceil_div(len, S), F8_TILE) * F8_TILE, F8_MAX_TILES * F8_TILE);
     pl.S = ceil_div(len, pl.TS);
   }
   return pl;
