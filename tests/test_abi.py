@@ -73,7 +73,7 @@ def _ws_for_splits(B, H, S, act):
     (1, 128, 4096, mla.MLA_BF16, mla.MLA_BF16, 0, 64),      # splits down to 64 tokens
     (4, 128, 131072, mla.MLA_BF16, mla.MLA_BF16, 0, 64),    # 2048 tokens per split
     (32, 128, 32768, mla.MLA_BF16, mla.MLA_BF16, 0, 16),    # 8 by CUs, but <= 2048 tokens per split
-    (32, 128, 32768, mla.MLA_BF16, mla.MLA_FP8_E4M3, 0, 16),  # fp8 matrix cores: <= 32 tiles of 64
+    (32, 128, 32768, mla.MLA_BF16, mla.MLA_FP8_E4M3, 0, 16),  # sized for 16; the fp8 kernel runs 8
     (32, 128, 8192, mla.MLA_BF16, mla.MLA_BF16, 0, 8),      # one workgroup per CU
     (1, 128, 100, mla.MLA_BF16, mla.MLA_BF16, 0, 2),
     (2, 128, 1024, mla.MLA_BF16, mla.MLA_BF16, 7, 7),       # forced: 160 tokens per split
