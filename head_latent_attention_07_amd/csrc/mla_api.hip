@@ -44,6 +44,11 @@ int env_int(const char* name) {
   return s ? std::atoi(s) : 0;
 }
 
+int env_int_or(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  return s ? std::atoi(s) : dflt;
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool dims_supported(const mla_dims* d) {
@@ -110,8 +115,9 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   return pl;
 }
 
-// Rows of more than 4 splits are merged in one level (mla_combine_kernel)
-// or two (mla_merge_splits_kernel folds each row's splits into groups,
+// Rows of more than 8 splits (5-8 take the row merge with 8 slots, see
+// run_decode) are merged in one level (mla_combine_kernel) or two
+// (mla_merge_splits_kernel folds each row's splits into groups,
 // mla_combine_s4_kernel merges the groups and applies W_UV). Measured: two
 // levels win above 16 splits (2 groups), and from 5 splits when there are
 // at most 32 sequences (1 group; mla_combine_kernel then has only one
@@ -652,6 +658,13 @@ mla_status run_decode(const mla_dims* dims, const void* q_nope, const void* q_pe
   auto launch_s4 = [&]() { launch_short_merge<CB_G>(cp, cgrid, stream); };
   if (pl.S <= CB_G) {
     launch_s4();
+    return launch_status();
+  }
+  // 5-8 partials per row: one launch of the row merge with 8 slots (which
+  // issues no load past the row's count); MLA_MERGE8=0, or a merge grouping
+  // asked for with MLA_MERGE_GROUPS, selects the paths below
+  if (pl.S <= 2 * CB_G && env_int_or("MLA_MERGE8", 1) != 0 && !std::getenv("MLA_MERGE_GROUPS")) {
+    launch_short_merge<2 * CB_G>(cp, cgrid, stream);
     return launch_status();
   }
   const int ng = merge_groups(pl.S, nbc);

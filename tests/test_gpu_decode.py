@@ -64,7 +64,7 @@ def test_bf16_paged_small(gpu):
     run_and_compare(gpu, inp, "bf16")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 32])
+@pytest.mark.parametrize("splits", [1, 2, 5, 7, 8, 32])
 def test_split_invariance(gpu, splits):
     """The split-KV merge is an exact re-association of the softmax: every
     forced split count agrees with the oracle."""
@@ -95,6 +95,19 @@ def test_merge_levels(gpu, monkeypatch, N, splits, groups):
     lengths = torch.tensor([N, N - 700, 33], dtype=torch.int32)
     inp = synth.make_inputs(2, B=3, N=N, lengths=lengths)
     run_and_compare(gpu, inp, "bf16", num_splits=splits)
+
+
+@pytest.mark.parametrize("merge8", ["1", "0"])
+@pytest.mark.parametrize("splits", [5, 8])
+def test_merge_eight_slots(gpu, monkeypatch, merge8, splits):
+    """5-8 partials per row: the row merge with 8 slots in one launch
+    (MLA_MERGE8=1, the default) or the general paths (0), for 40 sequences
+    (a full chunk of 32 and a chunk of 8) including short ones whose later
+    splits are empty."""
+    monkeypatch.setenv("MLA_MERGE8", merge8)
+    lengths = torch.tensor([(97 * i) % 700 + 1 for i in range(39)] + [700], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=40, N=700, lengths=lengths)
+    run_and_compare(gpu, inp, "bf16", batch_ids=[0, 5, 31, 32, 38, 39], num_splits=splits)
 
 
 @pytest.mark.parametrize("cols", [1, 2])
