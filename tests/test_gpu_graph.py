@@ -47,15 +47,17 @@ def capture_and_replay(call, outputs, between):
 
 
 def decode_case(gpu, cfg, B, N, lengths, paged, cache_dtype=None, num_splits=0, append=False,
-                seed=0):
+                seed=0, length_aware=False, other_lengths=None):
     print(f"[case] graph decode cfg={cfg} B={B} N={N} paged={paged} cache={cache_dtype} "
-          f"splits={num_splits} append={append}", flush=True)
+          f"splits={num_splits} append={append} length_aware={length_aware}", flush=True)
     inp = synth.make_inputs(cfg, B=B, N=N, lengths=lengths, paged=paged,
                             cache_dtype=cache_dtype).to("cuda")
-    other = synth.make_inputs(cfg, B=B, N=N, lengths=lengths, paged=paged,
-                              cache_dtype=cache_dtype, layer=1).to("cuda")
+    other = synth.make_inputs(cfg, B=B, N=N,
+                              lengths=lengths if other_lengths is None else other_lengths,
+                              paged=paged, cache_dtype=cache_dtype, layer=1).to("cuda")
     act, cdt = gpu.dtype_code(inp.q_nope.dtype), gpu.dtype_code(inp.cache.dtype)
-    ws = torch.empty(gpu.workspace_size(inp.H, B, inp.max_len, act, cdt, num_splits),
+    ws = torch.empty(gpu.workspace_size(inp.H, B, max(inp.max_len, other.max_len), act, cdt,
+                                        num_splits, length_aware),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((B, inp.H, 128), dtype=inp.q_nope.dtype, device="cuda")
     lse = torch.empty((B, inp.H), dtype=torch.float32, device="cuda")
@@ -65,18 +67,30 @@ def decode_case(gpu, cfg, B, N, lengths, paged, cache_dtype=None, num_splits=0, 
         app = (c_new, k_new, (inp.lengths - 1).to("cuda"))
 
     def call():
-        gpu.decode_inputs(inp, out=out, lse=lse, workspace=ws, num_splits=num_splits, append=app)
+        gpu.decode_inputs(inp, out=out, lse=lse, workspace=ws, num_splits=num_splits, append=app,
+                          length_aware=length_aware)
 
     call()
     torch.cuda.synchronize()
     capture_and_replay(call, [out, lse],
-                       lambda: gpu.decode_inputs(other, workspace=ws, num_splits=num_splits))
+                       lambda: gpu.decode_inputs(other, workspace=ws, num_splits=num_splits,
+                                                 length_aware=length_aware))
 
 
 def test_graph_decode_bf16_paged_append(gpu):
     """bf16, paged, ragged lengths, the new rows appended in the same call."""
     lengths = torch.tensor([1000, 1, 300, 777, 64, 65, 999, 512], dtype=torch.int32)
     decode_case(gpu, 3, 8, 1000, lengths, paged=True, append=True, seed=1)
+
+
+def test_graph_decode_length_aware(gpu):
+    """The length-aware plan (made in the absorb launch, in the workspace):
+    between replays an eager call plans other lengths into the same
+    workspace, and every replay re-plans its own."""
+    lengths = torch.tensor([1000, 1, 300, 777, 64, 65, 999, 512], dtype=torch.int32)
+    other = torch.tensor([40, 1000, 1000, 3, 700, 999, 2, 1000], dtype=torch.int32)
+    decode_case(gpu, 3, 8, 1000, lengths, paged=True, append=True, seed=4, length_aware=True,
+                other_lengths=other)
 
 
 def test_graph_decode_two_level_merge(gpu):
