@@ -110,7 +110,9 @@ typedef struct mla_append_args {
  *                  number of tokens. For batches of unequal lengths. Costs
  *                  one small planning launch; the workspace holds twice the
  *                  default split slots (query mla_decode_workspace_size with
- *                  the same options). Ignored for the f32 and fp8 caches.
+ *                  the same options). Ignored for the f32 and fp8 caches,
+ *                  by mla_decode_fused, and where the default plan has a
+ *                  single split per sequence.
  *   attn_begin/end if non-NULL, HIP events that record the start and the end
  *                  of the split attention kernel on `stream` (bf16 / fp8
  *                  path: taken from the kernel's own dispatch; f32 path:
