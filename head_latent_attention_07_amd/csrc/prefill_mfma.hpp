@@ -124,7 +124,10 @@ __device__ __forceinline__ int64_t prefill_row(const int32_t* __restrict__ table
   } else {
     r = (int64_t)b * seq_capacity + t;
   }
-  return (r >= 0 && r < rows) ? r : 0;
+  // (every caller passes a token of the sequence: t < its length)
+  const bool ok = r >= 0 && r < rows;
+  debug_flag(!ok, DBG_BLOCK);
+  return ok ? r : 0;
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))

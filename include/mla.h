@@ -486,8 +486,8 @@ mla_status mla_decode_paged_noalloc(const mla_dims* dims, const void* q_nope, co
 /* Debug checks of the device-resident integers (the preconditions the host
  * cannot check without a synchronisation): lengths[b] within [0, max_len],
  * every block-table entry a decode split reads (rows t < lengths[b]) within
- * [0, cache_rows / block_size), every cache row that the append and the
- * fp32 decode address within the cache arrays, and every append
+ * [0, cache_rows / block_size), every cache row that the append, the
+ * fp32 decode and the prefill address within the cache arrays, and every append
  * position within its sequence's capacity (seq_capacity, or max_blocks_per_seq
  * * block_size when paged). In every build the kernels clamp such values
  * (a length to [0, max_len], an out-of-range row to row 0, an out-of-range

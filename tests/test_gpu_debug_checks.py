@@ -152,3 +152,26 @@ def test_append_position_out_of_range(dbg):
     assert torch.equal(cache[0], before[0]) and torch.equal(cache[1], before[1])
     assert not torch.equal(cache[2, 10], before[2, 10])
     assert not torch.equal(cache[3, cap - 1], before[3, cap - 1])
+
+
+def test_prefill_block_entry_out_of_range(dbg):
+    """A paged prefill (chunk of 100 queries) with one block entry past the
+    pool: the debug build reports it, both builds read cache row 0 there."""
+    lengths = torch.tensor([300, 200], dtype=torch.int32)
+    inp = synth.make_inputs(2, B=2, N=300, lengths=lengths, paged=True)
+    table = inp.block_table.clone()
+    num_blocks = inp.cache.shape[0] // inp.block_size
+    table[1, 2] = num_blocks + 9
+    inp = dataclasses.replace(inp, block_table=table).to("cuda")
+    qn, qp = [t.cuda() for t in synth.prefill_queries(6400, 2, 100, inp.H)]
+    lat, rope = mla.split_cache(inp.cache)
+    print(f"[case] debug build, prefill with block entry {num_blocks + 9} (pool {num_blocks})",
+          flush=True)
+
+    def run():
+        return mla.prefill(qn, qp, inp.w_uk, inp.w_uv, lat, rope, inp.lengths, inp.max_len,
+                           block_table=inp.block_table, block_size=inp.block_size)
+
+    rel, got, word = on_both(dbg, run)
+    assert word == mla.DEBUG_BLOCK, hex(word)
+    assert same_bits(rel, got)
