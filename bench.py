@@ -803,7 +803,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (one process, no collectives); "
+        print("bench.py: this benchmark runs on one GPU only (one process, no collectives); "
               f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
         sys.exit(2)
 
