@@ -121,3 +121,69 @@ def test_head_counts(gpu, H):
     inp = synth.make_inputs(3, B=4, N=1500, H=H, lengths=lengths, paged=True)
     check(gpu, inp, heads=list(range(0, H, 7)))
 
+
+
+def _plan_layout(B, H, max_len, cus):
+    """Offsets of the length-aware plan in the decode workspace (bf16 path):
+    the default plan's splits S (as the library makes it for this CU count),
+    2S partial slots, B*S work items, then the splits per sequence."""
+    cdiv = lambda a, b: -(-a // b)
+    al = lambda x: (x + 255) // 256 * 256
+    S = min(cdiv(cus, B), cdiv(max_len, 64))
+    S = max(1, min(S, cdiv(max_len, 32)))
+    S = max(S, cdiv(max_len, 64 * 32))
+    ts = cdiv(cdiv(max_len, S), 32) * 32
+    S = cdiv(max_len, ts)
+    slots, nitems = 2 * S, B * S
+    rows = B * slots * H
+    po = al(B * H * 576 * 2)
+    ps = al(po + rows * 512 * 2)
+    pl = al(ps + rows * 4)
+    items = al(pl + rows * 4)
+    nsplit = al(items + nitems * 16)
+    return S, ts, slots, nitems, items, nsplit
+
+
+def test_plan_is_the_smallest_fitting_split(gpu):
+    """The plan the device made, read back from the workspace: every
+    sequence cut into n_b = max(1, ceil(len_b / c)) consecutive items
+    covering [0, len_b) in order, the unused items marked empty, and c the
+    smallest multiple of 32 tokens in [max_len / slots, default split
+    length] for which the splits of all sequences fit in the work items."""
+    g = torch.Generator().manual_seed(77)
+    lengths = torch.randint(1, 4097, (48,), generator=g, dtype=torch.int64).to(torch.int32)
+    lengths[5] = 0
+    lengths[9] = 4096
+    inp = synth.make_inputs(3, B=48, N=4096, lengths=lengths, paged=True).to("cuda")
+    B, H = inp.B, inp.H
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S, ts, slots, nitems, items_off, nsplit_off = _plan_layout(B, H, inp.max_len, cus)
+    act = gpu.dtype_code(inp.q_nope.dtype)
+    wsz = gpu.workspace_size(H, B, inp.max_len, act, act, 0, True)
+    assert wsz == (nsplit_off + B * 4 + 255) // 256 * 256
+    ws = torch.zeros(wsz, dtype=torch.uint8, device="cuda")
+    print(f"[case] plan readback B={B} S={S} slots={slots} items={nitems}", flush=True)
+    gpu.decode_inputs(inp, workspace=ws, length_aware=True)
+    torch.cuda.synchronize()
+    w = ws.cpu()
+    items = w[items_off:items_off + nitems * 16].view(torch.int32).view(nitems, 4).tolist()
+    nsplit = w[nsplit_off:nsplit_off + B * 4].view(torch.int32).tolist()
+    lens = [max(0, min(int(x), inp.max_len)) for x in lengths]
+    cdiv = lambda a, b: -(-a // b)
+    # the split length: the first item of a sequence with two or more
+    c = next(t1 - t0 for b_, s_, t0, t1 in items if b_ >= 0 and s_ == 0 and nsplit[b_] > 1)
+    assert c % 32 == 0 and cdiv(inp.max_len, slots) <= c <= ts, (c, ts)
+    count = lambda cc: sum(max(1, cdiv(n, cc)) for n in lens)
+    assert count(c) <= nitems
+    if c - 32 >= max(32, cdiv(cdiv(inp.max_len, slots), 32) * 32):
+        assert count(c - 32) > nitems
+    q = 0
+    for b in range(B):
+        n = max(1, cdiv(lens[b], c))
+        assert nsplit[b] == n
+        for s in range(n):
+            assert items[q] == [b, s, s * c, min((s + 1) * c, lens[b])], (q, items[q])
+            q += 1
+    assert q == sum(nsplit) <= nitems
+    assert all(it[0] == -1 for it in items[q:])
+    print(f"[result] c={c} tokens, {q} of {nitems} items used", flush=True)
