@@ -30,6 +30,8 @@ Prints ONE JSON line (see the fields below). Options:
   --clock SECONDS          after the timed steps, run the same steps for about
                            SECONDS more while a host thread samples the shader
                            clock through amdsmi (reported as "shader_clock")
+  --stream-read MIB        only measure the plain streaming-read rate of the
+                           device on MIB MiB (calibration kernel) and exit
   --with-projection        the step also computes the new rows from the tokens'
                            hidden states (d_model 7168): mla_project, then the
                            decode call appends from its workspace (with
@@ -77,6 +79,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--stream-read", type=int, default=0, metavar="MIB")
     ap.add_argument("--write-traffic", nargs=4, default=None)
     ap.add_argument("--write-mfma", nargs=2, default=None, metavar=("COUNTERS_CSV", "TRACE_CSV"))
     ap.add_argument("--project", action="store_true")
@@ -285,6 +288,48 @@ def copy_calibration(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def stream_read(mib: int):
+    """The achievable HBM read rate on this device: a plain streaming read of
+    mib MiB (larger than the 256 MB last-level cache) by the calibration
+    kernel (libmla_calib.so), timed by events the launch itself records, for
+    several grid sizes; 5 untimed then 20 timed launches each. Prints one
+    JSON line with the rate per grid and the best."""
+    import torch
+    from head_latent_attention_07_amd import build as b
+    if not os.path.exists(b.CALIB_LIB_PATH):
+        raise SystemExit(f"calibration library not built: {b.CALIB_LIB_PATH}")
+    lib = ctypes.CDLL(b.CALIB_LIB_PATH)
+    lib.mla_calib_stream_read.restype = ctypes.c_int
+    lib.mla_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    n = mib << 20
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(3)
+    grids = (512, 1024, 2048, 4096, 8192)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    rates = {}
+    for grid in grids:
+        for _ in range(5):
+            assert lib.mla_calib_stream_read(buf.data_ptr(), n, out.data_ptr(), grid, None, None,
+                                             stream) == 0
+        pairs = [(ev.create(), ev.create()) for _ in range(20)]
+        for a, e in pairs:
+            assert lib.mla_calib_stream_read(buf.data_ptr(), n, out.data_ptr(), grid, a, e,
+                                             stream) == 0
+        torch.cuda.synchronize()
+        ms = sorted(ev.elapsed_ms(a, e) for a, e in pairs)
+        for a, e in pairs:
+            ev.destroy(a)
+            ev.destroy(e)
+        rates[grid] = {"gbs_mean": n / (sum(ms) / len(ms) * 1e-3) / 1e9,
+                       "gbs_median": n / (ms[len(ms) // 2] * 1e-3) / 1e9}
+    best = max(r["gbs_mean"] for r in rates.values())
+    print(json.dumps({"stream_read_bytes": n, "workgroups_of_256": rates, "best_gbs": best,
+                      "frac_of_8000": best / HBM_PEAK_GBS}), flush=True)
 
 
 def _counter_mean(csv_path: str, kernel_substr: str, counter: str) -> float:
@@ -797,6 +842,9 @@ def main():
     if args.write_mfma:
         kern = FP8_KERNEL if args.config == "5" else "mla_decode_bf16_kernel"
         write_mfma(*args.write_mfma, args.config, kern)
+        return
+    if args.stream_read > 0:
+        stream_read(args.stream_read)
         return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)

@@ -15,6 +15,9 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # the same library with the debug checks of the device-resident integers
 # (lengths, block-table entries, append positions) compiled in
 DEBUG_LIB_PATH = os.path.join(HERE, "libmla_hip_debug.so")
+# the benchmark's calibration kernel (a plain streaming read; not the MLA path)
+CALIB_LIB_PATH = os.path.join(HERE, "libmla_calib.so")
+CALIB_SOURCES = [os.path.join(HERE, "csrc", "calib.hip")]
 SOURCES = [os.path.join(HERE, "csrc", "mla_api.hip")]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
@@ -152,11 +155,27 @@ def build(verbose: bool = False, debug_checks: bool = False) -> str:
     return lib_path
 
 
+def build_calib(verbose: bool = False) -> str:
+    """The benchmark's calibration library (libmla_calib.so)."""
+    tmp = CALIB_LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *CALIB_SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with status {r.returncode}")
+    os.replace(tmp, CALIB_LIB_PATH)
+    return CALIB_LIB_PATH
+
+
 def build_all(verbose: bool = False) -> list:
-    """The release and the debug-checks libraries, built concurrently."""
+    """The release and the debug-checks libraries and the calibration one,
+    built concurrently."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(2) as ex:
+    with ThreadPoolExecutor(3) as ex:
         futs = [ex.submit(build, verbose, dbg) for dbg in (False, True)]
+        futs.append(ex.submit(build_calib, verbose))
         return [f.result() for f in futs]
 
 
