@@ -80,7 +80,8 @@ struct Plan {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_options* opts) {
+Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_options* opts,
+               int nw = 0) {
   Plan pl;
   const int cus = device_cu_count();
   const int len = max_len > 0 ? max_len : 1;
@@ -94,6 +95,9 @@ Plan make_plan(int B, int H, int max_len, mla_dtype act, const mla_decode_option
   } else {
     const int hw = H / 32;
     pl.NW = (hw % 4 == 0) ? 4 : (hw % 2 == 0) ? 2 : 1;
+    if (nw > 0 && hw % nw == 0) pl.NW = nw;
+    const int fw = env_int("MLA_WAVES");   // A/B only: waves (32 heads each) per workgroup
+    if ((fw == 1 || fw == 2 || fw == 4) && hw % fw == 0) pl.NW = fw;
     pl.G = hw / pl.NW;
     // one resident workgroup per CU; splits no shorter than 64 tokens (at
     // B=1 N=4096, 64 splits of 64 tokens beat 16 of 256: 33.0 vs 38.5 us
@@ -181,6 +185,15 @@ bool use_fp8mma(mla_dtype cdt, const Plan& pl, const int32_t* block_table, int b
 Plan decode_plan(int B, int H, int max_len, mla_dtype act, mla_dtype cdt,
                  const int32_t* block_table, int block_size, const mla_decode_options* opts) {
   Plan pl = make_plan(B, H, max_len, act, opts);
+  // bf16 cache with at most half of the CUs holding a workgroup (a batch of
+  // one or two sequences): workgroups of two waves (64 heads), twice as many
+  // of them, each with half the queries to load and half the partial to
+  // write. Measured at B=1 N=4096: 14.2-14.4 vs 15.8-17.1 us per attention
+  // launch, 33.5 vs 34.8 us per step replayed from a graph. Never more
+  // splits than make_plan's (the splits fill the CUs for twice the groups).
+  if (act == MLA_BF16 && cdt == MLA_BF16 && pl.NW == 4 && !env_int("MLA_WAVES") &&
+      (int64_t)B * pl.S * pl.G * 2 <= device_cu_count())
+    pl = make_plan(B, H, max_len, act, opts, 2);
   if (act != MLA_F32 && use_fp8mma(cdt, pl, block_table, block_size)) {
     const int len = max_len > 0 ? max_len : 1;
     const bool forced = (opts && opts->num_splits > 0) || env_int("MLA_SPLITS") > 0;
