@@ -168,7 +168,7 @@ void launch_short_merge(const CombineParams& cp, dim3 cgrid, hipStream_t stream)
 
 // The fp8 cache goes to the fp8 matrix cores (decode_fp8mma.hpp) when its
 // layout fits that kernel: four waves of 32 heads per workgroup, splits of
-// whole 64-token tiles (at most 32 of them), and page blocks holding whole
+// whole 64-token tiles (at most 64 of them), and page blocks holding whole
 // tiles; MLA_FP8_KERNEL=widen selects the widening kernel instead.
 bool use_fp8mma(mla_dtype cdt, const Plan& pl, const int32_t* block_table, int block_size) {
   if (cdt != MLA_FP8_E4M3 || pl.NW != 4) return false;
