@@ -175,3 +175,16 @@ def test_prefill_block_entry_out_of_range(dbg):
     rel, got, word = on_both(dbg, run)
     assert word == mla.DEBUG_BLOCK, hex(word)
     assert same_bits(rel, got)
+
+
+def test_length_aware_plan_length_out_of_range(dbg):
+    """The length-aware plan reads the lengths in the absorb launch: a length
+    past max_len and a negative one are reported there and clamped, as in
+    the default plan."""
+    inp = small(3, paged=True)
+    bad = torch.tensor([inp.max_len + 7, -1] + LENGTHS[2:], dtype=torch.int32)
+    inp = dataclasses.replace(inp, lengths=bad).to("cuda")
+    print(f"[case] debug build, length-aware plan, lengths {bad.tolist()}", flush=True)
+    rel, got, word = on_both(dbg, lambda: mla.decode_inputs(inp, length_aware=True))
+    assert word == mla.DEBUG_LENGTH, hex(word)
+    assert same_bits(rel, got)
